@@ -1,0 +1,95 @@
+"""Pins of stochastic rounding, packing and decode in the oracle (CPU only).
+
+Page "Rate-adaptive KV-cache quantizer": Key formulas (3) (rounding up with
+probability (x-q_i)/(q_{i+1}-q_i), conditional mean x, conditional MSE
+(q_{i+1}-x)(x-q_i)) and Implementation notes (codebook, symbol stream and
+block lengths are stored; decoding before attention).
+"""
+
+import numpy as np
+import pytest
+
+from oracle import codes, ecasq
+from kv_cache_rate_amd import workloads as W
+from oracle import blocks as oblocks
+
+
+def test_code_width():
+    assert [codes.code_width(m) for m in range(1, 18)] == \
+        [0, 1, 2, 2, 3, 3, 3, 3, 4, 4, 4, 4, 4, 4, 4, 4, 5]
+
+
+def test_pack_worked_example():
+    """tests/golden/pack_example.txt, worked by hand."""
+    path = __file__.replace("test_oracle_codes.py", "golden/pack_example.txt")
+    vals = {}
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if line:
+            k, v = line.split("=")
+            vals[k.strip()] = eval(v)
+    words = codes.pack_block(np.array(vals["codes"]), vals["w"])
+    assert [int(v) for v in words] == vals["words"]
+    words3 = codes.pack_block(np.array(vals["codes3"]), 3)
+    assert [int(v) for v in words3] == vals["words3"]
+
+
+@pytest.mark.parametrize("w", [0, 1, 2, 3, 4])
+def test_pack_roundtrip(w, rng):
+    for n in (1, 31, 32, 33, 4096):
+        c = rng.integers(0, 1 << w, size=n) if w else np.zeros(n, dtype=np.int64)
+        words = codes.pack_block(c, w)
+        assert words.size == (n * w + 31) // 32
+        assert np.array_equal(codes.unpack_block(words, n, w), c.astype(np.uint32))
+        # unused tail bits are zero
+        if w and (n * w) % 32:
+            assert int(words[-1]) >> ((n * w) % 32) == 0
+
+
+def test_offsets_are_block_lengths():
+    off = codes.offsets(4096, [0, 1, 3, 4, 2])
+    assert list(off) == [0, 0, 128, 512, 1024, 1280]
+
+
+def test_codes_land_on_neighbours_and_decode_exactly(rng):
+    x = W.generate(W.DECODE_ADMIT_FP16)
+    b = oblocks.partition(x, 32, 128)[:4]
+    for r, blk in enumerate(b):
+        xs = np.sort(blk)
+        for Q in ecasq.grid_candidates(xs, 16)[::5]:
+            c, near = codes.quantize_block(blk, Q, 0, r)
+            i = ecasq.interval_index(Q, blk)
+            assert np.all((c == i) | (c == i + 1))
+            on = np.isin(blk, Q)  # entries on a codepoint keep it exactly
+            assert np.all(Q[c[on]] == blk[on])
+            xh = codes.dequantize_block(c, Q)
+            assert xh.dtype == np.float32
+            assert np.array_equal(xh.astype(np.float64), Q[c])
+
+
+def test_monte_carlo_unbiased_and_mse():
+    """Over many independent seeds the mean decoded value converges to x
+    (unbiasedness) and the empirical MSE matches the closed-form D."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(4096)
+    Q = np.unique(ecasq.uniform_points(x.min(), x.max(), 5))
+    D, _, _ = ecasq.score_codebook(x, Q)
+    M = 300
+    acc = np.zeros_like(x)
+    sq = np.zeros_like(x)
+    for seed in range(M):
+        c, _ = codes.quantize_block(x, Q, seed, 9)
+        xh = Q[c]
+        acc += xh - x
+        sq += (xh - x) ** 2
+    var = D / x.size  # per-entry conditional variance, averaged
+    mean_err = acc / M
+    # each entry's mean error has sd sqrt((b-x)(x-a)/M); pooled over the block
+    i = ecasq.interval_index(Q, x)
+    v = (Q[i + 1] - x) * (x - Q[i])
+    z = mean_err.sum() / np.sqrt(v.sum() / M)
+    assert abs(z) < 5
+    assert np.mean(np.abs(mean_err)) < 4 * np.sqrt(var / M)
+    mse = sq.sum() / (M * x.size)
+    # MSE estimate sd ~ sqrt(Var[(xh-x)^2]) / sqrt(M n); generous 6 sigma band
+    assert mse == pytest.approx(var, rel=6 / np.sqrt(M * x.size) * 3)

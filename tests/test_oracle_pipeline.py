@@ -1,0 +1,66 @@
+"""End-to-end checks of the oracle's admission pass (CPU only)."""
+
+import numpy as np
+import pytest
+
+from oracle import codes, ecasq, pipeline
+from oracle import blocks as oblocks
+from kv_cache_rate_amd import workloads as W
+
+
+@pytest.mark.parametrize("B", [3.0, 1.0])
+def test_tiny_end_to_end(B):
+    w = W.TINY_K_FP32
+    b = oblocks.partition(W.generate(w), w.tokens_per_block, w.dims_per_block)
+    out = pipeline.run(b, s=w.s, B=B, seed=w.seed)
+    n, R = b.shape[1], b.shape[0]
+    assert out["rate_bits"] <= B * n * R
+    if B >= 3.0:
+        # H <= log2 |Q| <= log2 8 = 3 for every candidate: the budget never binds
+        assert out["lam"] == 0.0
+    else:
+        assert out["lam"] > 0.0
+    assert out["words"].size == int(out["offsets"][-1])
+    for r in range(R):
+        w_r = int(out["width"][r])
+        seg = out["words"][int(out["offsets"][r]):int(out["offsets"][r + 1])]
+        c = codes.unpack_block(seg, n, w_r)
+        assert np.array_equal(c, out["codes"][r])
+        xh = codes.dequantize_block(c, out["chosen"][r])
+        # decoded values are codepoints bracketing each entry
+        Q = out["chosen"][r]
+        i = ecasq.interval_index(Q, b[r])
+        assert np.all((xh == Q[i].astype(np.float32)) | (xh == Q[i + 1].astype(np.float32)))
+    # packed bits are at least the modelled entropy
+    assert out["packed_bits_per_entry"] >= out["rate_per_entry"]
+
+
+def test_exact_dp_end_to_end():
+    w = W.FEATURE_GROUP_EXACT_FP32
+    b = oblocks.partition(W.generate(w), w.tokens_per_block, w.dims_per_block)[:12]
+    out = pipeline.run(b, search="exact_dp", s=8, alphabet_m=12, B=2.0, seed=0)
+    assert out["rate_bits"] <= 2.0 * b.size
+    assert np.all(out["m"] <= 8)
+    for r in range(b.shape[0]):
+        Q = out["chosen"][r]
+        A = out["alphabets"][r]
+        assert Q[0] == A[0] and Q[-1] == A[-1]
+        assert np.all(np.isin(Q, A))
+
+
+def test_partition_order_and_canonical_zero():
+    x = np.arange(2 * 3 * 64 * 32, dtype=np.float32).reshape(2, 3, 64, 32)
+    b = oblocks.partition([x], 32, 16)
+    assert b.shape == (2 * 3 * 2 * 2, 512)
+    # block 1 is (outer 0, head 0, chunk 0, feature group 1)
+    assert np.array_equal(b[1].reshape(32, 16), x[0, 0, :32, 16:32])
+    # block 2 is (outer 0, head 0, chunk 1, group 0)
+    assert np.array_equal(b[2].reshape(32, 16), x[0, 0, 32:64, :16])
+    assert np.array_equal(oblocks.block_of([x], 32, 16, 7), b[7])
+    z = np.full((1, 1, 32, 16), -0.0, dtype=np.float32)
+    zb = oblocks.partition([z], 32, 16)
+    assert not np.any(np.signbit(zb))
+    bad = z.copy()
+    bad[0, 0, 3, 3] = np.nan
+    with pytest.raises(ValueError):
+        oblocks.partition([bad], 32, 16)
