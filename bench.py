@@ -1,0 +1,217 @@
+"""Throughput of KV-cache admission with blockwise ECASQ on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over the workload's synthetic K/V
+tensors (already resident in HBM): kvq_plan_blocks, kvq_eval_candidates,
+kvq_solve_lambda (bisection to the bits-per-entry budget), kvq_quantize_pack
+and kvq_dequantize.  The default workload is the long-context admission
+shape: 32 layers x 8 KV heads x 32768 tokens x 128, fp16 K and V (4.3 GB),
+head x 32-token blocks, s = 16, B = 2.0 bits per entry.
+
+Prints ONE JSON line: the metric is KV GB/s quantized (input K/V bytes per
+second of step time) with the roofline of the dominant kernel (algorithmic
+bytes per launch over its HIP-event-timed duration against 8 TB/s) and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_rate_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(plan, words_total, in_bytes_per_entry):
+    """Bytes each call must move at minimum (inputs read once, outputs
+    written once)."""
+    R, n = plan.n_blocks, plan.n_entries
+    table = plan.D_bytes + plan.H_bytes
+    meta = plan.codebook_bytes + plan.m_bytes + plan.offsets_bytes
+    return {
+        "eval": n * in_bytes_per_entry + table + plan.stats_bytes,
+        "solve": table + plan.stats_bytes + meta + plan.choice_bytes,
+        "quantize_pack": n * in_bytes_per_entry + meta + 4 * words_total,
+        "dequantize": 4 * words_total + meta + 4 * n,
+    }
+
+
+def load_traffic(kernel, sha):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    k = rec.get(kernel)
+    if not k or k.get("source_sha") != sha:
+        return None
+    return k.get("bytes_per_launch")
+
+
+def cpu_baseline(w, tensors, target_s=10.0):
+    """The oracle, as it stands, on the first blocks of the workload: eval,
+    bisection, quantize+pack and decode, on all host cores."""
+    from oracle import blocks as oblocks
+    from oracle import codes as ocodes
+    from oracle import pipeline
+    procs = pipeline.default_processes()
+    per_tensor = tensors[0].shape[1] * (tensors[0].shape[2] // w.tokens_per_block) * \
+        (tensors[0].shape[3] // w.dims_per_block)
+    layer_blocks = per_tensor  # blocks of one outer index of tensor 0
+
+    def sample(nb):
+        sub = [tensors[0][:1]]
+        b = oblocks.partition(sub, w.tokens_per_block, w.dims_per_block)
+        return b[:nb]
+
+    def run(b):
+        t0 = time.perf_counter()
+        out = pipeline.run(b, search=w.search, s=w.s, alphabet_m=w.alphabet_m, B=w.B,
+                           mode="bisect", iters=w.iters, seed=w.seed, processes=procs)
+        for r in range(b.shape[0]):
+            ocodes.dequantize_block(out["codes"][r], out["chosen"][r])
+        return time.perf_counter() - t0
+
+    pilot_n = min(layer_blocks, 16 * procs)
+    t_pilot = run(sample(pilot_n))
+    nb = int(min(layer_blocks, max(pilot_n, pilot_n * target_s / max(t_pilot, 1e-3))))
+    b = sample(nb)
+    t = run(b)
+    in_bytes = b.size * (2 if w.dtype == "f16" else 4)
+    return {"value": in_bytes / t / 1e9, "unit": "GB/s", "cores": procs, "kind": "oracle",
+            "sample": f"first {nb} blocks ({b.size} entries) of layer 0 of K: eval, bisection "
+                      f"(B={w.B}), quantize+pack, decode; {t:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="long_context_kv_fp16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from kv_cache_rate_amd import kvq
+    from kv_cache_rate_amd import workloads as W
+
+    w = W.BY_NAME[a.workload]
+    log(f"generating {w.name}: {w.n_entries} entries, {w.input_bytes / 1e9:.2f} GB")
+    t0 = time.time()
+    host = W.generate(w)
+    log(f"generated in {time.time() - t0:.1f} s; copying to HBM")
+    dev = [torch.from_numpy(h).cuda() for h in host]
+    torch.cuda.synchronize()
+    search = kvq.KVQ_GRIDS if w.search == "grids" else kvq.KVQ_EXACT_DP
+    mode = kvq.KVQ_BISECT if w.mode == "bisect" else kvq.KVQ_SUBGRAD
+    plan = kvq.kvq_plan_blocks(dev, w.tokens_per_block, w.dims_per_block, w.s, search,
+                               w.alphabet_m if search else 0)
+    buf = kvq.allocate(plan, dequant=True)
+    stream = torch.cuda.current_stream()
+    names = ["eval", "solve", "quantize_pack", "dequantize"]
+
+    def step(events=None):
+        p = kvq.kvq_plan_blocks(dev, w.tokens_per_block, w.dims_per_block, w.s, search,
+                                w.alphabet_m if search else 0)
+        if events is not None:
+            events[0].record(stream)
+        kvq.kvq_eval_candidates(p, dev, buf["D"], buf["H"], buf["stats"], buf["workspace"], stream)
+        if events is not None:
+            events[1].record(stream)
+        lam, rate = kvq.kvq_solve_lambda(p, buf["D"], buf["H"], buf["stats"], w.B, mode, w.iters,
+                                         w.eta, 0.0, buf["choice"], buf["codebook"], buf["m"],
+                                         buf["off"], buf["workspace"], stream)
+        if events is not None:
+            events[2].record(stream)
+        kvq.kvq_quantize_pack(p, dev, buf["codebook"], buf["m"], buf["off"], w.seed, buf["codes"],
+                              stream=stream)
+        if events is not None:
+            events[3].record(stream)
+        kvq.kvq_dequantize(p, buf["codes"], buf["codebook"], buf["m"], buf["off"], buf["xhat"], stream)
+        if events is not None:
+            events[4].record(stream)
+        return lam, rate
+
+    for i in range(a.warmup):
+        lam, rate = step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        lam, rate = step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / max(1, a.steps)
+    per = {k: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(a.steps)]))
+           for j, k in enumerate(names)}
+    words_total = int(buf["off"][-1].item())
+    alg = algorithmic_bytes(plan, words_total, 2 if w.dtype == "f16" else 4)
+    dom = max(per, key=per.get)
+    achieved = alg[dom] / (per[dom] * 1e-3) / 1e9
+    sha = kernel_sources_sha()
+    traffic = load_traffic(dom, sha)
+    value = w.input_bytes / (ms_per_step * 1e-3) / 1e9
+    admit_ms = per["eval"] + per["quantize_pack"]
+    rec = {
+        "metric": "KV GB/s quantized (fp16 in) and % of HBM roofline at 32-token blocks",
+        "value": value, "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16" if w.dtype == "f16" else "f32",
+        "data": "synthetic (seeded numpy; N(0,1) x per-layer U[0.5,4] scale, 1% +-10 sigma)",
+        "config": {"workload": w.name, "tensors": [list(s) for _, s in w.tensors],
+                   "block": f"head x {w.tokens_per_block} tokens x {w.dims_per_block}",
+                   "s": w.s, "B_bits_per_entry": w.B, "lambda_search": f"{w.mode} {w.iters}",
+                   "n_blocks": w.n_blocks, "entries": w.n_entries,
+                   "step": "plan+eval+solve+quantize_pack+dequantize"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": alg[dom]},
+        "kernels_ms": per,
+        "eval_plus_quantize": {"ms": admit_ms,
+                               "kv_GBps": w.input_bytes / (admit_ms * 1e-3) / 1e9,
+                               "frac_of_hbm": (alg["eval"] + alg["quantize_pack"]) /
+                                              (admit_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "lambda": lam, "rate_bits_per_entry": rate,
+        "packed_bits_per_entry": 32.0 * words_total / w.n_entries,
+        "source_sha": sha,
+    }
+    if not a.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        rec["cpu_baseline"] = cpu_baseline(w, host)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,280 @@
+// libkvq C ABI: argument validation, block planning and launch sequencing.
+// The operations themselves are defined in include/kvq.h; every step runs in
+// the HIP kernels of kvq_eval.hip, kvq_solve.hip and kvq_quant.hip.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+kvq_status ok() {
+    g_err.clear();
+    return KVQ_OK;
+}
+
+kvq_status hip_fail(hipError_t e, const char* where) {
+    return fail(KVQ_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+int distinct_quantile_ranks(int n, int s, int32_t* out) {
+    // sorted distinct ranks j (n-1)/(k-1) rounded half up over k = 2..s
+    int32_t all[(KVQ_MAX_S + 1) * KVQ_MAX_S];
+    int cnt = 0;
+    for (int k = 2; k <= s; ++k)
+        for (int j = 0; j < k; ++j) all[cnt++] = kvq::quantile_rank(j, k, n);
+    for (int a = 1; a < cnt; ++a)  // insertion sort (at most 135 values)
+        for (int b = a; b > 0 && all[b - 1] > all[b]; --b) {
+            const int32_t tmp = all[b];
+            all[b] = all[b - 1];
+            all[b - 1] = tmp;
+        }
+    int u = 0;
+    for (int a = 0; a < cnt; ++a)
+        if (u == 0 || all[a] != all[u - 1]) all[u++] = all[a];
+    if (out)
+        for (int a = 0; a < u && a < kvq::kMaxStats; ++a) out[a] = all[a];
+    return u;
+}
+
+void rank_table(const kvq_plan& p, kvq::RankTable& rt) {
+    memset(&rt, 0, sizeof rt);
+    if (p.search != KVQ_GRIDS) return;
+    rt.n_stats = distinct_quantile_ranks(p.d_block, p.s, rt.rank);
+    for (int k = 2; k <= p.s; ++k)
+        for (int j = 0; j < k; ++j) {
+            const int q = kvq::quantile_rank(j, k, p.d_block);
+            for (int c = 0; c < rt.n_stats; ++c)
+                if (rt.rank[c] == q) rt.col[k][j] = (uint8_t)c;
+        }
+}
+
+bool valid_plan(const kvq_plan* p) {
+    return p && p->n_blocks >= 0 && p->d_block >= 2 && p->d_block <= KVQ_MAX_BLOCK && p->s >= 2 &&
+           p->s <= KVQ_MAX_S && (p->search == KVQ_GRIDS || p->search == KVQ_EXACT_DP) &&
+           p->n_tensors >= 1 && p->n_tensors <= KVQ_MAX_TENSORS;
+}
+
+// Validate tensors against the plan and build the kernels' geometry.
+kvq_status make_geom(const kvq_plan* p, const kvq_tensor* t, int32_t nt, kvq::Geom& g) {
+    if (!valid_plan(p)) return fail(KVQ_EINVAL, "invalid plan");
+    if (!t) return fail(KVQ_EINVAL, "null tensor array");
+    if (nt != p->n_tensors) return fail(KVQ_EINVAL, "plan is for %d tensors, got %d", p->n_tensors, nt);
+    memset(&g, 0, sizeof g);
+    g.contig = 1;
+    for (int i = 0; i < nt; ++i) {
+        if (!t[i].data) return fail(KVQ_EINVAL, "tensor %d: null data", i);
+        if (t[i].dtype != p->dtype) return fail(KVQ_EINVAL, "tensor %d: dtype differs from plan", i);
+        for (int d = 0; d < 4; ++d) {
+            if (t[i].shape[d] != p->shape[i][d])
+                return fail(KVQ_EINVAL, "tensor %d: shape differs from plan", i);
+            if (t[i].stride[d] <= 0) return fail(KVQ_EINVAL, "tensor %d: non-positive stride", i);
+        }
+        g.data[i] = t[i].data;
+        for (int d = 0; d < 4; ++d) g.stride[i][d] = t[i].stride[d];
+        if (!(t[i].stride[3] == 1 && t[i].stride[2] == p->dims_per_block)) g.contig = 0;
+    }
+    g.nb0 = p->tensor_blocks[0];
+    g.heads = (int32_t)p->shape[0][1];
+    g.chunks = (int32_t)(p->shape[0][2] / p->tokens_per_block);
+    g.groups = (int32_t)(p->shape[0][3] / p->dims_per_block);
+    g.Tb = p->tokens_per_block;
+    g.Db = p->dims_per_block;
+    g.n = p->d_block;
+    g.dtype = p->dtype;
+    return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_string(kvq_status st) {
+    switch (st) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_EINVAL: return "KVQ_EINVAL: invalid argument";
+    case KVQ_EINFEASIBLE: return "KVQ_EINFEASIBLE: budget below the least-entropy allocation";
+    case KVQ_ENONFINITE: return "KVQ_ENONFINITE: NaN or Inf in the KV input";
+    case KVQ_ENOSPC: return "KVQ_ENOSPC: output capacity too small";
+    case KVQ_EHIP: return "KVQ_EHIP: HIP runtime error";
+    default: return "unknown kvq status";
+    }
+}
+
+const char* kvq_last_error(void) { return g_err.c_str(); }
+
+kvq_status kvq_plan_blocks(const kvq_tensor* t, int32_t nt, const kvq_block_spec* spec, kvq_plan* out) {
+    if (!t || !spec || !out) return fail(KVQ_EINVAL, "null argument");
+    if (nt < 1 || nt > KVQ_MAX_TENSORS) return fail(KVQ_EINVAL, "n_tensors must be 1 or 2");
+    const int Tb = spec->tokens_per_block, Db = spec->dims_per_block;
+    if (Tb <= 0 || Db <= 0) return fail(KVQ_EINVAL, "block shape must be positive");
+    const int64_t n = (int64_t)Tb * Db;
+    if (n < 2 || n > KVQ_MAX_BLOCK) return fail(KVQ_EINVAL, "block of %lld entries (need 2..4096)", (long long)n);
+    if (spec->s < 2 || spec->s > KVQ_MAX_S) return fail(KVQ_EINVAL, "s=%d outside 2..16", spec->s);
+    if (spec->search != KVQ_GRIDS && spec->search != KVQ_EXACT_DP)
+        return fail(KVQ_EINVAL, "unknown search mode %d", spec->search);
+    if (spec->search == KVQ_EXACT_DP && (spec->alphabet_m < 2 || spec->alphabet_m > KVQ_MAX_ALPHABET))
+        return fail(KVQ_EINVAL, "alphabet_m=%d outside 2..12", spec->alphabet_m);
+    kvq_plan p;
+    memset(&p, 0, sizeof p);
+    p.dtype = t[0].dtype;
+    if (p.dtype != KVQ_F16 && p.dtype != KVQ_F32) return fail(KVQ_EINVAL, "dtype must be KVQ_F16 or KVQ_F32");
+    int64_t R = 0;
+    for (int i = 0; i < nt; ++i) {
+        if (t[i].dtype != p.dtype) return fail(KVQ_EINVAL, "tensors must share a dtype");
+        for (int d = 0; d < 4; ++d) {
+            if (t[i].shape[d] <= 0) return fail(KVQ_EINVAL, "tensor %d: empty or negative dimension", i);
+            if (t[i].shape[d] != t[0].shape[d]) return fail(KVQ_EINVAL, "tensors must share a shape");
+            if (t[i].stride[d] <= 0) return fail(KVQ_EINVAL, "tensor %d: non-positive stride", i);
+            p.shape[i][d] = t[i].shape[d];
+        }
+        if (t[i].shape[2] % Tb) return fail(KVQ_EINVAL, "tokens %lld not a multiple of %d", (long long)t[i].shape[2], Tb);
+        if (t[i].shape[3] % Db) return fail(KVQ_EINVAL, "dim %lld not a multiple of %d", (long long)t[i].shape[3], Db);
+        const int64_t nb = t[i].shape[0] * t[i].shape[1] * (t[i].shape[2] / Tb) * (t[i].shape[3] / Db);
+        p.tensor_blocks[i] = nb;
+        R += nb;
+    }
+    if (R >= (int64_t)1 << 31) return fail(KVQ_EINVAL, "too many blocks (%lld)", (long long)R);
+    if (t[0].shape[1] >= ((int64_t)1 << 31) || t[0].shape[2] / Tb >= ((int64_t)1 << 31))
+        return fail(KVQ_EINVAL, "dimension too large");
+    p.n_blocks = R;
+    p.n_entries = R * n;
+    p.d_block = (int32_t)n;
+    p.s = spec->s;
+    p.search = spec->search;
+    p.alphabet_m = spec->search == KVQ_EXACT_DP ? spec->alphabet_m : 0;
+    p.n_tensors = nt;
+    p.tokens_per_block = Tb;
+    p.dims_per_block = Db;
+    int max_levels;
+    if (p.search == KVQ_GRIDS) {
+        p.n_cand = 1 + 2 * (p.s - 2);
+        p.n_stats = distinct_quantile_ranks((int)n, p.s, nullptr);
+        if (p.n_stats > kvq::kMaxStats) return fail(KVQ_EINVAL, "too many order statistics");
+        p.D_bytes = (size_t)R * p.n_cand * sizeof(double);
+        p.H_bytes = p.D_bytes;
+        max_levels = p.s;
+    } else {
+        p.n_cand = kvq::kPairs;
+        p.n_stats = p.alphabet_m;
+        p.D_bytes = (size_t)R * kvq::kPairs * sizeof(double);
+        p.H_bytes = 2 * p.D_bytes;
+        max_levels = p.s < p.alphabet_m ? p.s : p.alphabet_m;
+    }
+    p.stats_bytes = (size_t)R * p.n_stats * sizeof(float);
+    p.choice_bytes = (size_t)R * sizeof(int32_t);
+    p.codebook_bytes = (size_t)R * p.s * sizeof(float);
+    p.m_bytes = (size_t)R;
+    p.offsets_bytes = (size_t)(R + 1) * sizeof(uint64_t);
+    const int64_t tiles = (R + 1023) / 1024 + 1;
+    p.workspace_bytes = (kvq::kWsHeaderBytes + (size_t)tiles * sizeof(uint64_t) + 255) & ~(size_t)255;
+    p.max_code_words = (uint64_t)R * (((uint64_t)n * kvq::code_width(max_levels) + 31) / 32);
+    // fixed point for exact rate sums: total <= n_entries * log2(levels) bits
+    const double max_rate = (double)p.n_entries * (double)kvq::code_width(max_levels) + 1.0;
+    int shift = 62 - (int)ceil(log2(max_rate));
+    p.rate_shift = shift > 40 ? 40 : (shift < 0 ? 0 : shift);
+    *out = p;
+    return ok();
+}
+
+kvq_status kvq_eval_candidates(const kvq_plan* p, const kvq_tensor* t, int32_t nt, double* D, double* H,
+                               float* stats, void* workspace, hipStream_t s) {
+    kvq::Geom g;
+    kvq_status st = make_geom(p, t, nt, g);
+    if (st) return st;
+    if (!D || !H || !stats || !workspace) return fail(KVQ_EINVAL, "null output or workspace");
+    hipError_t e = kvq::launch_ws_reset(workspace, s);
+    if (e != hipSuccess) return hip_fail(e, "ws_reset");
+    if (p->search == KVQ_GRIDS) {
+        kvq::RankTable rt;
+        rank_table(*p, rt);
+        e = kvq::launch_eval_grids(g, p->n_blocks, p->s, rt, D, H, stats, workspace, s);
+    } else {
+        e = kvq::launch_eval_alphabet(g, p->n_blocks, p->alphabet_m, D, H, stats, workspace, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "eval launch");
+    return ok();
+}
+
+kvq_status kvq_solve_lambda(const kvq_plan* p, const double* D, const double* H, const float* stats,
+                            double B, int32_t mode, int32_t iters, double eta, double* lambda_io,
+                            double* rate_out, int32_t* choice, float* codebook, uint8_t* m,
+                            uint64_t* word_off, void* workspace, hipStream_t s) {
+    if (!valid_plan(p)) return fail(KVQ_EINVAL, "invalid plan");
+    if (!D || !H || !stats || !choice || !codebook || !m || !word_off || !workspace)
+        return fail(KVQ_EINVAL, "null device pointer");
+    if (!lambda_io || !rate_out) return fail(KVQ_EINVAL, "null host pointer");
+    if (mode != KVQ_BISECT && mode != KVQ_SUBGRAD) return fail(KVQ_EINVAL, "unknown mode %d", mode);
+    if (!isfinite(B) || B < 0.0) return fail(KVQ_EINVAL, "budget must be finite and >= 0");
+    if (mode == KVQ_BISECT && (iters < 0 || iters > 63)) return fail(KVQ_EINVAL, "iters must be 0..63");
+    const double lam_in = *lambda_io;
+    if (mode == KVQ_SUBGRAD && (!isfinite(lam_in) || lam_in < 0.0 || !isfinite(eta)))
+        return fail(KVQ_EINVAL, "subgradient needs finite lambda >= 0 and finite eta");
+    kvq::RankTable rt;
+    rank_table(*p, rt);
+    hipError_t e = kvq::launch_solve(*p, rt, D, H, stats, B, mode, iters, lam_in, choice, codebook, m,
+                                     word_off, workspace, s);
+    if (e != hipSuccess) return hip_fail(e, "solve launch");
+    kvq::WsHeader hdr;
+    e = hipMemcpyAsync(&hdr, workspace, sizeof hdr, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "status copy");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "stream sync");
+    if (hdr.status & kvq::kStatusNonFinite) return fail(KVQ_ENONFINITE, "NaN or Inf among the KV entries");
+    if (hdr.err == KVQ_EINFEASIBLE)
+        return fail(KVQ_EINFEASIBLE, "no lambda <= 2^64 brings the rate under %g bits/entry", B);
+    if (hdr.err) return fail(KVQ_EINVAL, "solver state error %d", hdr.err);
+    const double rbar = ldexp((double)hdr.rate_final, -p->rate_shift) / (double)p->n_entries;
+    *rate_out = rbar;
+    if (mode == KVQ_SUBGRAD) {
+        const double nxt = lam_in + eta * (rbar - B);
+        *lambda_io = nxt > 0.0 ? nxt : 0.0;
+    } else {
+        *lambda_io = hdr.lam_final;
+    }
+    return ok();
+}
+
+kvq_status kvq_quantize_pack(const kvq_plan* p, const kvq_tensor* t, int32_t nt, const float* codebook,
+                             const uint8_t* m, const uint64_t* word_off, uint64_t seed, uint32_t* codes,
+                             uint64_t cap, hipStream_t s) {
+    kvq::Geom g;
+    kvq_status st = make_geom(p, t, nt, g);
+    if (st) return st;
+    if (!codebook || !m || !word_off || (!codes && p->max_code_words))
+        return fail(KVQ_EINVAL, "null device pointer");
+    if (cap < p->max_code_words)
+        return fail(KVQ_ENOSPC, "codes capacity %llu words < plan.max_code_words %llu",
+                    (unsigned long long)cap, (unsigned long long)p->max_code_words);
+    hipError_t e = kvq::launch_quantize(g, p->n_blocks, p->s, codebook, m, word_off, seed, codes, s);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    return ok();
+}
+
+kvq_status kvq_dequantize(const kvq_plan* p, const uint32_t* codes, const float* codebook, const uint8_t* m,
+                          const uint64_t* word_off, float* xhat, hipStream_t s) {
+    if (!valid_plan(p)) return fail(KVQ_EINVAL, "invalid plan");
+    if (!codebook || !m || !word_off || !xhat || (!codes && p->max_code_words))
+        return fail(KVQ_EINVAL, "null device pointer");
+    hipError_t e = kvq::launch_dequantize(p->n_blocks, p->d_block, p->s, codes, codebook, m, word_off, xhat, s);
+    if (e != hipSuccess) return hip_fail(e, "dequantize launch");
+    return ok();
+}
+
+}  // extern "C"

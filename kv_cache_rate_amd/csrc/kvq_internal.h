@@ -1,0 +1,165 @@
+// Internal declarations shared by the libkvq translation units: block
+// geometry, device helpers and the host-side launch functions of each
+// kernel file.  Not part of the public ABI (include/kvq.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int kMaxBlock = KVQ_MAX_BLOCK;          // entries per block
+constexpr int kMaxS = KVQ_MAX_S;                  // codebook size limit
+constexpr int kMaxCand = 1 + 2 * (kMaxS - 2);     // 29 grid candidates
+constexpr int kMaxStats = 80;                     // >= 73 distinct quantile ranks
+constexpr int kAlpha = KVQ_MAX_ALPHABET;          // 12
+constexpr int kPairs = kAlpha * (kAlpha - 1) / 2; // 66
+constexpr int kMaxLam = 64;                       // multipliers per solve pass
+
+// Device status bits (workspace header).
+constexpr uint32_t kStatusNonFinite = 1u;
+
+// Fixed header at the start of the caller's workspace.  All solve state lives
+// here so the whole bracket search runs on the device without host syncs.
+struct WsHeader {
+    uint32_t status;     // kStatus* bits set by kernels
+    int32_t phase;       // solve phase (see kvq_solve.hip)
+    int32_t done;        // 1 once lam_final is known
+    int32_t err;         // KVQ_EINFEASIBLE when the doubling overflows
+    int32_t nlam;        // multipliers probed by the next rates pass
+    int32_t bits_left;   // halvings still to emulate
+    int32_t bits_now;    // halvings covered by the current pass
+    int32_t pad0;
+    double lo, hi;       // bracket
+    double lam_final;    // multiplier the blocks are chosen at
+    uint64_t rate_final; // fixed-point rate of the final choice
+    uint64_t Btot_fx;    // budget in the same fixed point
+    double lam[kMaxLam + 8];
+    unsigned long long sums[kMaxLam + 8];
+};
+constexpr size_t kWsHeaderBytes = 4096;
+static_assert(sizeof(WsHeader) <= kWsHeaderBytes, "workspace header");
+
+// Block geometry as the kernels see it (passed by value).
+struct Geom {
+    const void* data[KVQ_MAX_TENSORS];
+    int64_t nb0;                          // blocks of tensor 0
+    int64_t stride[KVQ_MAX_TENSORS][4];   // element strides
+    int32_t heads, chunks, groups;        // same for every tensor
+    int32_t Tb, Db, n;                    // block shape, n = Tb * Db
+    int32_t dtype;                        // KVQ_F16 | KVQ_F32
+    int32_t contig;                       // 1: every block is n contiguous entries
+};
+
+// Tensor index and element offset of entry 0 of block r (block order:
+// tensor, outer, head, token chunk, feature group).
+__device__ __forceinline__ int64_t block_base(const Geom& g, int64_t r, int& ti) {
+    ti = r >= g.nb0 ? 1 : 0;
+    int64_t rl = ti ? r - g.nb0 : r;
+    const int64_t gr = rl % g.groups;
+    rl /= g.groups;
+    const int64_t c = rl % g.chunks;
+    rl /= g.chunks;
+    const int64_t h = rl % g.heads;
+    const int64_t o = rl / g.heads;
+    return o * g.stride[ti][0] + h * g.stride[ti][1] + c * (int64_t)g.Tb * g.stride[ti][2] +
+           gr * (int64_t)g.Db * g.stride[ti][3];
+}
+
+// Offset of entry t (row-major token, feature) from the block base.
+__device__ __forceinline__ int64_t entry_off(const Geom& g, int ti, int t) {
+    if (g.contig) return t;
+    const int tok = t / g.Db;
+    const int col = t - tok * g.Db;
+    return tok * g.stride[ti][2] + col * g.stride[ti][3];
+}
+
+__device__ __forceinline__ float load_entry(const Geom& g, int ti, int64_t off) {
+    if (g.dtype == KVQ_F16) return __half2float(reinterpret_cast<const __half*>(g.data[ti])[off]);
+    return reinterpret_cast<const float*>(g.data[ti])[off];
+}
+
+// Order-preserving map of fp32 bit patterns to unsigned keys.
+__device__ __forceinline__ uint32_t f32_key(float v) {
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_f32(uint32_t k) {
+    const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+
+// Rank of point j of the k-point empirical-quantile grid over n sorted
+// entries: j (n-1)/(k-1) rounded half up.
+__host__ __device__ __forceinline__ int quantile_rank(int j, int k, int n) {
+    return (2 * j * (n - 1) + (k - 1)) / (2 * (k - 1));
+}
+
+// Point j of the k-point uniform grid on [mn, mx]: fp64 round-to-nearest
+// mn + ((mx - mn) * j) / (k - 1) with no contraction, then fp32.
+__device__ __forceinline__ float uniform_point(float mn, float mx, int j, int k) {
+#pragma clang fp contract(off)
+    const double dmn = (double)mn;
+    const double span = (double)mx - dmn;
+    const double v = dmn + (span * (double)j) / (double)(k - 1);
+    return (float)v;
+}
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32x32->64 multiplies with the published multipliers, Weyl key schedule.
+__device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2,
+                                              uint32_t& c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int rnd = 0; rnd < 10; ++rnd) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c0 = n0;
+        c1 = (uint32_t)p1;
+        c2 = n2;
+        c3 = (uint32_t)p0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+}
+
+__host__ __device__ __forceinline__ int code_width(int m) {
+    int w = 0;
+    while ((1 << w) < m) ++w;
+    return w;
+}
+
+// Index of the pair (i < j) of a 12-point alphabet, row-major upper triangle.
+__host__ __device__ __forceinline__ int pair_index(int i, int j) {
+    return i * (2 * kAlpha - i - 1) / 2 + (j - i - 1);
+}
+
+// Quantile-rank lookup: stats column of rank quantile_rank(j, k, n).
+struct RankTable {
+    uint8_t col[kMaxS + 1][kMaxS];
+    int32_t rank[kMaxStats];
+    int32_t n_stats;
+};
+
+// ---- host-side launchers (defined in the kernel files) ----
+hipError_t launch_eval_grids(const Geom& g, int64_t R, int s, const RankTable& rt, double* D,
+                             double* H, float* stats, void* ws, hipStream_t st);
+hipError_t launch_eval_alphabet(const Geom& g, int64_t R, int alpha_m, double* D, double* H,
+                                float* stats, void* ws, hipStream_t st);
+hipError_t launch_ws_reset(void* ws, hipStream_t st);
+hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
+                        const double* H, const float* stats, double B, int mode, int iters,
+                        double lam_in, int32_t* choice, float* codebook, uint8_t* m,
+                        uint64_t* off, void* ws, hipStream_t st);
+hipError_t launch_quantize(const Geom& g, int64_t R, int s, const float* codebook,
+                           const uint8_t* m, const uint64_t* off, uint64_t seed,
+                           uint32_t* codes, hipStream_t st);
+hipError_t launch_dequantize(int64_t R, int n, int s, const uint32_t* codes,
+                             const float* codebook, const uint8_t* m, const uint64_t* off,
+                             float* xhat, hipStream_t st);
+
+}  // namespace kvq

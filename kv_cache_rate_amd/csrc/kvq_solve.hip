@@ -1,0 +1,548 @@
+// The global multiplier and each block's codebook (kvq_solve_lambda).
+//
+// Page "Rate-adaptive KV-cache quantizer", Key formulas (1)-(2): for a fixed
+// lambda every block minimises D_r + lambda d_r H_r on its own, so the
+// modelled rate R(lambda) = sum_r d_r H_r(choice_r(lambda)) is a sum of
+// independent per-block terms; Key formulas (4) gives the projected
+// subgradient step.  The bisection on lambda follows the page "Joint
+// Tucker-rank and residual-bit KV allocator" (Mathematical statement).
+//
+// Device design: a "rates" pass evaluates R at up to 64 multipliers at once
+// (one read of the score table per pass).  A one-thread "select" kernel then
+// advances the bracket held in the workspace header, so the whole search runs
+// without a host round trip:
+//   pass 0: lambda in {0, 2^0, ..., 2^62}; the first feasible power gives the
+//           doubling bracket exactly as sequential doubling from [0, 1] would;
+//   pass 1: {2^63, 2^64} only if none of those was feasible;
+//   passes 2..: the 2^b - 1 interior points of a dyadic grid over the
+//           bracket (b <= 6); the b halvings of sequential bisection are then
+//           replayed on those values (every midpoint it would probe is one of
+//           them, and all are exact in fp64), so 40 halvings take 7 passes
+//           and give the same final bracket bit for bit.
+// Rates are summed as unsigned fixed point (d_r H_r scaled by 2^shift and
+// rounded), so the sum is exact and independent of summation order.
+#include "kvq_internal.h"
+
+namespace kvq {
+
+constexpr int kSolveThreads = 256;
+constexpr int kScanPer = 4;
+constexpr int kScanTile = kSolveThreads * kScanPer;
+
+enum Phase : int32_t { kPhaseDouble = 0, kPhaseDouble2 = 1, kPhaseMulti = 2, kPhaseSubgrad = 10 };
+
+// Objective D + (lambda * d) * H, evaluated without contraction.
+__device__ __forceinline__ double objective(double Dv, double Hv, double lamd) {
+#pragma clang fp contract(off)
+    const double t = lamd * Hv;
+    return Dv + t;
+}
+
+__device__ __forceinline__ unsigned long long rate_fx(double d, double Hv, int shift) {
+    return __double2ull_rn(ldexp(d * Hv, shift));
+}
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_down(v, off, 64);
+    return v;
+}
+
+__global__ void solve_init_kernel(WsHeader* h, int mode, double lam_in, unsigned long long Btot_fx,
+                                  int iters) {
+    if (threadIdx.x != 0) return;
+    h->done = 0;
+    h->err = 0;
+    h->Btot_fx = Btot_fx;
+    h->bits_left = iters;
+    h->rate_final = 0;
+    for (int j = 0; j < kMaxLam + 8; ++j) h->sums[j] = 0ull;
+    if (mode == KVQ_SUBGRAD) {
+        h->phase = kPhaseSubgrad;
+        h->nlam = 1;
+        h->lam[0] = lam_in;
+    } else {
+        h->phase = kPhaseDouble;
+        h->nlam = kMaxLam;
+        h->lam[0] = 0.0;
+        for (int j = 1; j < kMaxLam; ++j) h->lam[j] = ldexp(1.0, j - 1);
+    }
+}
+
+__device__ void setup_multisection(WsHeader* h) {
+    if (h->bits_left <= 0) {
+        h->lam_final = h->hi;
+        h->done = 1;
+        h->nlam = 0;
+        return;
+    }
+    const int b = h->bits_left < 6 ? h->bits_left : 6;
+    const int pts = (1 << b) - 1;
+    const double lo = h->lo, width = h->hi - h->lo;
+    for (int i = 1; i <= pts; ++i) h->lam[i - 1] = lo + (width * (double)i) / (double)(1 << b);
+    h->bits_now = b;
+    h->nlam = pts;
+    h->phase = kPhaseMulti;
+}
+
+__global__ void solve_select_kernel(WsHeader* h) {
+    if (threadIdx.x != 0 || h->done) return;
+    const unsigned long long B = h->Btot_fx;
+    switch (h->phase) {
+    case kPhaseSubgrad:
+        h->lam_final = h->lam[0];
+        h->done = 1;
+        break;
+    case kPhaseDouble: {
+        if (h->sums[0] <= B) {
+            h->lam_final = 0.0;
+            h->done = 1;
+            break;
+        }
+        int first = -1;
+        for (int j = 1; j < kMaxLam; ++j)
+            if (h->sums[j] <= B) {
+                first = j;
+                break;
+            }
+        if (first > 0) {
+            h->hi = h->lam[first];
+            h->lo = first == 1 ? 0.0 : h->lam[first - 1];
+            setup_multisection(h);
+        } else {
+            h->phase = kPhaseDouble2;
+            h->nlam = 2;
+            h->lam[0] = ldexp(1.0, 63);
+            h->lam[1] = ldexp(1.0, 64);
+        }
+        break;
+    }
+    case kPhaseDouble2:
+        if (h->sums[0] <= B) {
+            h->lo = ldexp(1.0, 62);
+            h->hi = ldexp(1.0, 63);
+            setup_multisection(h);
+        } else if (h->sums[1] <= B) {
+            h->lo = ldexp(1.0, 63);
+            h->hi = ldexp(1.0, 64);
+            setup_multisection(h);
+        } else {
+            h->err = KVQ_EINFEASIBLE;
+            h->done = 1;
+            h->nlam = 0;
+        }
+        break;
+    case kPhaseMulti: {
+        const int b = h->bits_now;
+        int l = 0, u = 1 << b;
+        for (int step = 0; step < b; ++step) {
+            const int mid = (l + u) >> 1;
+            if (h->sums[mid - 1] <= B) u = mid;
+            else l = mid;
+        }
+        const double lo = h->lo, width = h->hi - h->lo;
+        h->lo = lo + (width * (double)l) / (double)(1 << b);
+        h->hi = lo + (width * (double)u) / (double)(1 << b);
+        h->bits_left -= b;
+        setup_multisection(h);
+        break;
+    }
+    default:
+        h->err = KVQ_EINVAL;
+        h->done = 1;
+    }
+    for (int j = 0; j < kMaxLam + 8; ++j) h->sums[j] = 0ull;
+}
+
+// ---------------------------------------------------------------- grids ----
+
+__global__ void __launch_bounds__(kSolveThreads)
+rates_grids_kernel(const double* __restrict__ D, const double* __restrict__ H, int64_t R, int C,
+                   double d, int shift, WsHeader* h) {
+    __shared__ unsigned long long part[kSolveThreads / 64][kMaxLam];
+    const int nlam = h->nlam;
+    if (h->done || nlam == 0) return;
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    double Dr[kMaxCand], Hr[kMaxCand];
+    if (r < R) {
+#pragma unroll
+        for (int c = 0; c < kMaxCand; ++c) {
+            if (c < C) {
+                Dr[c] = D[r * C + c];
+                Hr[c] = H[r * C + c];
+            }
+        }
+    }
+    const int wave = threadIdx.x >> 6;
+    for (int j = 0; j < nlam; ++j) {
+        unsigned long long v = 0;
+        if (r < R) {
+            const double lamd = h->lam[j] * d;
+            double best = objective(Dr[0], Hr[0], lamd);
+            double bh = Hr[0];
+#pragma unroll
+            for (int c = 1; c < kMaxCand; ++c) {
+                if (c < C) {
+                    const double o = objective(Dr[c], Hr[c], lamd);
+                    if (o < best) {
+                        best = o;
+                        bh = Hr[c];
+                    }
+                }
+            }
+            v = rate_fx(d, bh, shift);
+        }
+        v = wave_sum_u64(v);
+        if ((threadIdx.x & 63) == 0) part[wave][j] = v;
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < nlam; j += blockDim.x) {
+        unsigned long long t = 0;
+        for (int w = 0; w < kSolveThreads / 64; ++w) t += part[w][j];
+        atomicAdd(&h->sums[j], t);
+    }
+}
+
+// Codepoints of grid candidate c of a block from its order statistics.
+__device__ int build_grid_codebook(int c, const float* st, const RankTable& rt, int n, float* q) {
+    const float mn = st[0];
+    const float mx = st[rt.n_stats - 1];
+    if (mn == mx) {
+        q[0] = mn;
+        return 1;
+    }
+    int k;
+    bool uni = false;
+    if (c == 0) {
+        k = 2;
+    } else {
+        k = 3 + (c - 1) / 2;
+        uni = ((c - 1) & 1) == 0;
+    }
+    int m = 0;
+    for (int j = 0; j < k; ++j) {
+        float v;
+        if (c == 0) v = j == 0 ? mn : mx;
+        else if (uni) v = uniform_point(mn, mx, j, k);
+        else v = st[rt.col[k][j]];
+        if (m == 0 || v != q[m - 1]) q[m++] = v;
+    }
+    return m;
+}
+
+__global__ void __launch_bounds__(kSolveThreads)
+final_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
+                   const float* __restrict__ stats, int64_t R, int C, int s, int n, int shift,
+                   RankTable rt, WsHeader* h, int32_t* __restrict__ choice,
+                   float* __restrict__ codebook, uint8_t* __restrict__ m_out,
+                   uint64_t* __restrict__ off) {
+    __shared__ unsigned long long part[kSolveThreads / 64];
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r == 0) off[0] = 0;
+    unsigned long long v = 0;
+    if (r < R && h->err) {
+        // no feasible multiplier: leave a well-formed empty result
+        choice[r] = -1;
+        m_out[r] = 1;
+        for (int j = 0; j < s; ++j) codebook[r * s + j] = 0.0f;
+        off[r + 1] = 0;
+    } else if (r < R) {
+        const double d = (double)n;
+        const double lamd = h->lam_final * d;
+        const double* Dr = D + r * C;
+        const double* Hr = H + r * C;
+        double best = objective(Dr[0], Hr[0], lamd);
+        int bc = 0;
+        for (int c = 1; c < C; ++c) {
+            const double o = objective(Dr[c], Hr[c], lamd);
+            if (o < best) {
+                best = o;
+                bc = c;
+            }
+        }
+        v = rate_fx(d, Hr[bc], shift);
+        float q[kMaxS];
+        const int m = build_grid_codebook(bc, stats + r * rt.n_stats, rt, n, q);
+        choice[r] = bc;
+        m_out[r] = (uint8_t)m;
+        for (int j = 0; j < s; ++j) codebook[r * s + j] = j < m ? q[j] : 0.0f;
+        const int w = code_width(m);
+        off[r + 1] = ((uint64_t)n * (uint64_t)w + 31u) / 32u;
+    }
+    v = wave_sum_u64(v);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned long long t = 0;
+        for (int w = 0; w < kSolveThreads / 64; ++w) t += part[w];
+        atomicAdd(&h->rate_final, t);
+    }
+}
+
+// ------------------------------------------------------------ exact DP ----
+
+__device__ __forceinline__ double hbits(double p) { return p > 0.0 ? -p * log2(p) : 0.0; }
+
+// Pair-state dynamic program over the distinct alphabet A (m points):
+// f[i][j] is the best cost of a chain from point 0 whose last two points are
+// i < j, holding the distortion of its closed intervals and the entropy terms
+// of every point before j (a point's frequency needs both neighbours).
+// Rows are updated in place for descending j.  Returns the best objective and
+// the chain's bitmask.
+__device__ double dp_min(const double* Dp, const double* Mlr, int m, int smax, double inv_n,
+                         double w, uint32_t& best_mask) {
+    double f[kAlpha][kAlpha];
+    uint32_t mk[kAlpha][kAlpha];
+    const double INF = __builtin_huge_val();
+    if (m <= 1) {
+        best_mask = 1u;
+        return 0.0;
+    }
+    for (int i = 0; i < kAlpha; ++i)
+        for (int j = 0; j < kAlpha; ++j) {
+            f[i][j] = INF;
+            mk[i][j] = 0u;
+        }
+    for (int l = 1; l < m; ++l) {
+        const int p = pair_index(0, l);
+        f[0][l] = Dp[p] + w * hbits(Mlr[2 * p] * inv_n);
+        mk[0][l] = 1u | (1u << l);
+    }
+    double best = INF;
+    best_mask = 0u;
+    const int cmax = smax < m ? smax : m;
+    for (int c = 2;; ++c) {
+        for (int i = 0; i < m - 1; ++i) {
+            if (f[i][m - 1] < INF) {
+                const double tot = f[i][m - 1] + w * hbits(Mlr[2 * pair_index(i, m - 1) + 1] * inv_n);
+                if (tot < best) {
+                    best = tot;
+                    best_mask = mk[i][m - 1];
+                }
+            }
+        }
+        if (c >= cmax) break;
+        for (int j = m - 2; j >= 1; --j) {
+            for (int l = m - 1; l > j; --l) {
+                const int pjl = pair_index(j, l);
+                const double mass_right = Mlr[2 * pjl];
+                double bv = INF;
+                uint32_t bm = 0u;
+                for (int i = 0; i < j; ++i) {
+                    if (f[i][j] < INF) {
+                        const double v = f[i][j] +
+                                         w * hbits((Mlr[2 * pair_index(i, j) + 1] + mass_right) * inv_n);
+                        if (v < bv) {
+                            bv = v;
+                            bm = mk[i][j];
+                        }
+                    }
+                }
+                f[j][l] = bv < INF ? bv + Dp[pjl] : INF;
+                mk[j][l] = bm | (1u << l);
+            }
+        }
+        for (int l = 0; l < kAlpha; ++l) f[0][l] = INF;
+    }
+    return best;
+}
+
+// Entropy (bits per entry) of the subset given by mask.
+__device__ double subset_entropy(const double* Mlr, int m, uint32_t mask, double inv_n) {
+    int prev = -1;
+    double Hs = 0.0;
+    int pts[kAlpha];
+    int k = 0;
+    for (int i = 0; i < m; ++i)
+        if (mask & (1u << i)) pts[k++] = i;
+    if (k <= 1) return 0.0;
+    for (int t = 0; t < k; ++t) {
+        double mass = 0.0;
+        if (t > 0) mass += Mlr[2 * pair_index(pts[t - 1], pts[t]) + 1];
+        if (t + 1 < k) mass += Mlr[2 * pair_index(pts[t], pts[t + 1])];
+        Hs += hbits(mass * inv_n);
+    }
+    (void)prev;
+    return Hs;
+}
+
+__device__ int distinct_alphabet(const float* st, int alpha_m, float* A) {
+    int m = 0;
+    for (int j = 0; j < alpha_m; ++j)
+        if (m == 0 || st[j] != A[m - 1]) A[m++] = st[j];
+    return m;
+}
+
+__global__ void __launch_bounds__(64)
+rates_dp_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr,
+                const float* __restrict__ stats, int64_t R, int alpha_m, int smax, int n,
+                int shift, WsHeader* h) {
+    const int nlam = h->nlam;
+    if (h->done || nlam == 0) return;
+    const int64_t r = blockIdx.x;
+    const int j = threadIdx.x;
+    if (j >= nlam) return;
+    float A[kAlpha];
+    const int m = distinct_alphabet(stats + r * alpha_m, alpha_m, A);
+    const double inv_n = 1.0 / (double)n;
+    const double w = h->lam[j] * (double)n;
+    uint32_t mask;
+    dp_min(Dp + r * kPairs, Mlr + r * kPairs * 2, m, smax, inv_n, w, mask);
+    const double Hs = subset_entropy(Mlr + r * kPairs * 2, m, mask, inv_n);
+    atomicAdd(&h->sums[j], rate_fx((double)n, Hs, shift));
+}
+
+__global__ void __launch_bounds__(kSolveThreads)
+final_dp_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr,
+                const float* __restrict__ stats, int64_t R, int alpha_m, int smax, int s, int n,
+                int shift, WsHeader* h, int32_t* __restrict__ choice, float* __restrict__ codebook,
+                uint8_t* __restrict__ m_out, uint64_t* __restrict__ off) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r == 0) off[0] = 0;
+    if (r >= R) return;
+    if (h->err) {
+        choice[r] = -1;
+        m_out[r] = 1;
+        for (int j = 0; j < s; ++j) codebook[r * s + j] = 0.0f;
+        off[r + 1] = 0;
+        return;
+    }
+    float A[kAlpha];
+    const int m = distinct_alphabet(stats + r * alpha_m, alpha_m, A);
+    const double inv_n = 1.0 / (double)n;
+    const double w = h->lam_final * (double)n;
+    uint32_t mask;
+    dp_min(Dp + r * kPairs, Mlr + r * kPairs * 2, m, smax, inv_n, w, mask);
+    const double Hs = subset_entropy(Mlr + r * kPairs * 2, m, mask, inv_n);
+    atomicAdd(&h->rate_final, rate_fx((double)n, Hs, shift));
+    int k = 0;
+    for (int i = 0; i < m; ++i)
+        if (mask & (1u << i)) codebook[r * s + k++] = A[i];
+    for (int j = k; j < s; ++j) codebook[r * s + j] = 0.0f;
+    choice[r] = (int32_t)mask;
+    m_out[r] = (uint8_t)k;
+    off[r + 1] = ((uint64_t)n * (uint64_t)code_width(k) + 31u) / 32u;
+}
+
+// --------------------------------------------------------- offsets scan ----
+
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Block-wide inclusive scan of one value per thread; returns the inclusive
+// value and the block total.
+__device__ uint64_t block_incl_scan(uint64_t v, uint64_t& total) {
+    __shared__ uint64_t wsum[kSolveThreads / 64];
+    const uint64_t inc = wave_incl_scan_u64(v);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 63) wsum[wave] = inc;
+    __syncthreads();
+    uint64_t pre = 0, tot = 0;
+    for (int w = 0; w < kSolveThreads / 64; ++w) {
+        if (w < wave) pre += wsum[w];
+        tot += wsum[w];
+    }
+    __syncthreads();
+    total = tot;
+    return pre + inc;
+}
+
+// Inclusive scan of off[1..R] inside tiles of kScanTile entries.
+__global__ void __launch_bounds__(kSolveThreads)
+scan_tiles_kernel(uint64_t* off, int64_t R, uint64_t* tile_sums) {
+    const int64_t base = (int64_t)blockIdx.x * kScanTile;
+    uint64_t vals[kScanPer];
+    uint64_t run = 0;
+    for (int k = 0; k < kScanPer; ++k) {
+        const int64_t i = base + threadIdx.x * kScanPer + k;
+        vals[k] = i < R ? off[i + 1] : 0;
+        run += vals[k];
+        vals[k] = run;
+    }
+    uint64_t total;
+    const uint64_t inc = block_incl_scan(run, total);
+    const uint64_t pre = inc - run;
+    for (int k = 0; k < kScanPer; ++k) {
+        const int64_t i = base + threadIdx.x * kScanPer + k;
+        if (i < R) off[i + 1] = pre + vals[k];
+    }
+    if (threadIdx.x == 0) tile_sums[blockIdx.x] = total;
+}
+
+// Exclusive scan of the tile sums (one workgroup, any count).
+__global__ void __launch_bounds__(kSolveThreads)
+scan_sums_kernel(uint64_t* tile_sums, int64_t T) {
+    uint64_t carry = 0;
+    for (int64_t base = 0; base < T; base += kSolveThreads) {
+        const int64_t i = base + threadIdx.x;
+        const uint64_t v = i < T ? tile_sums[i] : 0;
+        uint64_t total;
+        const uint64_t inc = block_incl_scan(v, total);
+        if (i < T) tile_sums[i] = carry + inc - v;
+        carry += total;
+        __syncthreads();
+    }
+}
+
+__global__ void __launch_bounds__(kSolveThreads)
+scan_add_kernel(uint64_t* off, int64_t R, const uint64_t* tile_sums) {
+    const int64_t tile = blockIdx.x;
+    const uint64_t add = tile_sums[tile];
+    for (int k = 0; k < kScanPer; ++k) {
+        const int64_t i = tile * kScanTile + threadIdx.x * kScanPer + k;
+        if (i < R) off[i + 1] += add;
+    }
+}
+
+// ----------------------------------------------------------------- host ----
+
+hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D, const double* H,
+                        const float* stats, double B, int mode, int iters, double lam_in,
+                        int32_t* choice, float* codebook, uint8_t* m, uint64_t* off, void* ws,
+                        hipStream_t st) {
+    WsHeader* h = (WsHeader*)ws;
+    const int64_t R = p.n_blocks;
+    const int n = p.d_block;
+    const int shift = p.rate_shift;
+    const double Btot = B * (double)p.n_entries;
+    const double Bfx = ldexp(Btot, shift);
+    const unsigned long long Btot_fx =
+        Bfx >= 18446744073709551615.0 ? ~0ull : (unsigned long long)floor(Bfx);
+    hipLaunchKernelGGL(solve_init_kernel, dim3(1), dim3(64), 0, st, h, mode, lam_in, Btot_fx, iters);
+    const int passes = mode == KVQ_SUBGRAD ? 1 : 2 + (iters + 5) / 6;
+    const unsigned grid = (unsigned)((R + kSolveThreads - 1) / kSolveThreads);
+    for (int ps = 0; ps < passes; ++ps) {
+        if (p.search == KVQ_GRIDS) {
+            hipLaunchKernelGGL(rates_grids_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, R,
+                               p.n_cand, (double)n, shift, h);
+        } else {
+            hipLaunchKernelGGL(rates_dp_kernel, dim3((unsigned)R), dim3(64), 0, st, D, H, stats, R,
+                               p.alphabet_m, p.s, n, shift, h);
+        }
+        hipLaunchKernelGGL(solve_select_kernel, dim3(1), dim3(64), 0, st, h);
+    }
+    if (p.search == KVQ_GRIDS) {
+        hipLaunchKernelGGL(final_grids_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, stats, R,
+                           p.n_cand, p.s, n, shift, rt, h, choice, codebook, m, off);
+    } else {
+        hipLaunchKernelGGL(final_dp_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, stats, R,
+                           p.alphabet_m, p.s, p.s, n, shift, h, choice, codebook, m, off);
+    }
+    const int64_t tiles = (R + kScanTile - 1) / kScanTile;
+    uint64_t* tile_sums = (uint64_t*)((char*)ws + kWsHeaderBytes);
+    hipLaunchKernelGGL(scan_tiles_kernel, dim3((unsigned)tiles), dim3(kSolveThreads), 0, st, off, R,
+                       tile_sums);
+    hipLaunchKernelGGL(scan_sums_kernel, dim3(1), dim3(kSolveThreads), 0, st, tile_sums, tiles);
+    hipLaunchKernelGGL(scan_add_kernel, dim3((unsigned)tiles), dim3(kSolveThreads), 0, st, off, R,
+                       tile_sums);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,247 @@
+"""Thin ctypes binding of libkvq (include/kvq.h).
+
+The functions keep the C names (``kvq_plan_blocks``, ``kvq_eval_candidates``,
+``kvq_solve_lambda``, ``kvq_quantize_pack``, ``kvq_dequantize``) and only
+marshal arguments: every step of the computation runs in the HIP kernels of
+``libkvq.so``.  PyTorch provides device memory and the current stream.  The
+library is loaded on first use; if it is missing the call raises (there is
+no CPU fallback).
+"""
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkvq.so")
+
+KVQ_OK = 0
+KVQ_EINVAL = -1
+KVQ_EINFEASIBLE = -2
+KVQ_ENONFINITE = -3
+KVQ_ENOSPC = -4
+KVQ_EHIP = -5
+
+KVQ_F16 = 1
+KVQ_F32 = 2
+KVQ_GRIDS = 0
+KVQ_EXACT_DP = 1
+KVQ_BISECT = 0
+KVQ_SUBGRAD = 1
+
+EXPORTED = ("kvq_status_string", "kvq_last_error", "kvq_plan_blocks", "kvq_eval_candidates",
+            "kvq_solve_lambda", "kvq_quantize_pack", "kvq_dequantize")
+
+
+class KvqTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("pad_", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class KvqBlockSpec(ctypes.Structure):
+    _fields_ = [("tokens_per_block", ctypes.c_int32), ("dims_per_block", ctypes.c_int32),
+                ("s", ctypes.c_int32), ("search", ctypes.c_int32), ("alphabet_m", ctypes.c_int32)]
+
+
+class KvqPlan(ctypes.Structure):
+    _fields_ = [("n_blocks", ctypes.c_int64), ("n_entries", ctypes.c_int64),
+                ("d_block", ctypes.c_int32), ("n_cand", ctypes.c_int32),
+                ("n_stats", ctypes.c_int32), ("s", ctypes.c_int32), ("search", ctypes.c_int32),
+                ("alphabet_m", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("n_tensors", ctypes.c_int32), ("tokens_per_block", ctypes.c_int32),
+                ("dims_per_block", ctypes.c_int32),
+                ("tensor_blocks", ctypes.c_int64 * 2), ("shape", (ctypes.c_int64 * 4) * 2),
+                ("D_bytes", ctypes.c_size_t), ("H_bytes", ctypes.c_size_t),
+                ("stats_bytes", ctypes.c_size_t), ("choice_bytes", ctypes.c_size_t),
+                ("codebook_bytes", ctypes.c_size_t), ("m_bytes", ctypes.c_size_t),
+                ("offsets_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t),
+                ("max_code_words", ctypes.c_uint64), ("rate_shift", ctypes.c_int32),
+                ("pad_", ctypes.c_int32)]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__(f"{status_string(status)} ({detail})")
+        self.status = status
+        self.detail = detail
+
+
+_LIB = None
+
+
+def lib():
+    """Load libkvq.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m kv_cache_rate_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, u64, f64 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_uint64, ctypes.c_double)
+        L.kvq_status_string.restype = ctypes.c_char_p
+        L.kvq_status_string.argtypes = [i32]
+        L.kvq_last_error.restype = ctypes.c_char_p
+        L.kvq_last_error.argtypes = []
+        L.kvq_plan_blocks.restype = i32
+        L.kvq_plan_blocks.argtypes = [ctypes.POINTER(KvqTensor), i32, ctypes.POINTER(KvqBlockSpec),
+                                      ctypes.POINTER(KvqPlan)]
+        L.kvq_eval_candidates.restype = i32
+        L.kvq_eval_candidates.argtypes = [ctypes.POINTER(KvqPlan), ctypes.POINTER(KvqTensor), i32,
+                                          vp, vp, vp, vp, vp]
+        L.kvq_solve_lambda.restype = i32
+        L.kvq_solve_lambda.argtypes = [ctypes.POINTER(KvqPlan), vp, vp, vp, f64, i32, i32, f64,
+                                       ctypes.POINTER(f64), ctypes.POINTER(f64), vp, vp, vp, vp,
+                                       vp, vp]
+        L.kvq_quantize_pack.restype = i32
+        L.kvq_quantize_pack.argtypes = [ctypes.POINTER(KvqPlan), ctypes.POINTER(KvqTensor), i32,
+                                        vp, vp, vp, u64, vp, u64, vp]
+        L.kvq_dequantize.restype = i32
+        L.kvq_dequantize.argtypes = [ctypes.POINTER(KvqPlan), vp, vp, vp, vp, vp, vp]
+        _LIB = L
+    return _LIB
+
+
+def status_string(st):
+    return lib().kvq_status_string(st).decode()
+
+
+def last_error():
+    return lib().kvq_last_error().decode()
+
+
+def _check(st):
+    if st != KVQ_OK:
+        raise KvqError(st, last_error())
+
+
+def _dtype_code(t):
+    name = str(getattr(t, "dtype", ""))
+    if name.endswith("float16"):
+        return KVQ_F16
+    if name.endswith("float32"):
+        return KVQ_F32
+    raise ValueError(f"unsupported KV dtype {name}")
+
+
+def as_kvq_tensor(t):
+    """Describe a 4-D torch tensor (or numpy array, for planning only)."""
+    if t.ndim != 4:
+        raise ValueError("KV tensors are [outer, heads, tokens, dim]")
+    kt = KvqTensor()
+    if hasattr(t, "data_ptr"):
+        kt.data = t.data_ptr()
+        strides = t.stride()
+    else:  # numpy: planning reads shapes and strides only
+        kt.data = t.ctypes.data
+        strides = tuple(s // t.itemsize for s in t.strides)
+    kt.dtype = _dtype_code(t)
+    for d in range(4):
+        kt.shape[d] = t.shape[d]
+        kt.stride[d] = strides[d]
+    return kt
+
+
+def _tensor_array(tensors):
+    arr = (KvqTensor * len(tensors))()
+    for i, t in enumerate(tensors):
+        arr[i] = as_kvq_tensor(t)
+    return arr
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    return x.data_ptr() if hasattr(x, "data_ptr") else int(x)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def kvq_plan_blocks(tensors, tokens_per_block, dims_per_block, s, search=KVQ_GRIDS, alphabet_m=0):
+    spec = KvqBlockSpec(tokens_per_block, dims_per_block, s, search, alphabet_m)
+    plan = KvqPlan()
+    arr = _tensor_array(tensors)
+    _check(lib().kvq_plan_blocks(arr, len(tensors), ctypes.byref(spec), ctypes.byref(plan)))
+    return plan
+
+
+def kvq_eval_candidates(plan, tensors, D, H, stats, workspace, stream=None):
+    arr = _tensor_array(tensors)
+    _check(lib().kvq_eval_candidates(ctypes.byref(plan), arr, len(tensors), _ptr(D), _ptr(H),
+                                     _ptr(stats), _ptr(workspace), _stream(stream)))
+
+
+def kvq_solve_lambda(plan, D, H, stats, B, mode, iters, eta, lam, choice, codebook, m, word_off,
+                     workspace, stream=None):
+    """Returns ``(lambda, rate_bits_per_entry)``."""
+    lam_io = ctypes.c_double(lam)
+    rate = ctypes.c_double(0.0)
+    _check(lib().kvq_solve_lambda(ctypes.byref(plan), _ptr(D), _ptr(H), _ptr(stats), float(B), mode,
+                                  iters, float(eta), ctypes.byref(lam_io), ctypes.byref(rate),
+                                  _ptr(choice), _ptr(codebook), _ptr(m), _ptr(word_off),
+                                  _ptr(workspace), _stream(stream)))
+    return lam_io.value, rate.value
+
+
+def kvq_quantize_pack(plan, tensors, codebook, m, word_off, seed, codes, capacity_words=None,
+                      stream=None):
+    arr = _tensor_array(tensors)
+    cap = capacity_words if capacity_words is not None else codes.numel()
+    _check(lib().kvq_quantize_pack(ctypes.byref(plan), arr, len(tensors), _ptr(codebook), _ptr(m),
+                                   _ptr(word_off), int(seed), _ptr(codes), int(cap),
+                                   _stream(stream)))
+
+
+def kvq_dequantize(plan, codes, codebook, m, word_off, xhat, stream=None):
+    _check(lib().kvq_dequantize(ctypes.byref(plan), _ptr(codes), _ptr(codebook), _ptr(m),
+                                _ptr(word_off), _ptr(xhat), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Buffer allocation and chaining (marshalling only; no arithmetic).
+
+def allocate(plan, device="cuda", dequant=False):
+    """Device buffers of the sizes ``plan`` asks for, as torch tensors.
+
+    64-bit offsets are held in an int64 tensor and codes in an int32 tensor
+    (same bits as the uint64 / uint32 the library writes)."""
+    import torch
+    R = plan.n_blocks
+    if plan.search == KVQ_GRIDS:
+        D = torch.empty((R, plan.n_cand), dtype=torch.float64, device=device)
+        H = torch.empty((R, plan.n_cand), dtype=torch.float64, device=device)
+    else:
+        D = torch.empty((R, plan.n_cand), dtype=torch.float64, device=device)
+        H = torch.empty((R, plan.n_cand, 2), dtype=torch.float64, device=device)
+    buf = {
+        "D": D, "H": H,
+        "stats": torch.empty((R, plan.n_stats), dtype=torch.float32, device=device),
+        "choice": torch.empty(R, dtype=torch.int32, device=device),
+        "codebook": torch.empty((R, plan.s), dtype=torch.float32, device=device),
+        "m": torch.empty(R, dtype=torch.uint8, device=device),
+        "off": torch.empty(R + 1, dtype=torch.int64, device=device),
+        "workspace": torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=device),
+        "codes": torch.empty(max(1, plan.max_code_words), dtype=torch.int32, device=device),
+    }
+    if dequant:
+        buf["xhat"] = torch.empty((R, plan.d_block), dtype=torch.float32, device=device)
+    return buf
+
+
+def admit(plan, tensors, buf, B, mode=KVQ_BISECT, iters=40, eta=1e-3, lam=0.0, seed=0,
+          stream=None, dequant=False):
+    """Chain eval -> solve -> quantize_pack (-> dequantize) on ``buf``.
+    Returns ``(lambda, rate_bits_per_entry)``."""
+    kvq_eval_candidates(plan, tensors, buf["D"], buf["H"], buf["stats"], buf["workspace"], stream)
+    lam, rate = kvq_solve_lambda(plan, buf["D"], buf["H"], buf["stats"], B, mode, iters, eta, lam,
+                                 buf["choice"], buf["codebook"], buf["m"], buf["off"],
+                                 buf["workspace"], stream)
+    kvq_quantize_pack(plan, tensors, buf["codebook"], buf["m"], buf["off"], seed, buf["codes"],
+                      stream=stream)
+    if dequant:
+        kvq_dequantize(plan, buf["codes"], buf["codebook"], buf["m"], buf["off"], buf["xhat"], stream)
+    return lam, rate

@@ -91,7 +91,7 @@ def run(blocks, *, search="grids", s=16, alphabet_m=12, B=2.0, mode="bisect",
     out = {"n": n, "R": R}
     if search == "grids":
         D, H, stats, books = eval_grids(blocks, s, processes)
-        out.update(D=D, H=H, stats=stats)
+        out.update(D=D, H=H, stats=stats, books=books)
         Dt, Ht = D, H
     elif search == "exact_dp":
         ev = eval_exact(blocks, alphabet_m, s, processes)

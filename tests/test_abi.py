@@ -1,0 +1,121 @@
+"""The C-ABI library loads, exports every declared symbol, and validates
+arguments on the host (CPU only: no call here touches a GPU)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from kv_cache_rate_amd import kvq
+from kv_cache_rate_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(kvq_[a-z_]+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kvq.LIB_PATH):
+        pytest.fail("libkvq.so is not built (run python -m kv_cache_rate_amd.build)")
+    return kvq.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(kvq.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def test_status_strings(L):
+    for st in (0, -1, -2, -3, -4, -5):
+        assert kvq.status_string(st).startswith("KVQ_")
+    assert "unknown" in kvq.status_string(7)
+
+
+def _np(shape, dtype=np.float16):
+    return np.zeros(shape, dtype=dtype)
+
+
+@pytest.mark.parametrize("w", W.WORKLOADS, ids=[w.name for w in W.WORKLOADS])
+def test_plan_sizes(L, w):
+    ts = [np.lib.stride_tricks.as_strided(np.zeros(1, w.np_dtype), shape=shp,
+                                          strides=(0, 0, 0, 0)) for _, shp in w.tensors]
+    # as_strided with zero strides would give zero element strides; give real ones
+    ts = []
+    for _, shp in w.tensors:
+        o, h, t, d = shp
+        base = np.zeros(1, dtype=w.np_dtype)
+        ts.append(np.lib.stride_tricks.as_strided(
+            base, shape=shp, strides=tuple(s * base.itemsize for s in (h * t * d, t * d, d, 1))))
+    search = kvq.KVQ_GRIDS if w.search == "grids" else kvq.KVQ_EXACT_DP
+    p = kvq.kvq_plan_blocks(ts, w.tokens_per_block, w.dims_per_block, w.s, search,
+                            w.alphabet_m if search else 0)
+    assert p.n_blocks == w.n_blocks
+    assert p.n_entries == w.n_entries
+    assert p.d_block == 4096
+    if search == kvq.KVQ_GRIDS:
+        assert p.n_cand == 1 + 2 * (w.s - 2)
+        assert p.n_stats == (73 if w.s == 16 else 19)
+        assert p.D_bytes == w.n_blocks * p.n_cand * 8
+    else:
+        assert p.n_cand == 66 and p.n_stats == 12
+    assert p.max_code_words == w.n_blocks * (4096 * (w.s - 1).bit_length() // 32)
+    assert p.codebook_bytes == w.n_blocks * w.s * 4
+    assert p.offsets_bytes == (w.n_blocks + 1) * 8
+    # the exact rate sums cannot overflow 64 bits
+    assert w.n_entries * 4 * 2.0 ** p.rate_shift < 2.0 ** 63
+
+
+def test_plan_rejects_bad_arguments(L):
+    t = np.zeros((1, 2, 64, 128), dtype=np.float16)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_plan_blocks([t], 30, 128, 16)  # 64 tokens not a multiple of 30
+    assert e.value.status == kvq.KVQ_EINVAL
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_plan_blocks([t], 32, 128, 17)  # s > 16
+    assert e.value.status == kvq.KVQ_EINVAL and "s=17" in e.value.detail
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_plan_blocks([t], 64, 128, 16)  # 8192 entries per block
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_plan_blocks([t, t.astype(np.float32)], 32, 128, 16)  # dtype mismatch
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_plan_blocks([t], 32, 128, 8, kvq.KVQ_EXACT_DP, 13)  # alphabet > 12
+    with pytest.raises(ValueError):
+        kvq.kvq_plan_blocks([t.astype(np.float64)], 32, 128, 16)
+
+
+def test_calls_validate_before_launch(L):
+    """Null pointers, mismatched tensors and short code buffers are refused on
+    the host; nothing is launched so no GPU is needed."""
+    t = np.zeros((1, 2, 64, 128), dtype=np.float16)
+    p = kvq.kvq_plan_blocks([t], 32, 128, 16)
+    lam = ctypes.c_double(0.0)
+    rate = ctypes.c_double(0.0)
+    Lb = kvq.lib()
+    arr = kvq._tensor_array([t])
+    assert Lb.kvq_eval_candidates(ctypes.byref(p), arr, 1, None, None, None, None, None) == kvq.KVQ_EINVAL
+    assert "null" in kvq.last_error()
+    other = np.zeros((1, 2, 96, 128), dtype=np.float16)
+    arr2 = kvq._tensor_array([other])
+    assert Lb.kvq_eval_candidates(ctypes.byref(p), arr2, 1, 8, 8, 8, 8, None) == kvq.KVQ_EINVAL
+    assert "shape" in kvq.last_error()
+    assert Lb.kvq_solve_lambda(ctypes.byref(p), 8, 8, 8, -1.0, 0, 40, 0.0, ctypes.byref(lam),
+                               ctypes.byref(rate), 8, 8, 8, 8, 8, None) == kvq.KVQ_EINVAL
+    assert Lb.kvq_solve_lambda(ctypes.byref(p), 8, 8, 8, 2.0, 5, 40, 0.0, ctypes.byref(lam),
+                               ctypes.byref(rate), 8, 8, 8, 8, 8, None) == kvq.KVQ_EINVAL
+    assert Lb.kvq_quantize_pack(ctypes.byref(p), arr, 1, 8, 8, 8, 0, 8, p.max_code_words - 1,
+                                None) == kvq.KVQ_ENOSPC
+    assert Lb.kvq_dequantize(ctypes.byref(p), 8, None, 8, 8, 8, None) == kvq.KVQ_EINVAL

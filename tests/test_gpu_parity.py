@@ -1,0 +1,168 @@
+"""GPU parity: the HIP library (through its C ABI) against the oracle on the
+same seeded inputs.  Bars are listed in tests/parity.py."""
+
+import sys
+
+import numpy as np
+import pytest
+
+from kv_cache_rate_amd import workloads as W
+from oracle import blocks as oblocks
+from oracle import ecasq
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _kw(w, **over):
+    kw = dict(tokens_per_block=w.tokens_per_block, dims_per_block=w.dims_per_block, s=w.s,
+              search=w.search, alphabet_m=w.alphabet_m, B=w.B, mode=w.mode, iters=w.iters,
+              eta=w.eta, seed=w.seed)
+    kw.update(over)
+    return kw
+
+
+def _check(w, tensors, **over):
+    kw = _kw(w, **over)
+    _say(f"{w.name} {kw}")
+    g = parity.run_gpu(tensors, **kw)
+    o = parity.run_oracle(tensors, **kw)
+    rep = parity.full_compare(g, o, kw["search"], kw["seed"], kw["B"], kw["mode"])
+    _say(f"{w.name} report {rep}")
+    return g, o, rep
+
+
+@pytest.mark.parametrize("B", [3.0, 0.8, 1.0, 1.2])
+def test_tiny_k_fp32(B):
+    w = W.TINY_K_FP32
+    g, o, rep = _check(w, W.generate(w), B=B)
+    if B == 3.0:
+        assert g["lam"] == 0.0  # log2 8 = 3 bits per entry never binds
+    else:
+        assert g["lam"] > 0.0
+
+
+def test_prefill_kv_fp16():
+    w = W.PREFILL_KV_FP16
+    _check(w, W.generate(w))
+
+
+def test_decode_admission_subgradient():
+    """Previous batch: bisection gives lambda_prev; measured batch: choose at
+    lambda_prev, one projected subgradient step (eta = 1e-3)."""
+    w = W.DECODE_ADMIT_FP16
+    prev = W.generate(w, which=0)
+    g0, o0, _ = _check(w, prev, mode="bisect", seed=w.extra["prev_seed"])
+    lam_prev = g0["lam"]
+    assert lam_prev == o0["lam"]
+    cur = W.generate(w, which=1)
+    g1, o1, rep = _check(w, cur, mode="subgrad", lam=lam_prev, seed=w.seed)
+    assert g1["rate_per_entry"] == pytest.approx(o1["rate_per_entry"], rel=1e-9)
+    assert g1["lam"] == pytest.approx(o1["lam"], rel=1e-12, abs=1e-15)
+
+
+def test_feature_group_exact_dp():
+    w = W.FEATURE_GROUP_EXACT_FP32
+    g, o, rep = _check(w, W.generate(w))
+    # the GPU's pair-state DP agrees with brute force on the first 64 blocks
+    assert np.array_equal(g["choice"][:64].astype(np.int64), o["mask"][:64]) or rep["ties"] > 0
+
+
+def test_long_context_one_layer():
+    """The long-context workload reduced to one layer of K and V (16384
+    blocks), same per-layer streams as the full tensors."""
+    w = W.reduced(W.LONG_CONTEXT_KV_FP16, 1)
+    _check(w, W.generate(w))
+
+
+# ------------------------------------------------------------ edge cases ---
+
+def _small(dtype, shape, rng, kind="normal"):
+    if kind == "normal":
+        x = rng.standard_normal(shape)
+    elif kind == "ties":
+        x = np.round(rng.standard_normal(shape) * 2) / 2
+    elif kind == "const":
+        x = np.full(shape, 0.75)
+    return x.astype(dtype)
+
+
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+def test_ragged_small_blocks(dtype):
+    """Blocks of 3 tokens x 32 features (96 entries: not a power of two),
+    R = 5 x 3 x 3 = 45 blocks (not a multiple of any workgroup tile)."""
+    rng = np.random.default_rng(5)
+    x = _small(dtype, (5, 3, 9, 32), rng)
+    w = W.Workload(name="ragged", index=0, tensors=(("K", x.shape),), dtype="f16",
+                   tokens_per_block=3, dims_per_block=32, s=6, search="grids", B=1.5,
+                   mode="bisect")
+    _check(w, [x])
+
+
+def test_ties_constant_and_negative_zero():
+    """fp16 ties (fewer distinct levels than k), constant blocks (one level,
+    zero-width codes) and -0 entries (equal to +0)."""
+    rng = np.random.default_rng(6)
+    x = _small(np.float16, (2, 2, 64, 128), rng, "ties")
+    x[0, 0, :32] = np.float16(0.75)          # constant block
+    x[1, 1, 32:, :64] = np.float16(-0.0)     # -0 entries
+    x[1, 1, 32:, 64:] = np.float16(0.0)
+    w = W.Workload(name="ties", index=0, tensors=(("K", x.shape),), dtype="f16",
+                   tokens_per_block=32, dims_per_block=128, s=16, search="grids", B=1.0,
+                   mode="bisect")
+    g, o, rep = _check(w, [x])
+    assert g["m"][0] == 1 and g["off"][1] == 0
+
+
+def test_strided_input():
+    """A non-contiguous view (every other head of a larger tensor)."""
+    import torch
+    rng = np.random.default_rng(8)
+    full = rng.standard_normal((1, 8, 64, 128)).astype(np.float16)
+    dev = torch.from_numpy(full).cuda()[:, ::2]
+    host = full[:, ::2]
+    kw = dict(tokens_per_block=32, dims_per_block=128, s=16, search="grids", B=2.0,
+              mode="bisect")
+    _say(f"strided {kw}")
+    g = parity.run_gpu([host], tensors_dev=[dev], **kw)
+    o = parity.run_oracle([np.ascontiguousarray(host)], **kw)
+    parity.full_compare(g, o, "grids", 0, 2.0)
+
+
+def test_nonfinite_and_infeasible_are_reported():
+    import torch
+    from kv_cache_rate_amd import kvq
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((1, 2, 32, 128)).astype(np.float16)
+    x[0, 1, 5, 7] = np.nan
+    dev = [torch.from_numpy(x).cuda()]
+    plan = kvq.kvq_plan_blocks(dev, 32, 128, 16)
+    buf = kvq.allocate(plan)
+    _say("nonfinite")
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.admit(plan, dev, buf, 2.0)
+    assert e.value.status == kvq.KVQ_ENONFINITE
+    x[0, 1, 5, 7] = 1.0
+    dev = [torch.from_numpy(x).cuda()]
+    _say("infeasible")
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.admit(plan, dev, buf, 0.0)  # no allocation has zero entropy here
+    assert e.value.status == kvq.KVQ_EINFEASIBLE
+
+
+def test_deterministic_repeat():
+    """Two runs on the same inputs give bitwise equal outputs."""
+    w = W.DECODE_ADMIT_FP16
+    x = W.generate(w, which=1)
+    kw = _kw(w, mode="bisect")
+    _say("repeat")
+    a = parity.run_gpu(x, **kw)
+    b = parity.run_gpu(x, **kw)
+    for k in ("D", "H", "stats", "codebook", "m", "off", "codes", "xhat"):
+        assert np.array_equal(a[k], b[k]), k
+    assert a["lam"] == b["lam"]
