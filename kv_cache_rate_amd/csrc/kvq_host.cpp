@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <string>
@@ -99,6 +100,22 @@ kvq_status make_geom(const kvq_plan* p, const kvq_tensor* t, int32_t nt, kvq::Ge
     g.n = p->d_block;
     g.dtype = p->dtype;
     return KVQ_OK;
+}
+
+// The sort-free fp16 kernel covers s = 16 blocks of 4096 contiguous entries
+// (whole head_dim rows, fully contiguous tensors, 16-byte aligned).
+bool fast_fp16_path(const kvq_plan* p, const kvq_tensor* t, int32_t nt) {
+    if (getenv("KVQ_FORCE_GENERIC")) return false;
+    if (p->dtype != KVQ_F16 || p->s != 16 || p->d_block != 4096 || p->search != KVQ_GRIDS) return false;
+    for (int i = 0; i < nt; ++i) {
+        const int64_t* sh = t[i].shape;
+        const int64_t* st = t[i].stride;
+        if (p->dims_per_block != sh[3]) return false;
+        if (st[3] != 1 || st[2] != sh[3] || st[1] != sh[2] * sh[3] || st[0] != sh[1] * sh[2] * sh[3])
+            return false;
+        if (((uintptr_t)t[i].data) & 15u) return false;
+    }
+    return true;
 }
 
 }  // namespace
@@ -204,7 +221,11 @@ kvq_status kvq_eval_candidates(const kvq_plan* p, const kvq_tensor* t, int32_t n
     if (p->search == KVQ_GRIDS) {
         kvq::RankTable rt;
         rank_table(*p, rt);
-        e = kvq::launch_eval_grids(g, p->n_blocks, p->s, rt, D, H, stats, workspace, s);
+        if (fast_fp16_path(p, t, nt))
+            e = kvq::launch_eval16(t[0].data, nt > 1 ? t[1].data : t[0].data, p->tensor_blocks[0],
+                                   p->n_blocks, rt, D, H, stats, workspace, s);
+        else
+            e = kvq::launch_eval_grids(g, p->n_blocks, p->s, rt, D, H, stats, workspace, s);
     } else {
         e = kvq::launch_eval_alphabet(g, p->n_blocks, p->alphabet_m, D, H, stats, workspace, s);
     }

@@ -148,6 +148,8 @@ struct RankTable {
 // ---- host-side launchers (defined in the kernel files) ----
 hipError_t launch_eval_grids(const Geom& g, int64_t R, int s, const RankTable& rt, double* D,
                              double* H, float* stats, void* ws, hipStream_t st);
+hipError_t launch_eval16(const void* x0, const void* x1, int64_t nb0, int64_t R, const RankTable& rt,
+                         double* D, double* H, float* stats, void* ws, hipStream_t st);
 hipError_t launch_eval_alphabet(const Geom& g, int64_t R, int alpha_m, double* D, double* H,
                                 float* stats, void* ws, hipStream_t st);
 hipError_t launch_ws_reset(void* ws, hipStream_t st);

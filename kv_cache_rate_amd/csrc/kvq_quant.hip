@@ -12,6 +12,8 @@
 // draw of entry t of block r is word t & 3 of Philox4x32-10 on counter
 // (t >> 2, r lo, r hi, 0) under key (seed lo, seed hi): one generator call
 // serves four consecutive entries.
+#include <stdlib.h>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -24,7 +26,7 @@ quantize_kernel(Geom g, int s, const float* __restrict__ codebook, const uint8_t
                 uint32_t* __restrict__ codes) {
     __shared__ float q[kMaxS];
     const int64_t r = blockIdx.x;
-    const int m = m_in[r];
+    const int m = min(max((int)m_in[r], 1), s);
     if (threadIdx.x < s) q[threadIdx.x] = codebook[r * s + threadIdx.x];
     __syncthreads();
     const int w = code_width(m);
@@ -77,7 +79,7 @@ dequantize_kernel(int n, int s, const uint32_t* __restrict__ codes, const float*
                   float* __restrict__ xhat) {
     __shared__ float q[kMaxS];
     const int64_t r = blockIdx.x;
-    const int m = m_in[r];
+    const int m = min(max((int)m_in[r], 1), s);
     if (threadIdx.x < s) q[threadIdx.x] = codebook[r * s + threadIdx.x];
     __syncthreads();
     const int w = code_width(m);
@@ -106,19 +108,185 @@ dequantize_kernel(int n, int s, const uint32_t* __restrict__ codes, const float*
     }
 }
 
+// ---------------------------------------------------------------------------
+// Blocks of 4096 contiguous entries.  Lane t of the 256-thread workgroup owns
+// the 8-entry chunks t and t + 256.  A chunk's eight w-bit codes are exactly
+// w bytes of the block's little-endian stream (chunk c at byte w c), so loads
+// are 16-byte coalesced and stores are byte-granular with no cross-lane
+// packing.  Codepoints live in LDS padded with +inf to 16 slots, so the
+// interval search is a fixed four-step binary search; p uses the reciprocal
+// of the interval width.
+
+constexpr int kQT = 256;
+
+__device__ __forceinline__ void load8(const void* src, int dtype, int64_t e0, float* x) {
+    if (dtype == KVQ_F16) {
+        const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(src) + e0);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[2 * k] = __half2float(__ushort_as_half((unsigned short)(w[k] & 0xffffu)));
+            x[2 * k + 1] = __half2float(__ushort_as_half((unsigned short)(w[k] >> 16)));
+        }
+    } else {
+        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + e0);
+        const float4 a = p[0], b = p[1];
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+}
+
+__device__ __forceinline__ void store_bytes(uint8_t* dst, uint32_t bits, int w) {
+    switch (w) {
+    case 1: dst[0] = (uint8_t)bits; break;
+    case 2: *reinterpret_cast<uint16_t*>(dst) = (uint16_t)bits; break;
+    case 3:
+        if (((uintptr_t)dst & 1u) == 0) {
+            *reinterpret_cast<uint16_t*>(dst) = (uint16_t)bits;
+            dst[2] = (uint8_t)(bits >> 16);
+        } else {
+            dst[0] = (uint8_t)bits;
+            *reinterpret_cast<uint16_t*>(dst + 1) = (uint16_t)(bits >> 8);
+        }
+        break;
+    default: *reinterpret_cast<uint32_t*>(dst) = bits; break;
+    }
+}
+
+__device__ __forceinline__ uint32_t load_bytes(const uint8_t* src, int w) {
+    switch (w) {
+    case 1: return src[0];
+    case 2: return *reinterpret_cast<const uint16_t*>(src);
+    case 3:
+        if (((uintptr_t)src & 1u) == 0)
+            return (uint32_t)*reinterpret_cast<const uint16_t*>(src) | ((uint32_t)src[2] << 16);
+        return (uint32_t)src[0] | ((uint32_t)*reinterpret_cast<const uint16_t*>(src + 1) << 8);
+    default: return *reinterpret_cast<const uint32_t*>(src);
+    }
+}
+
+__global__ void __launch_bounds__(kQT)
+quantize4096_kernel(const void* __restrict__ x0, const void* __restrict__ x1, int64_t nb0, int dtype,
+                    int s, const float* __restrict__ codebook, const uint8_t* __restrict__ m_in,
+                    const uint64_t* __restrict__ off, uint32_t k0, uint32_t k1,
+                    uint32_t* __restrict__ codes) {
+    __shared__ float q[kMaxS];
+    __shared__ float inv[kMaxS];
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int m = min(max((int)m_in[r], 1), s);
+    if (tid < kMaxS) q[tid] = tid < m ? codebook[r * s + tid] : __builtin_huge_valf();
+    __syncthreads();
+    if (tid + 1 < m) inv[tid] = 1.0f / (q[tid + 1] - q[tid]);
+    __syncthreads();
+    const int w = code_width(m);
+    if (w == 0) return;
+    const void* src = r < nb0 ? x0 : x1;
+    const int64_t e_base = (r < nb0 ? r : r - nb0) * 4096;
+    uint8_t* out = reinterpret_cast<uint8_t*>(codes + off[r]);
+    const uint32_t rlo = (uint32_t)r, rhi = (uint32_t)((uint64_t)r >> 32);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int ch = tid + half * kQT;
+        float x[8];
+        load8(src, dtype, e_base + 8 * ch, x);
+        uint32_t wd[8];
+        {
+            uint32_t a0 = (uint32_t)(2 * ch), a1 = rlo, a2 = rhi, a3 = 0u;
+            philox4x32_10(a0, a1, a2, a3, k0, k1);
+            uint32_t b0 = (uint32_t)(2 * ch + 1), b1 = rlo, b2 = rhi, b3 = 0u;
+            philox4x32_10(b0, b1, b2, b3, k0, k1);
+            wd[0] = a0; wd[1] = a1; wd[2] = a2; wd[3] = a3;
+            wd[4] = b0; wd[5] = b1; wd[6] = b2; wd[7] = b3;
+        }
+        uint32_t bits = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float xv = x[e];
+            int i = 0;
+            i += (q[i + 8] <= xv) ? 8 : 0;
+            i += (q[i + 4] <= xv) ? 4 : 0;
+            i += (q[i + 2] <= xv) ? 2 : 0;
+            i += (q[i + 1] <= xv) ? 1 : 0;
+            i = min(i, m - 2);
+            float p = (xv - q[i]) * inv[i];
+            p = fminf(fmaxf(p, 0.0f), 1.0f);
+            const float u = (float)(wd[e] >> 8) * 0x1p-24f;
+            const uint32_t code = (uint32_t)i + (u < p ? 1u : 0u);
+            bits |= code << (w * e);
+        }
+        store_bytes(out + w * ch, bits, w);
+    }
+}
+
+__global__ void __launch_bounds__(kQT)
+dequantize4096_kernel(int s, const uint32_t* __restrict__ codes, const float* __restrict__ codebook,
+                      const uint8_t* __restrict__ m_in, const uint64_t* __restrict__ off,
+                      float* __restrict__ xhat) {
+    __shared__ float q[kMaxS];
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int m = min(max((int)m_in[r], 1), s);
+    if (tid < kMaxS) q[tid] = tid < m ? codebook[r * s + tid] : 0.0f;
+    __syncthreads();
+    const int w = code_width(m);
+    const uint8_t* in = reinterpret_cast<const uint8_t*>(codes + off[r]);
+    const uint32_t mask = (1u << w) - 1u;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int ch = tid + half * kQT;
+        const uint32_t bits = w ? load_bytes(in + w * ch, w) : 0u;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            int code = (int)((bits >> (w * e)) & mask);
+            code = code < m ? code : m - 1;
+            v[e] = q[code];
+        }
+        float4* o = reinterpret_cast<float4*>(xhat + r * 4096 + 8 * ch);
+        o[0] = make_float4(v[0], v[1], v[2], v[3]);
+        o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+}
+
+static bool fast_layout(const Geom& g) {
+    if (getenv("KVQ_FORCE_GENERIC")) return false;
+    if (g.n != 4096 || !g.contig) return false;
+    for (int i = 0; i < KVQ_MAX_TENSORS; ++i) {
+        if (!g.data[i]) continue;
+        // whole tensor contiguous: block r of a tensor starts at entry 4096 r
+        if (g.stride[i][1] != (int64_t)g.chunks * g.Tb * g.Db * g.groups) return false;
+        if (g.stride[i][0] != (int64_t)g.heads * g.stride[i][1]) return false;
+        if (g.groups != 1) return false;
+        if (((uintptr_t)g.data[i]) & 15u) return false;
+    }
+    return true;
+}
+
 hipError_t launch_quantize(const Geom& g, int64_t R, int s, const float* codebook, const uint8_t* m,
                            const uint64_t* off, uint64_t seed, uint32_t* codes, hipStream_t st) {
     if (R == 0) return hipSuccess;
-    hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)R), dim3(kQuantThreads), 0, st, g, s, codebook,
-                       m, off, (uint32_t)seed, (uint32_t)(seed >> 32), codes);
+    if (fast_layout(g)) {
+        hipLaunchKernelGGL(quantize4096_kernel, dim3((unsigned)R), dim3(kQT), 0, st, g.data[0],
+                           g.data[1] ? g.data[1] : g.data[0], g.nb0, g.dtype, s, codebook, m, off,
+                           (uint32_t)seed, (uint32_t)(seed >> 32), codes);
+    } else {
+        hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)R), dim3(kQuantThreads), 0, st, g, s,
+                           codebook, m, off, (uint32_t)seed, (uint32_t)(seed >> 32), codes);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_dequantize(int64_t R, int n, int s, const uint32_t* codes, const float* codebook,
                              const uint8_t* m, const uint64_t* off, float* xhat, hipStream_t st) {
     if (R == 0) return hipSuccess;
-    hipLaunchKernelGGL(dequantize_kernel, dim3((unsigned)R), dim3(kQuantThreads), 0, st, n, s, codes,
-                       codebook, m, off, xhat);
+    if (n == 4096 && !getenv("KVQ_FORCE_GENERIC") && !(((uintptr_t)xhat) & 15u)) {
+        hipLaunchKernelGGL(dequantize4096_kernel, dim3((unsigned)R), dim3(kQT), 0, st, s, codes,
+                           codebook, m, off, xhat);
+    } else {
+        hipLaunchKernelGGL(dequantize_kernel, dim3((unsigned)R), dim3(kQuantThreads), 0, st, n, s,
+                           codes, codebook, m, off, xhat);
+    }
     return hipGetLastError();
 }
 
