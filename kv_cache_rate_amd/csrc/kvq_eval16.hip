@@ -20,11 +20,16 @@
 // these; a prefix over bins gives counts and exact fp64 sums at bin edges
 // (fp16 sums of 4096 entries are exact in fp64).  The coarse bins that hold
 // a wanted order statistic or a uniform-grid threshold get per-key counts in
-// sweep 2 (packed 16-bit counters), and one lane per threshold finishes its
-// prefix inside the bin.  Order statistics are therefore exact data values
-// and every prefix is exact; only the final per-interval algebra rounds.
+// sweep 2 (packed 16-bit counters, rows padded to 33 words so lanes reading
+// different bins hit different LDS banks) plus totals of each run of 8 keys,
+// and one lane per threshold finishes its prefix inside the bin in at most
+// 8 + 4 steps.  Order statistics are therefore exact data values and every
+// prefix is exact; only the final per-interval algebra rounds (fp64).
 //
-// Workgroup = one block, 256 threads x 16 entries kept in registers.
+// Workgroup = one block, 256 threads x 16 entries kept in registers; the
+// candidate phase maps one 16-lane row to one candidate so its totals are a
+// row reduction.
+#include <math.h>
 #include <string.h>
 
 #include "kvq_internal.h"
@@ -36,38 +41,41 @@ namespace {
 constexpr int kT = 256;            // threads per block
 constexpr int kPer = 16;           // entries per thread
 constexpr int kNC = 1024;          // coarse bins
-constexpr int kFine = 64;          // keys per coarse bin
-constexpr int kSlotWords = kFine / 2;
-constexpr int kMaxSlots = 128;     // coarse bins resolved per batch
+constexpr int kSlotStride = 33;    // 32 words of packed 16-bit counts + pad
+constexpr int kGrpStride = 9;      // 8 group words + pad
+constexpr int kMaxSlots = 144;     // every target and threshold bin fits
 constexpr int kNU = 71;            // distinct interior uniform fractions, s = 16
 constexpr int kNQ = 73;            // order statistics, s = 16, n = 4096
+constexpr int kPS = kMaxS + 1;     // padded row of per-candidate arrays
+constexpr int kSlots = kMaxCand * kMaxS;  // 464 (candidate, point) slots
 constexpr uint16_t kNoSlot = 0xffff;
+// point sources (per (candidate, point) slot)
+constexpr uint16_t kSrcNone = 0xffff, kSrcMin = 0, kSrcMax = 1, kSrcUni = 0x100, kSrcQnt = 0x200;
 
-struct Phase1 {
-    uint32_t cnt[kNC];        // sweep 1 payload: count | sum(f) << 13
-    uint32_t pc[kNC + 1];     // exclusive prefix counts
-    double ps1[kNC + 1];      // exclusive prefix sums
-    uint16_t slot[kNC];       // resolved-bin slot or kNoSlot
-    uint32_t fine[kMaxSlots][kSlotWords];
+struct PhaseA {                    // sweep 1 .. threshold search
+    uint32_t cnt[kNC + 1];         // payload count | sum(f) << 13, then exclusive prefix counts
+    double ps1[kNC + 1];           // exclusive prefix sums
 };
-
-struct Phase2 {
-    float pval[kMaxCand][kMaxS];   // candidate codepoints
-    uint32_t pcnt[kMaxCand][kMaxS];  // entries below the codepoint (n at the closed end)
-    double ps1[kMaxCand][kMaxS];   // their sum
-    double ma[kMaxCand][kMaxS];    // mass of interval j sent to its left end
-    double mb[kMaxCand][kMaxS];    // ... and to its right end
-    double qm[kMaxCand][kMaxS];    // q_j^2 M_j
-    double hb[kMaxCand][kMaxS];    // -pi_j log2 pi_j
-    int cm[kMaxCand];
+struct PhaseB {                    // sweep 2 .. prefix finish
+    uint32_t fine[kMaxSlots * kSlotStride];
+    uint32_t grp[kMaxSlots * kGrpStride];  // count | sum(f within group) << 16
+};
+struct PhaseC {                    // candidate points and interval masses
+    float pval[kMaxCand * kPS];
+    uint32_t pcnt[kMaxCand * kPS];
+    double ps1[kMaxCand * kPS];
+    double ma[kMaxCand * kPS];
+    double mb[kMaxCand * kPS];
 };
 
 struct Shared {
     union {
-        Phase1 p1;
-        Phase2 p2;
+        PhaseA a;
+        PhaseB b;
+        PhaseC c;
     } u;
-    // order statistics (targets) and uniform thresholds
+    uint16_t slot[kNC];            // resolved bin -> slot * kSlotStride, or kNoSlot
+    uint16_t src[kSlots];          // point source of slot (c, j)
     uint16_t tbin[kNQ];
     uint16_t tloc[kNQ];
     float tval[kNQ];
@@ -77,14 +85,18 @@ struct Shared {
     float uval[kNU];
     uint32_t ucnt[kNU];
     double us1[kNU];
-    // reductions
-    uint32_t kmin[kT / 64], kmax[kT / 64];
+    double lg_c[32];
+    double lg_inv[32];
+    uint32_t wmin[kT / 64], wmax[kT / 64], wamax[kT / 64];
     double wsq[kT / 64];
     uint32_t wtot[kT / 64];
     double wts1[kT / 64];
     int nslots;
-    int bad;
 };
+
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+typedef short short2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t half_key(uint32_t h) {
     return (h & 0x8000u) ? (~h & 0xffffu) : (h | 0x8000u);
@@ -103,49 +115,49 @@ __device__ __forceinline__ uint32_t key_ceil(float t) {
     return key;
 }
 
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
-    return v;
+// 1/x to ~1 ulp: hardware reciprocal estimate and two Newton steps.
+__device__ __forceinline__ double recip(double x) {
+    double r = __builtin_amdgcn_rcp(x);
+    double e = fma(-x, r, 1.0);
+    r = fma(r, e, r);
+    e = fma(-x, r, 1.0);
+    return fma(r, e, r);
 }
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-    return v;
-}
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-__device__ __forceinline__ uint32_t wave_incl_u32(uint32_t v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = (uint32_t)__shfl_up((int)v, o, 64);
-        if (lane >= o) v += t;
-    }
-    return v;
-}
-__device__ __forceinline__ double wave_incl_f64(double v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const double t = __shfl_up(v, o, 64);
-        if (lane >= o) v += t;
-    }
-    return v;
+
+// log2 of x in (0, 1], relative error ~1e-15: x = m 2^e with m in [1, 2);
+// c = 1 + (2i + 1)/64 is the centre of the 1/32-wide cell of m, so
+// log2 m = log2 c + log1p(t)/ln 2 with t = (m - c)/c, |t| < 1/64, and a
+// degree-8 series for log1p.
+__device__ __forceinline__ double log2_unit(double x, const double* lg_c, const double* lg_inv) {
+    int e;
+    double m = frexp(x, &e);  // [0.5, 1)
+    m *= 2.0;
+    e -= 1;
+    const int i = (int)((__double_as_longlong(m) >> 47) & 31);
+    const double c = 1.0 + (double)(2 * i + 1) * (1.0 / 64.0);
+    const double t = (m - c) * lg_inv[i];
+    double p = -1.0 / 8.0;
+    p = fma(p, t, 1.0 / 7.0);
+    p = fma(p, t, -1.0 / 6.0);
+    p = fma(p, t, 1.0 / 5.0);
+    p = fma(p, t, -1.0 / 4.0);
+    p = fma(p, t, 1.0 / 3.0);
+    p = fma(p, t, -1.0 / 2.0);
+    p = fma(p, t, 1.0);
+    const double l1p = p * t;
+    return ((double)e + lg_c[i]) + l1p * 1.4426950408889634;  // 1/ln 2
 }
 
 }  // namespace
 
-// Threshold tables from the host: quantile ranks / stats columns and the
-// reduced fractions of the uniform grids.
+// Threshold tables from the host.
 struct Eval16Tables {
     RankTable rt;
-    uint8_t unum[kNU];   // numerator of distinct fraction u
-    uint8_t uden[kNU];   // denominator
-    uint8_t ucol[kMaxS + 1][kMaxS];  // fraction index of U_k point j (interior j)
+    uint8_t unum[kNU];              // numerator of distinct fraction u
+    uint8_t uden[kNU];              // denominator
+    uint16_t src[kSlots];           // point source of (candidate, point) slot
+    double lg_c[32];                // log2(1 + (2i+1)/64)
+    double lg_inv[32];              // 1 / (1 + (2i+1)/64)
 };
 
 __global__ void __launch_bounds__(kT)
@@ -167,67 +179,80 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         hw[0] = a.x; hw[1] = a.y; hw[2] = a.z; hw[3] = a.w;
         hw[4] = b.x; hw[5] = b.y; hw[6] = b.z; hw[7] = b.w;
     }
-    for (int i = tid; i < kNC; i += kT) sh.u.p1.cnt[i] = 0u;
-    if (tid == 0) sh.bad = 0;
+    for (int i = tid; i < kNC; i += kT) sh.u.a.cnt[i] = 0u;
+    for (int i = tid; i < kSlots; i += kT) sh.src[i] = tb.src[i];
+    if (tid < 32) {
+        sh.lg_c[tid] = tb.lg_c[tid];
+        sh.lg_inv[tid] = tb.lg_inv[tid];
+    }
     __syncthreads();
 
-    // ---- sweep 1: keys, coarse histogram, min/max, sum of squares
-    uint32_t kmin = 0xffffu, kmax = 0u;
+    // ---- sweep 1 (two entries per 32-bit word): canonical -0, keys,
+    //      coarse histogram, min/max keys, max |bits|, sum of squares
+    ushort2_t kmin2 = {0xffff, 0xffff}, kmax2 = {0, 0}, amax2 = {0, 0};
     double sq = 0.0;
-    bool bad = false;
-    uint32_t keys[kPer];
+    uint32_t keys2[kPer / 2];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        uint32_t h = (hw[i >> 1] >> ((i & 1) * 16)) & 0xffffu;
-        if (h == 0x8000u) h = 0u;  // -0 -> +0
-        bad |= (h & 0x7c00u) == 0x7c00u;
-        const uint32_t key = half_key(h);
-        keys[i] = key;
-        kmin = min(kmin, key);
-        kmax = max(kmax, key);
-        const float v = __half2float(__ushort_as_half((unsigned short)h));
-        sq += (double)v * (double)v;
-        atomicAdd(&sh.u.p1.cnt[key >> 6], 1u | ((key & 63u) << 13));
+    for (int p = 0; p < kPer / 2; ++p) {
+        // x + (+0) maps -0 to +0 and leaves every other value (NaN stays NaN)
+        half2_t hv = __builtin_bit_cast(half2_t, hw[p]) + (half2_t){(_Float16)0.0f, (_Float16)0.0f};
+        const uint32_t w = __builtin_bit_cast(uint32_t, hv);
+        const short2_t sg = __builtin_bit_cast(short2_t, w) >> (short2_t){15, 15};
+        const uint32_t msk = (__builtin_bit_cast(uint32_t, sg) & 0x7fff7fffu) | 0x80008000u;
+        const uint32_t k2 = w ^ msk;  // order-preserving keys of both halves
+        keys2[p] = k2;
+        const ushort2_t kv = __builtin_bit_cast(ushort2_t, k2);
+        kmin2 = __builtin_elementwise_min(kmin2, kv);
+        kmax2 = __builtin_elementwise_max(kmax2, kv);
+        amax2 = __builtin_elementwise_max(amax2, __builtin_bit_cast(ushort2_t, w & 0x7fff7fffu));
+        const double v0 = (double)(float)hv.x, v1 = (double)(float)hv.y;
+        sq = fma(v0, v0, sq);
+        sq = fma(v1, v1, sq);
+        const uint32_t klo = k2 & 0xffffu, khi = k2 >> 16;
+        atomicAdd(&sh.u.a.cnt[klo >> 6], 1u | ((klo & 63u) << 13));
+        atomicAdd(&sh.u.a.cnt[khi >> 6], 1u | ((khi & 63u) << 13));
     }
-    if (bad) sh.bad = 1;
-    kmin = wave_min_u32(kmin);
-    kmax = wave_max_u32(kmax);
-    sq = wave_sum_f64(sq);
-    if (lane == 0) {
-        sh.kmin[wave] = kmin;
-        sh.kmax[wave] = kmax;
-        sh.wsq[wave] = sq;
+    {
+        const uint32_t kmin = wave_min_u32_dpp(min((uint32_t)kmin2.x, (uint32_t)kmin2.y));
+        const uint32_t kmax = wave_max_u32_dpp(max((uint32_t)kmax2.x, (uint32_t)kmax2.y));
+        const uint32_t amax = wave_max_u32_dpp(max((uint32_t)amax2.x, (uint32_t)amax2.y));
+        const double sqw = wave_last_f64(wave_scan_add_f64(sq));
+        if (lane == 0) {
+            sh.wmin[wave] = kmin;
+            sh.wmax[wave] = kmax;
+            sh.wamax[wave] = amax;
+            sh.wsq[wave] = sqw;
+        }
     }
     __syncthreads();
-    if (sh.bad && tid == 0) atomicOr(&ws->status, kStatusNonFinite);
-    kmin = min(min(sh.kmin[0], sh.kmin[1]), min(sh.kmin[2], sh.kmin[3]));
-    kmax = max(max(sh.kmax[0], sh.kmax[1]), max(sh.kmax[2], sh.kmax[3]));
+    const uint32_t kmin = min(min(sh.wmin[0], sh.wmin[1]), min(sh.wmin[2], sh.wmin[3]));
+    const uint32_t kmax = max(max(sh.wmax[0], sh.wmax[1]), max(sh.wmax[2], sh.wmax[3]));
+    if (tid == 0 && max(max(sh.wamax[0], sh.wamax[1]), max(sh.wamax[2], sh.wamax[3])) >= 0x7c00u)
+        atomicOr(&ws->status, kStatusNonFinite);
     const double sumsq = (sh.wsq[0] + sh.wsq[1]) + (sh.wsq[2] + sh.wsq[3]);
     const float mn = key_value(kmin);
     const float mx = key_value(kmax);
 
-    // ---- coarse prefix: thread owns bins [4 tid, 4 tid + 4)
+    // ---- coarse prefix: thread owns bins [4 tid, 4 tid + 4) (one binade,
+    //      B_k = B0 + 64 k U), prefix counts written over the payloads
     {
-        uint32_t c[4];
-        double s[4];
-        uint32_t ct = 0;
-        double st = 0.0;
+        const uint32_t bin0 = 4 * tid;
+        const float B0 = key_value(bin0 << 6);
+        const double U = (double)(key_value((bin0 << 6) | 1u) - B0);
+        uint32_t c[4], acc[4];
+        uint32_t ct = 0, at = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const uint32_t bin = 4 * tid + k;
-            const uint32_t p = sh.u.p1.cnt[bin];
-            const uint32_t C = p & 0x1fffu;
-            const uint32_t SF = p >> 13;
-            const float B = key_value(bin << 6);
-            const float U = key_value((bin << 6) | 1u) - B;
-            c[k] = C;
-            // empty bins add exactly 0 (the Inf/NaN code bins have no finite base)
-            s[k] = C ? (double)C * (double)B + (double)U * (double)SF : 0.0;
-            ct += C;
-            st += s[k];
+            const uint32_t p = sh.u.a.cnt[bin0 + k];
+            c[k] = p & 0x1fffu;
+            acc[k] = 64u * (uint32_t)k * c[k] + (p >> 13);
+            ct += c[k];
+            at += acc[k];
         }
-        const uint32_t ic = wave_incl_u32(ct);
-        const double is = wave_incl_f64(st);
+        // empty threads add exactly 0 (the Inf/NaN code bins have no finite base)
+        const double st = ct ? (double)ct * (double)B0 + U * (double)at : 0.0;
+        const uint32_t ic = wave_scan_add_u32(ct);
+        const double is = wave_scan_add_f64(st);
         if (lane == 63) {
             sh.wtot[wave] = ic;
             sh.wts1[wave] = is;
@@ -239,36 +264,41 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
             oc += sh.wtot[w];
             os += sh.wts1[w];
         }
-        uint32_t runc = oc + ic - ct;
-        double runs = os + (is - st);
+        const uint32_t base_c = oc + ic - ct;
+        const double base_s = os + (is - st);
+        uint32_t runc = 0, runa = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            sh.u.p1.pc[4 * tid + k] = runc;
-            sh.u.p1.ps1[4 * tid + k] = runs;
+            sh.u.a.cnt[bin0 + k] = base_c + runc;
+            sh.u.a.ps1[bin0 + k] = runc ? base_s + (double)runc * (double)B0 + U * (double)runa : base_s;
             runc += c[k];
-            runs += s[k];
+            runa += acc[k];
+            sh.slot[bin0 + k] = kNoSlot;
         }
         if (tid == kT - 1) {
-            sh.u.p1.pc[kNC] = runc;
-            sh.u.p1.ps1[kNC] = runs;
+            sh.u.a.cnt[kNC] = base_c + ct;
+            sh.u.a.ps1[kNC] = base_s + st;
         }
-        for (int i = tid; i < kNC; i += kT) sh.u.p1.slot[i] = kNoSlot;
     }
     __syncthreads();
 
-    // ---- targets (order statistics) and uniform thresholds
+    // ---- targets (order statistics) on threads 0..72, uniform thresholds on
+    //      threads 128..198: find the bin, read its prefix, mark it
     const int nq = tb.rt.n_stats;  // 73
     if (tid < nq) {
         const uint32_t rank = (uint32_t)tb.rt.rank[tid];
-        int lo = 0, hi = kNC - 1;  // last bin with pc[bin] <= rank
+        int lo = 0, hi = kNC - 1;  // last bin with prefix count <= rank
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (sh.u.p1.pc[mid] <= rank) lo = mid;
+            if (sh.u.a.cnt[mid] <= rank) lo = mid;
             else hi = mid - 1;
         }
+        const uint32_t pc = sh.u.a.cnt[lo];
         sh.tbin[tid] = (uint16_t)lo;
-        sh.tloc[tid] = (uint16_t)(rank - sh.u.p1.pc[lo]);
-        sh.u.p1.slot[lo] = 0;  // mark
+        sh.tloc[tid] = (uint16_t)(rank - pc);
+        sh.tcnt[tid] = pc;
+        sh.ts1[tid] = sh.u.a.ps1[lo];
+        sh.slot[lo] = 0;  // mark
     } else if (tid >= 128 && tid < 128 + kNU) {
         const int u = tid - 128;
         float t;
@@ -279,17 +309,21 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
             t = (float)(dmn + (span * (double)tb.unum[u]) / (double)tb.uden[u]);
         }
         const uint32_t key = key_ceil(t);
+        const uint32_t bin = key >> 6;
         sh.uval[u] = t;
         sh.ukey[u] = (uint16_t)key;
-        sh.u.p1.slot[key >> 6] = 0;  // mark
+        sh.ucnt[u] = sh.u.a.cnt[bin];
+        sh.us1[u] = sh.u.a.ps1[bin];
+        sh.slot[bin] = 0;  // mark
     }
+    const double total_s1 = sh.u.a.ps1[kNC];
     __syncthreads();
-    // compact marked bins into slots (thread owns 4 bins)
+    // compact marked bins into slots (thread owns 4 bins); at most 73 + 71
     {
         uint32_t m4 = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) m4 += sh.u.p1.slot[4 * tid + k] == 0 ? 1u : 0u;
-        const uint32_t im = wave_incl_u32(m4);
+        for (int k = 0; k < 4; ++k) m4 += sh.slot[4 * tid + k] == 0 ? 1u : 0u;
+        const uint32_t im = wave_scan_add_u32(m4);
         if (lane == 63) sh.wtot[wave] = im;
         __syncthreads();
         uint32_t o = 0;
@@ -298,163 +332,189 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int bin = 4 * tid + k;
-            if (sh.u.p1.slot[bin] == 0) sh.u.p1.slot[bin] = (uint16_t)(s++);
+            if (sh.slot[bin] == 0) sh.slot[bin] = (uint16_t)(kSlotStride * s++);
         }
         if (tid == kT - 1) sh.nslots = (int)s;
     }
     __syncthreads();
-    const int nslots = sh.nslots;
+    const int nslots = sh.nslots;  // <= 144 = kMaxSlots
+    for (int i = tid; i < nslots * kSlotStride; i += kT) sh.u.b.fine[i] = 0u;
+    __syncthreads();
 
-    // ---- sweep 2 (in batches of kMaxSlots resolved bins) and prefix finish
-    for (int base = 0; base < nslots; base += kMaxSlots) {
-        for (int i = tid; i < kMaxSlots * kSlotWords; i += kT) (&sh.u.p1.fine[0][0])[i] = 0u;
-        __syncthreads();
+    // ---- sweep 2: per-key counts in resolved bins
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const uint32_t key = keys[i];
-            const uint32_t sl = (uint32_t)sh.u.p1.slot[key >> 6] - (uint32_t)base;
-            if (sl < (uint32_t)kMaxSlots) {
-                const uint32_t f = key & 63u;
-                atomicAdd(&sh.u.p1.fine[sl][f >> 1], 1u << ((f & 1u) * 16));
-            }
+    for (int p = 0; p < kPer / 2; ++p) {
+#pragma unroll
+        for (int hpart = 0; hpart < 2; ++hpart) {
+            const uint32_t key = hpart ? keys2[p] >> 16 : keys2[p] & 0xffffu;
+            const uint32_t sl = sh.slot[key >> 6];
+            if (sl != kNoSlot)
+                atomicAdd(&sh.u.b.fine[sl + ((key & 63u) >> 1)], 1u << ((key & 1u) * 16));
         }
-        __syncthreads();
-        if (tid < nq) {
-            const uint32_t bin = sh.tbin[tid];
-            const uint32_t sl = (uint32_t)sh.u.p1.slot[bin] - (uint32_t)base;
-            if (sl < (uint32_t)kMaxSlots) {
-                const uint32_t loc = sh.tloc[tid];
-                uint32_t N = 0, F1 = 0, f = 0;
-                for (int wd = 0; wd < kSlotWords; ++wd) {
-                    const uint32_t w = sh.u.p1.fine[sl][wd];
-                    const uint32_t c0 = w & 0xffffu, c1 = w >> 16;
-                    if (N + c0 > loc) { f = 2 * wd; break; }
-                    N += c0;
-                    F1 += (2 * wd) * c0;
-                    if (N + c1 > loc) { f = 2 * wd + 1; break; }
-                    N += c1;
-                    F1 += (2 * wd + 1) * c1;
-                }
-                const float B = key_value(bin << 6);
-                const float U = key_value((bin << 6) | 1u) - B;
-                sh.tval[tid] = key_value((bin << 6) | f);
-                sh.tcnt[tid] = sh.u.p1.pc[bin] + N;
-                sh.ts1[tid] = sh.u.p1.ps1[bin] + (double)B * (double)N + (double)U * (double)F1;
-            }
-        } else if (tid >= 128 && tid < 128 + kNU) {
-            const int u = tid - 128;
-            const uint32_t key = sh.ukey[u];
-            const uint32_t bin = key >> 6;
-            const uint32_t sl = (uint32_t)sh.u.p1.slot[bin] - (uint32_t)base;
-            if (sl < (uint32_t)kMaxSlots) {
-                const uint32_t fstop = key & 63u;
-                uint32_t N = 0, F1 = 0;
-                for (uint32_t f = 0; f < fstop; ++f) {
-                    const uint32_t c = (sh.u.p1.fine[sl][f >> 1] >> ((f & 1u) * 16)) & 0xffffu;
-                    N += c;
-                    F1 += f * c;
-                }
-                const float B = key_value(bin << 6);
-                const float U = key_value((bin << 6) | 1u) - B;
-                sh.ucnt[u] = sh.u.p1.pc[bin] + N;
-                sh.us1[u] = sh.u.p1.ps1[bin] + (double)B * (double)N + (double)U * (double)F1;
-            }
-        }
-        __syncthreads();
     }
-    const double total_s1 = sh.u.p1.ps1[kNC];
-    __syncthreads();  // phase-1 storage is reused below
+    __syncthreads();
+    // group totals: 8 keys (4 words) per group, 8 groups per slot
+    for (int g = tid; g < nslots * 8; g += kT) {
+        const int s = g >> 3, gi = g & 7;
+        const uint32_t* fw = &sh.u.b.fine[s * kSlotStride + 4 * gi];
+        uint32_t cn = 0, fs = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t w = fw[q];
+            const uint32_t c0 = w & 0xffffu, c1 = w >> 16;
+            cn += c0 + c1;
+            fs += (2 * q) * c0 + (2 * q + 1) * c1;
+        }
+        sh.u.b.grp[s * kGrpStride + gi] = cn | (fs << 16);
+    }
+    __syncthreads();
+
+    // ---- finish the prefixes inside the bins
+    if (tid < nq) {
+        const uint32_t bin = sh.tbin[tid];
+        const uint32_t sbase = sh.slot[bin];
+        const uint32_t loc = sh.tloc[tid];
+        const uint32_t* gw = &sh.u.b.grp[(sbase / kSlotStride) * kGrpStride];
+        uint32_t N = 0, F1 = 0;
+        int gi = 0;
+        for (; gi < 7; ++gi) {
+            const uint32_t g = gw[gi];
+            const uint32_t gc = g & 0xffffu;
+            if (N + gc > loc) break;
+            N += gc;
+            F1 += 8u * (uint32_t)gi * gc + (g >> 16);
+        }
+        const uint32_t* fw = &sh.u.b.fine[sbase + 4 * gi];
+        uint32_t f = 8 * gi + 7;
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t w = fw[q];
+            const uint32_t c0 = w & 0xffffu, c1 = w >> 16;
+            const uint32_t f0 = 8 * gi + 2 * q;
+            if (N + c0 > loc) { f = f0; break; }
+            N += c0;
+            F1 += f0 * c0;
+            if (N + c1 > loc) { f = f0 + 1; break; }
+            N += c1;
+            F1 += (f0 + 1) * c1;
+        }
+        const float B = key_value(bin << 6);
+        const float U = key_value((bin << 6) | 1u) - B;
+        sh.tval[tid] = key_value((bin << 6) | f);
+        sh.tcnt[tid] += N;
+        if (N) sh.ts1[tid] += (double)B * (double)N + (double)U * (double)F1;
+    } else if (tid >= 128 && tid < 128 + kNU) {
+        const int u = tid - 128;
+        const uint32_t key = sh.ukey[u];
+        const uint32_t bin = key >> 6;
+        const uint32_t sbase = sh.slot[bin];
+        const uint32_t fstop = key & 63u;
+        const uint32_t* gw = &sh.u.b.grp[(sbase / kSlotStride) * kGrpStride];
+        uint32_t N = 0, F1 = 0;
+        const int gstop = (int)(fstop >> 3);
+        for (int gi = 0; gi < gstop; ++gi) {
+            const uint32_t g = gw[gi];
+            const uint32_t gc = g & 0xffffu;
+            N += gc;
+            F1 += 8u * (uint32_t)gi * gc + (g >> 16);
+        }
+        const uint32_t* fw = &sh.u.b.fine[sbase + 4 * gstop];
+        for (uint32_t f = 8u * gstop; f < fstop; ++f) {
+            const uint32_t c = (fw[(f >> 1) - 4u * gstop] >> ((f & 1u) * 16)) & 0xffffu;
+            N += c;
+            F1 += f * c;
+        }
+        const float B = key_value(bin << 6);
+        const float U = key_value((bin << 6) | 1u) - B;
+        sh.ucnt[u] += N;
+        if (N) sh.us1[u] += (double)B * (double)N + (double)U * (double)F1;
+    }
+    __syncthreads();  // phase-B storage is reused below
 
     // ---- order statistics out
     if (tid < nq) stats[r * nq + tid] = sh.tval[tid];
 
-    // ---- candidate codepoints with their prefixes (closed last interval)
-    const int C = kMaxCand;  // s = 16
-    Phase2& p2 = sh.u.p2;
-    if (tid < C) {
-        const int c = tid;
-        int k;
-        bool uni = false;
-        if (c == 0) k = 2;
-        else {
-            k = 3 + (c - 1) / 2;
-            uni = ((c - 1) & 1) == 0;
-        }
-        int m = 0;
-        for (int j = 0; j < k; ++j) {
+    // ---- raw candidate points: slot (c, j), repeats kept
+    PhaseC& pc = sh.u.c;
+    for (int sl = tid; sl < kSlots; sl += kT) {
+        const uint16_t sc = sh.src[sl];
+        if (sc != kSrcNone) {
             float v;
             uint32_t cn;
             double s1;
-            if (j == 0) {
+            if (sc == kSrcMin) {
                 v = mn; cn = 0; s1 = 0.0;
-            } else if (j == k - 1) {
+            } else if (sc == kSrcMax) {
                 v = mx; cn = 4096; s1 = total_s1;
-            } else if (uni) {
-                const int u = tb.ucol[k][j];
+            } else if (sc < kSrcQnt) {
+                const int u = sc - kSrcUni;
                 v = sh.uval[u]; cn = sh.ucnt[u]; s1 = sh.us1[u];
             } else {
-                const int q = tb.rt.col[k][j];
+                const int q = sc - kSrcQnt;
                 v = sh.tval[q]; cn = sh.tcnt[q]; s1 = sh.ts1[q];
             }
-            if (m > 0 && v == p2.pval[c][m - 1]) {
-                if (j == k - 1) {  // the maximum keeps the closed end
-                    p2.pcnt[c][m - 1] = cn;
-                    p2.ps1[c][m - 1] = s1;
-                }
-                continue;
+            const int i0 = (sl >> 4) * kPS + (sl & 15);
+            pc.pval[i0] = v;
+            pc.pcnt[i0] = cn;
+            pc.ps1[i0] = s1;
+        }
+    }
+    __syncthreads();
+    // interval masses; an interval between two equal points carries the
+    // entries equal to that point (possible only at the closed maximum)
+    for (int sl = tid; sl < kSlots; sl += kT) {
+        if ((sl & 15) < 15 && sh.src[sl + 1] != kSrcNone) {
+            const int i0 = (sl >> 4) * kPS + (sl & 15);
+            const double a = pc.pval[i0], b = pc.pval[i0 + 1];
+            const double Cn = (double)(pc.pcnt[i0 + 1] - pc.pcnt[i0]);
+            double mbv = Cn;
+            if (b > a) {
+                const double S1 = pc.ps1[i0 + 1] - pc.ps1[i0];
+                mbv = (S1 - a * Cn) * recip(b - a);
+                mbv = fmin(fmax(mbv, 0.0), Cn);
             }
-            p2.pval[c][m] = v;
-            p2.pcnt[c][m] = cn;
-            p2.ps1[c][m] = s1;
-            ++m;
-        }
-        p2.cm[c] = m;
-    }
-    __syncthreads();
-    // interval masses: slot (c, j) for interval [q_j, q_{j+1}]
-    for (int sl = tid; sl < C * kMaxS; sl += kT) {
-        const int c = sl / kMaxS, j = sl - c * kMaxS;
-        const int m = p2.cm[c];
-        if (j + 1 < m) {
-            const double a = p2.pval[c][j], b = p2.pval[c][j + 1];
-            const double Cn = (double)(p2.pcnt[c][j + 1] - p2.pcnt[c][j]);
-            const double S1 = p2.ps1[c][j + 1] - p2.ps1[c][j];
-            double mbv = (S1 - a * Cn) / (b - a);
-            mbv = fmin(fmax(mbv, 0.0), Cn);
-            p2.mb[c][j] = mbv;
-            p2.ma[c][j] = Cn - mbv;
+            pc.mb[i0] = mbv;
+            pc.ma[i0] = Cn - mbv;
         }
     }
     __syncthreads();
-    // point terms: q_j^2 M_j and -pi_j log2 pi_j
-    for (int sl = tid; sl < C * kMaxS; sl += kT) {
-        const int c = sl / kMaxS, j = sl - c * kMaxS;
-        const int m = p2.cm[c];
-        if (j < m && m >= 2) {
+    // point terms, then one 16-lane row per candidate: D = sum q^2 M - sum x^2
+    // and H = sum over distinct values of -pi log2 pi
+#pragma unroll
+    for (int round = 0; round < 2; ++round) {
+        const int sl = tid + round * kT;
+        const int c = sl >> 4, j = sl & 15;
+        double qm = 0.0, hb = 0.0;
+        if (sl < kSlots && sh.src[sl] != kSrcNone) {
+            const int i0 = c * kPS + j;
+            const bool has_right = j < 15 && sh.src[sl + 1] != kSrcNone;
             double M = 0.0;
-            if (j > 0) M += p2.mb[c][j - 1];
-            if (j + 1 < m) M += p2.ma[c][j];
-            const double q = p2.pval[c][j];
-            p2.qm[c][j] = q * q * M;
-            const double pi = M * (1.0 / 4096.0);
-            p2.hb[c][j] = pi > 0.0 ? -pi * log2(pi) : 0.0;
-        }
-    }
-    __syncthreads();
-    if (tid < C) {
-        const int c = tid;
-        const int m = p2.cm[c];
-        double Dc = 0.0, Hc = 0.0;
-        if (m >= 2) {
-            double qs = 0.0;
-            for (int j = 0; j < m; ++j) {
-                qs += p2.qm[c][j];
-                Hc += p2.hb[c][j];
+            if (j > 0) M += pc.mb[i0 - 1];
+            if (has_right) M += pc.ma[i0];
+            const double q = pc.pval[i0];
+            qm = q * q * M;
+            if (j == 0 || pc.pval[i0 - 1] != pc.pval[i0]) {
+                double Mv = M;
+                for (int jj = j + 1; jj < 16 && sh.src[c * kMaxS + jj] != kSrcNone &&
+                                     pc.pval[c * kPS + jj] == pc.pval[i0];
+                     ++jj) {
+                    Mv += pc.mb[c * kPS + jj - 1];
+                    if (jj < 15 && sh.src[c * kMaxS + jj + 1] != kSrcNone) Mv += pc.ma[c * kPS + jj];
+                }
+                const double pi = Mv * (1.0 / 4096.0);
+                if (pi > 0.0) hb = -pi * log2_unit(pi, sh.lg_c, sh.lg_inv);
             }
-            Dc = qs - sumsq;
         }
-        Dout[r * C + c] = fmax(Dc, 0.0);
-        Hout[r * C + c] = fmax(Hc, 0.0);
+        qm = row_sum_f64(qm);
+        hb = row_sum_f64(hb);
+        if (j == 15 && c < kMaxCand) {
+            double Dc = 0.0, Hc = 0.0;
+            if (mx > mn) {
+                Dc = qm - sumsq;
+                Hc = hb;
+            }
+            Dout[r * kMaxCand + c] = fmax(Dc, 0.0);
+            Hout[r * kMaxCand + c] = fmax(Hc, 0.0);
+        }
     }
 }
 
@@ -465,6 +525,8 @@ hipError_t launch_eval16(const void* x0, const void* x1, int64_t nb0, int64_t R,
     memset(&tb, 0, sizeof tb);
     tb.rt = rt;
     // distinct interior fractions j/(k-1), k = 3..16, in order of first appearance
+    uint8_t ucol[kMaxS + 1][kMaxS];
+    memset(ucol, 0, sizeof ucol);
     int nu = 0;
     for (int k = 3; k <= kMaxS; ++k)
         for (int j = 1; j <= k - 2; ++j) {
@@ -485,9 +547,26 @@ hipError_t launch_eval16(const void* x0, const void* x1, int64_t nb0, int64_t R,
                 tb.uden[nu] = (uint8_t)b;
                 found = nu++;
             }
-            tb.ucol[k][j] = (uint8_t)found;
+            ucol[k][j] = (uint8_t)found;
         }
     if (nu != kNU || rt.n_stats != kNQ) return hipErrorInvalidValue;
+    // point sources: candidate 0 is {min, max}; then U_k, E_k for k = 3..16
+    for (int c = 0; c < kMaxCand; ++c) {
+        const int k = c == 0 ? 2 : 3 + (c - 1) / 2;
+        const bool uni = c > 0 && ((c - 1) & 1) == 0;
+        for (int j = 0; j < kMaxS; ++j) {
+            uint16_t v = kSrcNone;
+            if (j == 0) v = kSrcMin;
+            else if (j == k - 1) v = kSrcMax;
+            else if (j < k) v = uni ? (uint16_t)(kSrcUni + ucol[k][j]) : (uint16_t)(kSrcQnt + rt.col[k][j]);
+            tb.src[c * kMaxS + j] = v;
+        }
+    }
+    for (int i = 0; i < 32; ++i) {
+        const double c = 1.0 + (double)(2 * i + 1) / 64.0;
+        tb.lg_c[i] = log2(c);
+        tb.lg_inv[i] = 1.0 / c;
+    }
     hipLaunchKernelGGL(eval16_kernel, dim3((unsigned)R), dim3(kT), 0, st, (const __half*)x0,
                        (const __half*)x1, nb0, tb, D, H, stats, (WsHeader*)ws);
     return hipGetLastError();

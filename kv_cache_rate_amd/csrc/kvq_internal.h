@@ -133,6 +133,98 @@ __host__ __device__ __forceinline__ int code_width(int m) {
     return w;
 }
 
+// ---- wave64 cross-lane operations through DPP (gfx9 family) ----
+// row_shr:k moves lane l - k to lane l inside each 16-lane row (lanes whose
+// source falls outside the row keep `old`); row_bcast:15 / row_bcast:31 copy
+// lane 15 of a row (lane 31) into the following row(s) selected by row_mask.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114,
+              kDppRowShr8 = 0x118, kDppBcast15 = 0x142, kDppBcast31 = 0x143,
+              kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141;
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double old, double v) {
+    const uint64_t o = (uint64_t)__double_as_longlong(old), x = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)o, (uint32_t)x);
+    const uint32_t hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(o >> 32), (uint32_t)(x >> 32));
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t old, uint64_t v) {
+    const uint32_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)old, (uint32_t)v);
+    const uint32_t hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(old >> 32), (uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_scan_add_u32(uint32_t v) {
+    v += dpp_u32<kDppRowShr1>(0u, v);
+    v += dpp_u32<kDppRowShr2>(0u, v);
+    v += dpp_u32<kDppRowShr4>(0u, v);
+    v += dpp_u32<kDppRowShr8>(0u, v);
+    v += dpp_u32<kDppBcast15, 0xA>(0u, v);
+    v += dpp_u32<kDppBcast31, 0xC>(0u, v);
+    return v;
+}
+__device__ __forceinline__ double wave_scan_add_f64(double v) {
+    v += dpp_f64<kDppRowShr1>(0.0, v);
+    v += dpp_f64<kDppRowShr2>(0.0, v);
+    v += dpp_f64<kDppRowShr4>(0.0, v);
+    v += dpp_f64<kDppRowShr8>(0.0, v);
+    v += dpp_f64<kDppBcast15, 0xA>(0.0, v);
+    v += dpp_f64<kDppBcast31, 0xC>(0.0, v);
+    return v;
+}
+__device__ __forceinline__ uint64_t wave_scan_add_u64(uint64_t v) {
+    v += dpp_u64<kDppRowShr1>(0ull, v);
+    v += dpp_u64<kDppRowShr2>(0ull, v);
+    v += dpp_u64<kDppRowShr4>(0ull, v);
+    v += dpp_u64<kDppRowShr8>(0ull, v);
+    v += dpp_u64<kDppBcast15, 0xA>(0ull, v);
+    v += dpp_u64<kDppBcast31, 0xC>(0ull, v);
+    return v;
+}
+// Value of lane 63 (the wave total after an inclusive scan), wave-uniform.
+__device__ __forceinline__ uint32_t wave_last_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ double wave_last_f64(double v) {
+    const uint64_t x = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// Wave-wide min / max (every lane gets the result).
+__device__ __forceinline__ uint32_t wave_min_u32_dpp(uint32_t v) {
+    v = min(v, dpp_u32<kDppRowShr1>(0xffffffffu, v));
+    v = min(v, dpp_u32<kDppRowShr2>(0xffffffffu, v));
+    v = min(v, dpp_u32<kDppRowShr4>(0xffffffffu, v));
+    v = min(v, dpp_u32<kDppRowShr8>(0xffffffffu, v));
+    v = min(v, dpp_u32<kDppBcast15, 0xA>(0xffffffffu, v));
+    v = min(v, dpp_u32<kDppBcast31, 0xC>(0xffffffffu, v));
+    return wave_last_u32(v);
+}
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+    v = max(v, dpp_u32<kDppRowShr1>(0u, v));
+    v = max(v, dpp_u32<kDppRowShr2>(0u, v));
+    v = max(v, dpp_u32<kDppRowShr4>(0u, v));
+    v = max(v, dpp_u32<kDppRowShr8>(0u, v));
+    v = max(v, dpp_u32<kDppBcast15, 0xA>(0u, v));
+    v = max(v, dpp_u32<kDppBcast31, 0xC>(0u, v));
+    return wave_last_u32(v);
+}
+// Sum over each 16-lane row; the row total lands in the row's lane 15.
+__device__ __forceinline__ double row_sum_f64(double v) {
+    v += dpp_f64<kDppRowShr1>(0.0, v);
+    v += dpp_f64<kDppRowShr2>(0.0, v);
+    v += dpp_f64<kDppRowShr4>(0.0, v);
+    v += dpp_f64<kDppRowShr8>(0.0, v);
+    return v;
+}
+
 // Index of the pair (i < j) of a 12-point alphabet, row-major upper triangle.
 __host__ __device__ __forceinline__ int pair_index(int i, int j) {
     return i * (2 * kAlpha - i - 1) / 2 + (j - i - 1);
