@@ -115,7 +115,7 @@ typedef struct {
     int64_t shape[KVQ_MAX_TENSORS][4];      /* tensor shapes the plan was made for */
     size_t D_bytes;        /* kvq_eval_candidates D */
     size_t H_bytes;        /* kvq_eval_candidates H */
-    size_t stats_bytes;    /* order statistics, fp32 [R][n_stats] */
+    size_t stats_bytes;    /* order statistics, fp32 [n_stats][R] (GRIDS) or [R][m] (EXACT_DP) */
     size_t choice_bytes;   /* int32 [R] */
     size_t codebook_bytes; /* fp32 [R][s] */
     size_t m_bytes;        /* uint8 [R] */
@@ -143,11 +143,13 @@ kvq_status kvq_plan_blocks(const kvq_tensor* t, int32_t n_tensors,
 
 /* Score every candidate codebook of every block (Implementation notes; Key
    formulas (3); Mathematical statement for H_r).
-   KVQ_GRIDS:  D[R][C]  (fp64) block distortion sum_t (q_{i+1}-x_t)(x_t-q_i),
-               H[R][C]  (fp64) entropy in bits per entry of the expected
+   KVQ_GRIDS (candidate-major tables, so the solve's passes read them with
+               coalesced loads):
+               D[C][R]  (fp64) block distortion sum_t (q_{i+1}-x_t)(x_t-q_i),
+               H[C][R]  (fp64) entropy in bits per entry of the expected
                         frequencies, candidates in the order {min,max},
                         U_3, E_3, ..., U_s, E_s;
-               stats[R][n_stats] (fp32) order statistics at the sorted
+               stats[n_stats][R] (fp32) order statistics at the sorted
                         distinct quantile ranks j (n-1)/(k-1) rounded half up
                         (first = minimum, last = maximum).
    KVQ_EXACT_DP: stats[R][alphabet_m] the alphabet order statistics (with

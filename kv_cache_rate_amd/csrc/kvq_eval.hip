@@ -176,7 +176,8 @@ eval_grids_kernel(Geom g, int s, int NP, RankTable rt, double* __restrict__ D,
     const int CH = (NP + kEvalThreads - 1) / kEvalThreads;
     chunk_prefix(xs, n, CH, tp1, tp2, wt1, wt2);
 
-    for (int k = tid; k < rt.n_stats; k += blockDim.x) stats[r * rt.n_stats + k] = xs[rt.rank[k]];
+    const int64_t R = gridDim.x;
+    for (int k = tid; k < rt.n_stats; k += blockDim.x) stats[k * R + r] = xs[rt.rank[k]];
 
     const float mn = xs[0];
     const float mx = xs[n - 1];
@@ -239,8 +240,8 @@ eval_grids_kernel(Geom g, int s, int NP, RankTable rt, double* __restrict__ D,
             const double pl = carry * inv_n;
             if (pl > 0.0) Hc -= pl * log2(pl);
         }
-        D[r * C + c] = fmax(Dc, 0.0);
-        H[r * C + c] = fmax(Hc, 0.0);
+        D[c * R + r] = fmax(Dc, 0.0);
+        H[c * R + r] = fmax(Hc, 0.0);
     }
 }
 

@@ -169,6 +169,7 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int64_t r = blockIdx.x;
+    const int64_t R = gridDim.x;
     const __half* src = r < nb0 ? x0 + r * 4096 : x1 + (r - nb0) * 4096;
 
     // ---- load: thread owns entries [8 tid, 8 tid + 8) and [2048 + 8 tid, ...)
@@ -431,7 +432,7 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     __syncthreads();  // phase-B storage is reused below
 
     // ---- order statistics out
-    if (tid < nq) stats[r * nq + tid] = sh.tval[tid];
+    if (tid < nq) stats[tid * R + r] = sh.tval[tid];
 
     // ---- raw candidate points: slot (c, j), repeats kept
     PhaseC& pc = sh.u.c;
@@ -512,8 +513,8 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
                 Dc = qm - sumsq;
                 Hc = hb;
             }
-            Dout[r * kMaxCand + c] = fmax(Dc, 0.0);
-            Hout[r * kMaxCand + c] = fmax(Hc, 0.0);
+            Dout[c * R + r] = fmax(Dc, 0.0);
+            Hout[c * R + r] = fmax(Hc, 0.0);
         }
     }
 }

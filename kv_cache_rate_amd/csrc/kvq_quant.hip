@@ -171,13 +171,13 @@ quantize4096_kernel(const void* __restrict__ x0, const void* __restrict__ x1, in
                     const uint64_t* __restrict__ off, uint32_t k0, uint32_t k1,
                     uint32_t* __restrict__ codes) {
     __shared__ float q[kMaxS];
-    __shared__ float inv[kMaxS];
+    __shared__ float inv[kMaxS];  // 2^24 / (q[i+1] - q[i])
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x;
     const int m = min(max((int)m_in[r], 1), s);
     if (tid < kMaxS) q[tid] = tid < m ? codebook[r * s + tid] : __builtin_huge_valf();
     __syncthreads();
-    if (tid + 1 < m) inv[tid] = 1.0f / (q[tid + 1] - q[tid]);
+    if (tid + 1 < m) inv[tid] = 0x1p24f / (q[tid + 1] - q[tid]);
     __syncthreads();
     const int w = code_width(m);
     if (w == 0) return;
@@ -203,16 +203,19 @@ quantize4096_kernel(const void* __restrict__ x0, const void* __restrict__ x1, in
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float xv = x[e];
-            int i = 0;
-            i += (q[i + 8] <= xv) ? 8 : 0;
-            i += (q[i + 4] <= xv) ? 4 : 0;
-            i += (q[i + 2] <= xv) ? 2 : 0;
-            i += (q[i + 1] <= xv) ? 1 : 0;
-            i = min(i, m - 2);
-            float p = (xv - q[i]) * inv[i];
-            p = fminf(fmaxf(p, 0.0f), 1.0f);
-            const float u = (float)(wd[e] >> 8) * 0x1p-24f;
-            const uint32_t code = (uint32_t)i + (u < p ? 1u : 0u);
+            // branch-free search over the 16 padded slots, in byte offsets so
+            // every probe is one LDS read with an immediate offset
+            const char* qb = reinterpret_cast<const char*>(q);
+            uint32_t o = 0;
+            o = (*reinterpret_cast<const float*>(qb + o + 32) <= xv) ? o + 32 : o;
+            o = (*reinterpret_cast<const float*>(qb + o + 16) <= xv) ? o + 16 : o;
+            o = (*reinterpret_cast<const float*>(qb + o + 8) <= xv) ? o + 8 : o;
+            o = (*reinterpret_cast<const float*>(qb + o + 4) <= xv) ? o + 4 : o;
+            const int i = min((int)(o >> 2), m - 2);
+            // p 2^24 against the 24-bit draw (word >> 8): u < p without scaling u;
+            // p outside [0, 1] by round-off decides the same way as its clamp
+            const float p24 = (xv - q[i]) * inv[i];
+            const uint32_t code = (uint32_t)i + ((float)(wd[e] >> 8) < p24 ? 1u : 0u);
             bits |= code << (w * e);
         }
         store_bytes(out + w * ch, bits, w);

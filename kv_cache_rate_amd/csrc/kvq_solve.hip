@@ -168,8 +168,8 @@ rates_grids_kernel(const double* __restrict__ D, const double* __restrict__ H, i
 #pragma unroll
         for (int c = 0; c < kMaxCand; ++c) {
             if (c < C) {
-                Dr[c] = D[r * C + c];
-                Hr[c] = H[r * C + c];
+                Dr[c] = D[c * R + r];
+                Hr[c] = H[c * R + r];
             }
         }
     }
@@ -204,9 +204,10 @@ rates_grids_kernel(const double* __restrict__ D, const double* __restrict__ H, i
 }
 
 // Codepoints of grid candidate c of a block from its order statistics.
-__device__ int build_grid_codebook(int c, const float* st, const RankTable& rt, int n, float* q) {
+__device__ int build_grid_codebook(int c, const float* st, int64_t stride, const RankTable& rt, int n,
+                                   float* q) {
     const float mn = st[0];
-    const float mx = st[rt.n_stats - 1];
+    const float mx = st[(rt.n_stats - 1) * stride];
     if (mn == mx) {
         q[0] = mn;
         return 1;
@@ -224,7 +225,7 @@ __device__ int build_grid_codebook(int c, const float* st, const RankTable& rt, 
         float v;
         if (c == 0) v = j == 0 ? mn : mx;
         else if (uni) v = uniform_point(mn, mx, j, k);
-        else v = st[rt.col[k][j]];
+        else v = st[rt.col[k][j] * stride];
         if (m == 0 || v != q[m - 1]) q[m++] = v;
     }
     return m;
@@ -249,20 +250,20 @@ final_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
     } else if (r < R) {
         const double d = (double)n;
         const double lamd = h->lam_final * d;
-        const double* Dr = D + r * C;
-        const double* Hr = H + r * C;
+        const double* Dr = D + r;
+        const double* Hr = H + r;
         double best = objective(Dr[0], Hr[0], lamd);
         int bc = 0;
         for (int c = 1; c < C; ++c) {
-            const double o = objective(Dr[c], Hr[c], lamd);
+            const double o = objective(Dr[c * R], Hr[c * R], lamd);
             if (o < best) {
                 best = o;
                 bc = c;
             }
         }
-        v = rate_fx(d, Hr[bc], shift);
+        v = rate_fx(d, Hr[bc * R], shift);
         float q[kMaxS];
-        const int m = build_grid_codebook(bc, stats + r * rt.n_stats, rt, n, q);
+        const int m = build_grid_codebook(bc, stats + r, R, rt, n, q);
         choice[r] = bc;
         m_out[r] = (uint8_t)m;
         for (int j = 0; j < s; ++j) codebook[r * s + j] = j < m ? q[j] : 0.0f;

@@ -205,21 +205,23 @@ def kvq_dequantize(plan, codes, codebook, m, word_off, xhat, stream=None):
 # Buffer allocation and chaining (marshalling only; no arithmetic).
 
 def allocate(plan, device="cuda", dequant=False):
-    """Device buffers of the sizes ``plan`` asks for, as torch tensors.
+    """Device buffers of the sizes ``plan`` asks for, as torch tensors
+    (GRIDS tables are candidate-major: D, H are [C, R], stats [n_stats, R]).
 
     64-bit offsets are held in an int64 tensor and codes in an int32 tensor
     (same bits as the uint64 / uint32 the library writes)."""
     import torch
     R = plan.n_blocks
-    if plan.search == KVQ_GRIDS:
-        D = torch.empty((R, plan.n_cand), dtype=torch.float64, device=device)
-        H = torch.empty((R, plan.n_cand), dtype=torch.float64, device=device)
+    if plan.search == KVQ_GRIDS:  # candidate-major tables
+        D = torch.empty((plan.n_cand, R), dtype=torch.float64, device=device)
+        H = torch.empty((plan.n_cand, R), dtype=torch.float64, device=device)
+        stats = torch.empty((plan.n_stats, R), dtype=torch.float32, device=device)
     else:
         D = torch.empty((R, plan.n_cand), dtype=torch.float64, device=device)
         H = torch.empty((R, plan.n_cand, 2), dtype=torch.float64, device=device)
+        stats = torch.empty((R, plan.n_stats), dtype=torch.float32, device=device)
     buf = {
-        "D": D, "H": H,
-        "stats": torch.empty((R, plan.n_stats), dtype=torch.float32, device=device),
+        "D": D, "H": H, "stats": stats,
         "choice": torch.empty(R, dtype=torch.int32, device=device),
         "codebook": torch.empty((R, plan.s), dtype=torch.float32, device=device),
         "m": torch.empty(R, dtype=torch.uint8, device=device),

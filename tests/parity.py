@@ -43,6 +43,10 @@ def run_gpu(tensors, *, tokens_per_block, dims_per_block, s, search, alphabet_m=
     lam_out, rate = kvq.admit(plan, dev, buf, B, md, iters, eta, lam, seed, dequant=dequant)
     torch.cuda.synchronize()
     out = {k: v.cpu().numpy() for k, v in buf.items() if k != "workspace"}
+    if sm == kvq.KVQ_GRIDS:  # candidate-major on the device; block-major here
+        out["D"] = np.ascontiguousarray(out["D"].T)
+        out["H"] = np.ascontiguousarray(out["H"].T)
+        out["stats"] = np.ascontiguousarray(out["stats"].T)
     out["off"] = out["off"].view(np.uint64)
     out["codes"] = out["codes"].view(np.uint32)
     out["lam"] = lam_out
