@@ -113,6 +113,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="long_context_kv_fp16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a device-to-device copy of BYTES (reference for HBM "
+                         "byte counters) and exit")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -123,6 +126,15 @@ def main():
     import torch
     from kv_cache_rate_amd import kvq
     from kv_cache_rate_amd import workloads as W
+
+    if a.copy_probe:
+        src = torch.ones(a.copy_probe // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": src.numel() * 4, "copies": 3}), flush=True)
+        return
 
     w = W.BY_NAME[a.workload]
     log(f"generating {w.name}: {w.n_entries} entries, {w.input_bytes / 1e9:.2f} GB")

@@ -167,7 +167,7 @@ eval_grids_kernel(Geom g, int s, int NP, RankTable rt, double* __restrict__ D,
     __shared__ int crank[kMaxCand][kMaxS];
     __shared__ double cp1[kMaxCand][kMaxS], cp2[kMaxCand][kMaxS];
 
-    const int64_t r = blockIdx.x;
+    const int64_t r = xcd_block(blockIdx.x, gridDim.x);
     const int n = g.n;
     const int C = 1 + 2 * (s - 2);
     const int tid = threadIdx.x;

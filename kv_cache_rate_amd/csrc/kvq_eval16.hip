@@ -168,8 +168,8 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t r = blockIdx.x;
     const int64_t R = gridDim.x;
+    const int64_t r = xcd_block(blockIdx.x, R);
     const __half* src = r < nb0 ? x0 + r * 4096 : x1 + (r - nb0) * 4096;
 
     // ---- load: thread owns entries [8 tid, 8 tid + 8) and [2048 + 8 tid, ...)

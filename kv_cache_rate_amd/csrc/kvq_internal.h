@@ -226,6 +226,18 @@ __device__ __forceinline__ double row_sum_f64(double v) {
     return v;
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  Mapping workgroup b to block r so that XCD x owns the contiguous
+// range of blocks [start_x, start_x + count_x) lets neighbouring blocks'
+// writes into block-interleaved tables combine in one L2.  Bijective on
+// [0, R).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t R) {
+    const int64_t x = b % kXcds, idx = b / kXcds;
+    const int64_t q = R / kXcds, rem = R % kXcds;
+    return x * q + (x < rem ? x : rem) + idx;
+}
+
 // Index of the pair (i < j) of a 12-point alphabet, row-major upper triangle.
 __host__ __device__ __forceinline__ int pair_index(int i, int j) {
     return i * (2 * kAlpha - i - 1) / 2 + (j - i - 1);

@@ -119,3 +119,17 @@ def test_calls_validate_before_launch(L):
     assert Lb.kvq_quantize_pack(ctypes.byref(p), arr, 1, 8, 8, 8, 0, 8, p.max_code_words - 1,
                                 None) == kvq.KVQ_ENOSPC
     assert Lb.kvq_dequantize(ctypes.byref(p), 8, None, 8, 8, 8, None) == kvq.KVQ_EINVAL
+
+
+def test_xcd_block_mapping_is_a_bijection():
+    """Host-side check of the workgroup -> block mapping used by the scoring
+    kernels (XCD x owns a contiguous range of blocks)."""
+    def xcd_block(b, R, X=8):
+        x, idx = b % X, b // X
+        q, rem = R // X, R % X
+        return x * q + min(x, rem) + idx
+    for R in (1, 7, 8, 9, 45, 64, 1000, 8192, 524288 + 3):
+        got = sorted(xcd_block(b, R) for b in range(R))
+        assert got == list(range(R))
+        # XCD 0's blocks are contiguous from 0
+        assert [xcd_block(b, R) for b in range(0, min(R, 64), 8)] == list(range(len(range(0, min(R, 64), 8))))
