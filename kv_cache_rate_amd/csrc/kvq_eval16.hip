@@ -16,19 +16,22 @@
 // fp16 entries are mapped to order-preserving 16-bit keys.  A key's top 10
 // bits pick a coarse bin (1024 bins); inside a bin the 64 values are
 // v = B + f U (f = low 6 key bits, U = the bin's ulp), so a bin is summarised
-// exactly by (count, sum of f) packed in one 32-bit LDS word.  Sweep 1 fills
-// these; a prefix over bins gives counts and exact fp64 sums at bin edges
-// (fp16 sums of 4096 entries are exact in fp64).  The coarse bins that hold
-// a wanted order statistic or a uniform-grid threshold get per-key counts in
-// sweep 2 (packed 16-bit counters, rows padded to 33 words so lanes reading
-// different bins hit different LDS banks) plus totals of each run of 8 keys,
-// and one lane per threshold finishes its prefix inside the bin in at most
-// 8 + 4 steps.  Order statistics are therefore exact data values and every
-// prefix is exact; only the final per-interval algebra rounds (fp64).
+// exactly by (count, sum of f) packed in one 32-bit LDS word, count in the
+// top 13 bits.  Sweep 1 fills these; a prefix over bins gives counts and
+// exact fp64 sums at bin edges (fp16 sums of 4096 entries are exact in fp64).
+// The bins that hold a wanted order statistic or a uniform-grid threshold
+// claim a slot; sweep 2 gives each slot per-key 16-bit counts and packed
+// (count, sum f) totals of its eight 8-key groups.  One lane per threshold
+// then finishes its prefix inside the bin with two branch-free 8-step scans
+// (groups, then keys).  Order statistics are therefore exact data values and
+// every prefix is exact; only the per-interval algebra rounds (fp64).
 //
-// Workgroup = one block, 256 threads x 16 entries kept in registers; the
-// candidate phase maps one 16-lane row to one candidate so its totals are a
-// row reduction.
+// Candidate phase: one lane per candidate interval (239 intervals over the 29
+// candidates, packed two candidates to a 16-lane row so that a row shift
+// brings in the neighbouring interval), then one lane per candidate sums its
+// intervals' terms in a fixed order.
+//
+// Workgroup = one block, 256 threads x 16 entries kept in registers.
 #include <math.h>
 #include <string.h>
 
@@ -41,57 +44,58 @@ namespace {
 constexpr int kT = 256;            // threads per block
 constexpr int kPer = 16;           // entries per thread
 constexpr int kNC = 1024;          // coarse bins
-constexpr int kSlotStride = 33;    // 32 words of packed 16-bit counts + pad
-constexpr int kGrpStride = 9;      // 8 group words + pad
 constexpr int kMaxSlots = 144;     // every target and threshold bin fits
+constexpr int kFW = 32;            // per-key count words of a slot (64 x 16 bit)
+constexpr int kSW = 40;            // words per slot: 32 per-key + 8 group totals
 constexpr int kNU = 71;            // distinct interior uniform fractions, s = 16
 constexpr int kNQ = 73;            // order statistics, s = 16, n = 4096
-constexpr int kPS = kMaxS + 1;     // padded row of per-candidate arrays
-constexpr int kSlots = kMaxCand * kMaxS;  // 464 (candidate, point) slots
-constexpr uint16_t kNoSlot = 0xffff;
-// point sources (per (candidate, point) slot)
-constexpr uint16_t kSrcNone = 0xffff, kSrcMin = 0, kSrcMax = 1, kSrcUni = 0x100, kSrcQnt = 0x200;
+constexpr int kPU = 2;             // point table: 0 = min, 1 = max,
+constexpr int kPQ = kPU + kNU;     //   then uniform thresholds, then order statistics
+constexpr int kNP = kPQ + kNQ;     // 146 points
+constexpr int kRows = 15;          // 16-lane rows of candidate intervals
+constexpr uint32_t kNoSlot = 0xffffffffu, kClaim = 0xfffffffeu;
+constexpr uint32_t kCnt1 = 1u << 19;       // one entry in a packed (count, sum f) word
+constexpr uint32_t kLowF = kCnt1 - 1u;     // sum-of-f field
+constexpr uint32_t kNoLane = 0xffffffffu;  // lane without an interval
+constexpr int kDppRowShl1 = 0x101;         // row_shl:1, lane l reads lane l + 1
+
+struct Point {                     // a codepoint and the entries below it
+    float v;
+    uint32_t cnt;
+    double s1;
+};
 
 struct PhaseA {                    // sweep 1 .. threshold search
-    uint32_t cnt[kNC + 1];         // payload count | sum(f) << 13, then exclusive prefix counts
+    uint32_t cnt[kNC + 4];         // payload, then exclusive prefix counts
     double ps1[kNC + 1];           // exclusive prefix sums
 };
 struct PhaseB {                    // sweep 2 .. prefix finish
-    uint32_t fine[kMaxSlots * kSlotStride];
-    uint32_t grp[kMaxSlots * kGrpStride];  // count | sum(f within group) << 16
+    uint32_t w[kMaxSlots * kSW];
 };
-struct PhaseC {                    // candidate points and interval masses
-    float pval[kMaxCand * kPS];
-    uint32_t pcnt[kMaxCand * kPS];
-    double ps1[kMaxCand * kPS];
-    double ma[kMaxCand * kPS];
-    double mb[kMaxCand * kPS];
+struct PhaseC {                    // candidate intervals
+    double dterm[kT];
+    double hterm[kT];
+    double mr[kT];                 // mass at the interval's right point
+    double ma[kT];                 // mass the interval sends to its left point
+    float bv[kT];                  // right point
 };
 
 struct Shared {
-    union {
+    union alignas(16) {
         PhaseA a;
         PhaseB b;
         PhaseC c;
     } u;
-    uint16_t slot[kNC];            // resolved bin -> slot * kSlotStride, or kNoSlot
-    uint16_t src[kSlots];          // point source of slot (c, j)
+    alignas(16) uint32_t slot[kNC];  // bin -> byte offset of its slot, or kNoSlot
+    alignas(16) Point P[kNP];
     uint16_t tbin[kNQ];
     uint16_t tloc[kNQ];
-    float tval[kNQ];
-    uint32_t tcnt[kNQ];
-    double ts1[kNQ];
     uint16_t ukey[kNU];
-    float uval[kNU];
-    uint32_t ucnt[kNU];
-    double us1[kNU];
     double lg_c[32];
     double lg_inv[32];
-    uint32_t wmin[kT / 64], wmax[kT / 64], wamax[kT / 64];
-    double wsq[kT / 64];
-    uint32_t wtot[kT / 64];
-    double wts1[kT / 64];
-    int nslots;
+    uint32_t wmin[kT / 64], wmax[kT / 64], wtot[kT / 64];
+    double wsq[kT / 64], wts1[kT / 64];
+    uint32_t nslots;
 };
 
 typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
@@ -148,19 +152,59 @@ __device__ __forceinline__ double log2_unit(double x, const double* lg_c, const 
     return ((double)e + lg_c[i]) + l1p * 1.4426950408889634;  // 1/ln 2
 }
 
+// -pi log2 pi of a point holding mass m of the 4096 entries.
+__device__ __forceinline__ double point_entropy(double m, const double* lg_c, const double* lg_inv) {
+    const double pi = m * (1.0 / 4096.0);
+    return pi > 0.0 ? -pi * log2_unit(pi, lg_c, lg_inv) : 0.0;
+}
+
+// Claim a slot for coarse bin `bin` (first caller wins; the slot's byte
+// offset is visible after the next barrier).
+__device__ __forceinline__ void claim_slot(Shared& sh, uint32_t bin) {
+    if (atomicCAS(&sh.slot[bin], kNoSlot, kClaim) == kNoSlot)
+        sh.slot[bin] = atomicAdd(&sh.nslots, 1u) * (uint32_t)(4 * kSW);
+}
+
+// 16-byte quad q of the slot at byte offset sb (q 0..7: per-key counts of
+// group q; 8, 9: the group totals).
+__device__ __forceinline__ uint4 slot_quad(const Shared& sh, uint32_t sb, uint32_t q) {
+    const char* p = reinterpret_cast<const char*>(sh.u.b.w) + sb + 16u * q;
+    return *reinterpret_cast<const uint4*>(__builtin_assume_aligned(p, 16));
+}
+
+// 16-bit count of key i (0..7) of a group held in four words.
+__device__ __forceinline__ uint32_t key_count(const uint4& w, int i) {
+    const uint32_t x = (i >> 1) == 0 ? w.x : (i >> 1) == 1 ? w.y : (i >> 1) == 2 ? w.z : w.w;
+    return (i & 1) ? (x >> 16) : (x & 0xffffu);
+}
+__device__ __forceinline__ uint32_t word_of(const uint4& a, const uint4& b, int i) {
+    switch (i) {
+        case 0: return a.x;
+        case 1: return a.y;
+        case 2: return a.z;
+        case 3: return a.w;
+        case 4: return b.x;
+        case 5: return b.y;
+        case 6: return b.z;
+        default: return b.w;
+    }
+}
+
 }  // namespace
 
-// Threshold tables from the host.
+// Tables from the host.
 struct Eval16Tables {
     RankTable rt;
     uint8_t unum[kNU];              // numerator of distinct fraction u
     uint8_t uden[kNU];              // denominator
-    uint16_t src[kSlots];           // point source of (candidate, point) slot
+    uint16_t red[kMaxCand];         // candidate c: first lane | interval count << 8
+    uint32_t desc[kT];              // lane: left point | right point << 8 |
+                                    //   first << 21 | last << 22, or kNoLane
     double lg_c[32];                // log2(1 + (2i+1)/64)
     double lg_inv[32];              // 1 / (1 + (2i+1)/64)
 };
 
-__global__ void __launch_bounds__(kT)
+__global__ void __launch_bounds__(kT, 5)
 eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int64_t nb0,
               Eval16Tables tb, double* __restrict__ Dout, double* __restrict__ Hout,
               float* __restrict__ stats, WsHeader* ws) {
@@ -180,17 +224,18 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         hw[0] = a.x; hw[1] = a.y; hw[2] = a.z; hw[3] = a.w;
         hw[4] = b.x; hw[5] = b.y; hw[6] = b.z; hw[7] = b.w;
     }
-    for (int i = tid; i < kNC; i += kT) sh.u.a.cnt[i] = 0u;
-    for (int i = tid; i < kSlots; i += kT) sh.src[i] = tb.src[i];
+    reinterpret_cast<uint4*>(sh.u.a.cnt)[tid] = make_uint4(0u, 0u, 0u, 0u);
     if (tid < 32) {
         sh.lg_c[tid] = tb.lg_c[tid];
         sh.lg_inv[tid] = tb.lg_inv[tid];
     }
+    if (tid == 0) sh.nslots = 0u;
     __syncthreads();
 
     // ---- sweep 1 (two entries per 32-bit word): canonical -0, keys,
-    //      coarse histogram, min/max keys, max |bits|, sum of squares
-    ushort2_t kmin2 = {0xffff, 0xffff}, kmax2 = {0, 0}, amax2 = {0, 0};
+    //      coarse histogram, min/max keys, sum of squares.  NaN and Inf land
+    //      in bins 0..15 and 1008..1023, which hold nothing else.
+    ushort2_t kmin2 = {0xffff, 0xffff}, kmax2 = {0, 0};
     double sq = 0.0;
     uint32_t keys2[kPer / 2];
 #pragma unroll
@@ -205,51 +250,42 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         const ushort2_t kv = __builtin_bit_cast(ushort2_t, k2);
         kmin2 = __builtin_elementwise_min(kmin2, kv);
         kmax2 = __builtin_elementwise_max(kmax2, kv);
-        amax2 = __builtin_elementwise_max(amax2, __builtin_bit_cast(ushort2_t, w & 0x7fff7fffu));
         const double v0 = (double)(float)hv.x, v1 = (double)(float)hv.y;
         sq = fma(v0, v0, sq);
         sq = fma(v1, v1, sq);
         const uint32_t klo = k2 & 0xffffu, khi = k2 >> 16;
-        atomicAdd(&sh.u.a.cnt[klo >> 6], 1u | ((klo & 63u) << 13));
-        atomicAdd(&sh.u.a.cnt[khi >> 6], 1u | ((khi & 63u) << 13));
+        atomicAdd(&sh.u.a.cnt[klo >> 6], (klo & 63u) | kCnt1);
+        atomicAdd(&sh.u.a.cnt[khi >> 6], (khi & 63u) | kCnt1);
     }
     {
         const uint32_t kmin = wave_min_u32_dpp(min((uint32_t)kmin2.x, (uint32_t)kmin2.y));
         const uint32_t kmax = wave_max_u32_dpp(max((uint32_t)kmax2.x, (uint32_t)kmax2.y));
-        const uint32_t amax = wave_max_u32_dpp(max((uint32_t)amax2.x, (uint32_t)amax2.y));
         const double sqw = wave_last_f64(wave_scan_add_f64(sq));
         if (lane == 0) {
             sh.wmin[wave] = kmin;
             sh.wmax[wave] = kmax;
-            sh.wamax[wave] = amax;
             sh.wsq[wave] = sqw;
         }
     }
     __syncthreads();
     const uint32_t kmin = min(min(sh.wmin[0], sh.wmin[1]), min(sh.wmin[2], sh.wmin[3]));
     const uint32_t kmax = max(max(sh.wmax[0], sh.wmax[1]), max(sh.wmax[2], sh.wmax[3]));
-    if (tid == 0 && max(max(sh.wamax[0], sh.wamax[1]), max(sh.wamax[2], sh.wamax[3])) >= 0x7c00u)
-        atomicOr(&ws->status, kStatusNonFinite);
     const double sumsq = (sh.wsq[0] + sh.wsq[1]) + (sh.wsq[2] + sh.wsq[3]);
     const float mn = key_value(kmin);
     const float mx = key_value(kmax);
 
-    // ---- coarse prefix: thread owns bins [4 tid, 4 tid + 4) (one binade,
-    //      B_k = B0 + 64 k U), prefix counts written over the payloads
+    // ---- coarse prefix: thread owns bins [4 tid, 4 tid + 4) = keys
+    //      [256 tid, 256 tid + 256), one binade: value = B0 + (key offset) U
     {
-        const uint32_t bin0 = 4 * tid;
-        const float B0 = key_value(bin0 << 6);
-        const double U = (double)(key_value((bin0 << 6) | 1u) - B0);
-        uint32_t c[4], acc[4];
-        uint32_t ct = 0, at = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t p = sh.u.a.cnt[bin0 + k];
-            c[k] = p & 0x1fffu;
-            acc[k] = 64u * (uint32_t)k * c[k] + (p >> 13);
-            ct += c[k];
-            at += acc[k];
-        }
+        const float B0 = key_value((uint32_t)tid << 8);
+        const double U = (double)(key_value(((uint32_t)tid << 8) | 1u) - B0);
+        const uint4 pw = reinterpret_cast<const uint4*>(sh.u.a.cnt)[tid];
+        const uint32_t c[4] = {pw.x >> 19, pw.y >> 19, pw.z >> 19, pw.w >> 19};
+        const uint32_t acc[4] = {pw.x & kLowF, 64u * c[1] + (pw.y & kLowF),
+                                 128u * c[2] + (pw.z & kLowF), 192u * c[3] + (pw.w & kLowF)};
+        const uint32_t ct = (c[0] + c[1]) + (c[2] + c[3]);
+        const uint32_t at = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        if ((tid < 4 || tid >= kT - 4) && ct != 0u) atomicOr(&ws->status, kStatusNonFinite);
         // empty threads add exactly 0 (the Inf/NaN code bins have no finite base)
         const double st = ct ? (double)ct * (double)B0 + U * (double)at : 0.0;
         const uint32_t ic = wave_scan_add_u32(ct);
@@ -259,23 +295,27 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
             sh.wts1[wave] = is;
         }
         __syncthreads();
-        uint32_t oc = 0;
-        double os = 0.0;
-        for (int w = 0; w < wave; ++w) {
-            oc += sh.wtot[w];
-            os += sh.wts1[w];
-        }
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        const uint32_t oc = (wv > 0 ? sh.wtot[0] : 0u) + (wv > 1 ? sh.wtot[1] : 0u) +
+                            (wv > 2 ? sh.wtot[2] : 0u);
+        const double os = ((wv > 0 ? sh.wts1[0] : 0.0) + (wv > 1 ? sh.wts1[1] : 0.0)) +
+                          (wv > 2 ? sh.wts1[2] : 0.0);
         const uint32_t base_c = oc + ic - ct;
         const double base_s = os + (is - st);
         uint32_t runc = 0, runa = 0;
+        uint32_t pc[4];
+        double ps[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            sh.u.a.cnt[bin0 + k] = base_c + runc;
-            sh.u.a.ps1[bin0 + k] = runc ? base_s + (double)runc * (double)B0 + U * (double)runa : base_s;
+            pc[k] = base_c + runc;
+            ps[k] = runc ? base_s + (double)runc * (double)B0 + U * (double)runa : base_s;
             runc += c[k];
             runa += acc[k];
-            sh.slot[bin0 + k] = kNoSlot;
         }
+        reinterpret_cast<uint4*>(sh.u.a.cnt)[tid] = make_uint4(pc[0], pc[1], pc[2], pc[3]);
+        reinterpret_cast<double2*>(sh.u.a.ps1)[2 * tid] = make_double2(ps[0], ps[1]);
+        reinterpret_cast<double2*>(sh.u.a.ps1)[2 * tid + 1] = make_double2(ps[2], ps[3]);
+        reinterpret_cast<uint4*>(sh.slot)[tid] = make_uint4(kNoSlot, kNoSlot, kNoSlot, kNoSlot);
         if (tid == kT - 1) {
             sh.u.a.cnt[kNC] = base_c + ct;
             sh.u.a.ps1[kNC] = base_s + st;
@@ -283,23 +323,20 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     }
     __syncthreads();
 
-    // ---- targets (order statistics) on threads 0..72, uniform thresholds on
-    //      threads 128..198: find the bin, read its prefix, mark it
-    const int nq = tb.rt.n_stats;  // 73
-    if (tid < nq) {
+    // ---- order statistics on threads 0..72, uniform thresholds on threads
+    //      128..198: find the bin, read its prefix, claim a slot
+    if (tid < kNQ) {
         const uint32_t rank = (uint32_t)tb.rt.rank[tid];
-        int lo = 0, hi = kNC - 1;  // last bin with prefix count <= rank
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (sh.u.a.cnt[mid] <= rank) lo = mid;
-            else hi = mid - 1;
-        }
+        uint32_t lo = 0;  // last bin with prefix count <= rank
+#pragma unroll
+        for (uint32_t half = kNC / 2; half; half >>= 1)
+            if (sh.u.a.cnt[lo + half] <= rank) lo += half;
         const uint32_t pc = sh.u.a.cnt[lo];
         sh.tbin[tid] = (uint16_t)lo;
         sh.tloc[tid] = (uint16_t)(rank - pc);
-        sh.tcnt[tid] = pc;
-        sh.ts1[tid] = sh.u.a.ps1[lo];
-        sh.slot[lo] = 0;  // mark
+        sh.P[kPQ + tid].cnt = pc;
+        sh.P[kPQ + tid].s1 = sh.u.a.ps1[lo];
+        claim_slot(sh, lo);
     } else if (tid >= 128 && tid < 128 + kNU) {
         const int u = tid - 128;
         float t;
@@ -311,211 +348,190 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         }
         const uint32_t key = key_ceil(t);
         const uint32_t bin = key >> 6;
-        sh.uval[u] = t;
+        const uint32_t pc = sh.u.a.cnt[bin];
         sh.ukey[u] = (uint16_t)key;
-        sh.ucnt[u] = sh.u.a.cnt[bin];
-        sh.us1[u] = sh.u.a.ps1[bin];
-        sh.slot[bin] = 0;  // mark
-    }
-    const double total_s1 = sh.u.a.ps1[kNC];
-    __syncthreads();
-    // compact marked bins into slots (thread owns 4 bins); at most 73 + 71
-    {
-        uint32_t m4 = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) m4 += sh.slot[4 * tid + k] == 0 ? 1u : 0u;
-        const uint32_t im = wave_scan_add_u32(m4);
-        if (lane == 63) sh.wtot[wave] = im;
-        __syncthreads();
-        uint32_t o = 0;
-        for (int w = 0; w < wave; ++w) o += sh.wtot[w];
-        uint32_t s = o + im - m4;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int bin = 4 * tid + k;
-            if (sh.slot[bin] == 0) sh.slot[bin] = (uint16_t)(kSlotStride * s++);
-        }
-        if (tid == kT - 1) sh.nslots = (int)s;
+        sh.P[kPU + u].v = t;
+        sh.P[kPU + u].cnt = pc;
+        sh.P[kPU + u].s1 = sh.u.a.ps1[bin];
+        if (sh.u.a.cnt[bin + 1] != pc) claim_slot(sh, bin);  // an empty bin's edge is exact
+    } else if (tid == kT - 1) {
+        sh.P[0].v = mn;
+        sh.P[0].cnt = 0u;
+        sh.P[0].s1 = 0.0;
+        sh.P[1].v = mx;
+        sh.P[1].cnt = 4096u;
+        sh.P[1].s1 = sh.u.a.ps1[kNC];
     }
     __syncthreads();
-    const int nslots = sh.nslots;  // <= 144 = kMaxSlots
-    for (int i = tid; i < nslots * kSlotStride; i += kT) sh.u.b.fine[i] = 0u;
+    const uint32_t nslots = sh.nslots;  // <= 144 = kMaxSlots
+    for (uint32_t i = tid; i < nslots * (kSW / 4); i += kT)
+        reinterpret_cast<uint4*>(sh.u.b.w)[i] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
 
-    // ---- sweep 2: per-key counts in resolved bins
+    // ---- sweep 2: per-key counts and group totals in the claimed bins
+    //      (the keys pass through an empty asm so that sweep 1's payloads are
+    //      recomputed here rather than held in registers across the phases)
+    uint32_t sl[kPer];
 #pragma unroll
     for (int p = 0; p < kPer / 2; ++p) {
-#pragma unroll
-        for (int hpart = 0; hpart < 2; ++hpart) {
-            const uint32_t key = hpart ? keys2[p] >> 16 : keys2[p] & 0xffffu;
-            const uint32_t sl = sh.slot[key >> 6];
-            if (sl != kNoSlot)
-                atomicAdd(&sh.u.b.fine[sl + ((key & 63u) >> 1)], 1u << ((key & 1u) * 16));
-        }
+        asm volatile("" : "+v"(keys2[p]));
+        sl[2 * p] = sh.slot[(keys2[p] & 0xffffu) >> 6];
+        sl[2 * p + 1] = sh.slot[keys2[p] >> 22];
     }
-    __syncthreads();
-    // group totals: 8 keys (4 words) per group, 8 groups per slot
-    for (int g = tid; g < nslots * 8; g += kT) {
-        const int s = g >> 3, gi = g & 7;
-        const uint32_t* fw = &sh.u.b.fine[s * kSlotStride + 4 * gi];
-        uint32_t cn = 0, fs = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t w = fw[q];
-            const uint32_t c0 = w & 0xffffu, c1 = w >> 16;
-            cn += c0 + c1;
-            fs += (2 * q) * c0 + (2 * q + 1) * c1;
+    for (int i = 0; i < kPer; ++i) {
+        if (sl[i] != kNoSlot) {
+            const uint32_t key = (i & 1) ? keys2[i >> 1] >> 16 : keys2[i >> 1];
+            char* base = reinterpret_cast<char*>(sh.u.b.w) + sl[i];
+            // key (f = key & 63) counts 1 in the 16-bit half f & 1 of word f >> 1
+            atomicAdd(reinterpret_cast<uint32_t*>(base + ((key & 62u) << 1)),
+                      1u + (key & 1u) * 0xffffu);
+            atomicAdd(reinterpret_cast<uint32_t*>(base + 4 * kFW + ((key >> 1) & 28u)),
+                      (key & 63u) + kCnt1);
         }
-        sh.u.b.grp[s * kGrpStride + gi] = cn | (fs << 16);
     }
     __syncthreads();
 
     // ---- finish the prefixes inside the bins
-    if (tid < nq) {
+    if (tid < kNQ) {
         const uint32_t bin = sh.tbin[tid];
-        const uint32_t sbase = sh.slot[bin];
+        const uint32_t s = sh.slot[bin];
         const uint32_t loc = sh.tloc[tid];
-        const uint32_t* gw = &sh.u.b.grp[(sbase / kSlotStride) * kGrpStride];
-        uint32_t N = 0, F1 = 0;
-        int gi = 0;
-        for (; gi < 7; ++gi) {
-            const uint32_t g = gw[gi];
-            const uint32_t gc = g & 0xffffu;
-            if (N + gc > loc) break;
-            N += gc;
-            F1 += 8u * (uint32_t)gi * gc + (g >> 16);
+        const uint4 ga = slot_quad(sh, s, 8), gb = slot_quad(sh, s, 9);
+        // group holding local rank loc: groups whose running count <= loc
+        const uint32_t lim = (loc + 1u) << 19;
+        uint32_t S = 0, Pg = 0, gi = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            S += word_of(ga, gb, i);
+            const bool take = S < lim;
+            gi += take ? 1u : 0u;
+            Pg = take ? S : Pg;
         }
-        const uint32_t* fw = &sh.u.b.fine[sbase + 4 * gi];
-        uint32_t f = 8 * gi + 7;
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t w = fw[q];
-            const uint32_t c0 = w & 0xffffu, c1 = w >> 16;
-            const uint32_t f0 = 8 * gi + 2 * q;
-            if (N + c0 > loc) { f = f0; break; }
-            N += c0;
-            F1 += f0 * c0;
-            if (N + c1 > loc) { f = f0 + 1; break; }
-            N += c1;
-            F1 += (f0 + 1) * c1;
+        gi = min(gi, 7u);
+        const uint4 fw = slot_quad(sh, s, gi);
+        const uint32_t rlim = (loc - (Pg >> 19) + 1u) << 19;
+        uint32_t T = 0, Ts = 0, kk = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            T += key_count(fw, i) * (kCnt1 + (uint32_t)i);
+            const bool take = T < rlim;
+            kk += take ? 1u : 0u;
+            Ts = take ? T : Ts;
         }
+        const uint32_t f = min(8u * gi + kk, 63u);
+        const uint32_t nl = Ts >> 19;
+        const uint32_t N = (Pg >> 19) + nl;
+        const uint32_t F = (Pg & kLowF) + 8u * gi * nl + (Ts & kLowF);
         const float B = key_value(bin << 6);
         const float U = key_value((bin << 6) | 1u) - B;
-        sh.tval[tid] = key_value((bin << 6) | f);
-        sh.tcnt[tid] += N;
-        if (N) sh.ts1[tid] += (double)B * (double)N + (double)U * (double)F1;
+        const float v = key_value((bin << 6) | f);
+        sh.P[kPQ + tid].v = v;
+        sh.P[kPQ + tid].cnt += N;
+        if (N) sh.P[kPQ + tid].s1 += (double)B * (double)N + (double)U * (double)F;
+        stats[tid * R + r] = v;
     } else if (tid >= 128 && tid < 128 + kNU) {
         const int u = tid - 128;
         const uint32_t key = sh.ukey[u];
         const uint32_t bin = key >> 6;
-        const uint32_t sbase = sh.slot[bin];
-        const uint32_t fstop = key & 63u;
-        const uint32_t* gw = &sh.u.b.grp[(sbase / kSlotStride) * kGrpStride];
-        uint32_t N = 0, F1 = 0;
-        const int gstop = (int)(fstop >> 3);
-        for (int gi = 0; gi < gstop; ++gi) {
-            const uint32_t g = gw[gi];
-            const uint32_t gc = g & 0xffffu;
-            N += gc;
-            F1 += 8u * (uint32_t)gi * gc + (g >> 16);
+        const uint32_t s = sh.slot[bin];
+        if (s != kNoSlot) {
+            const uint32_t f = key & 63u;
+            const uint32_t gs = f >> 3, fs = f & 7u;
+            const uint4 ga = slot_quad(sh, s, 8), gb = slot_quad(sh, s, 9);
+            uint32_t S = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) S += (uint32_t)i < gs ? word_of(ga, gb, i) : 0u;
+            const uint4 fw = slot_quad(sh, s, gs);
+            uint32_t T = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                T += (uint32_t)i < fs ? key_count(fw, i) * (kCnt1 + (uint32_t)i) : 0u;
+            const uint32_t nl = T >> 19;
+            const uint32_t N = (S >> 19) + nl;
+            const uint32_t F = (S & kLowF) + 8u * gs * nl + (T & kLowF);
+            const float B = key_value(bin << 6);
+            const float U = key_value((bin << 6) | 1u) - B;
+            sh.P[kPU + u].cnt += N;
+            if (N) sh.P[kPU + u].s1 += (double)B * (double)N + (double)U * (double)F;
         }
-        const uint32_t* fw = &sh.u.b.fine[sbase + 4 * gstop];
-        for (uint32_t f = 8u * gstop; f < fstop; ++f) {
-            const uint32_t c = (fw[(f >> 1) - 4u * gstop] >> ((f & 1u) * 16)) & 0xffffu;
-            N += c;
-            F1 += f * c;
-        }
-        const float B = key_value(bin << 6);
-        const float U = key_value((bin << 6) | 1u) - B;
-        sh.ucnt[u] += N;
-        if (N) sh.us1[u] += (double)B * (double)N + (double)U * (double)F1;
     }
     __syncthreads();  // phase-B storage is reused below
 
-    // ---- order statistics out
-    if (tid < nq) stats[tid * R + r] = sh.tval[tid];
-
-    // ---- raw candidate points: slot (c, j), repeats kept
+    // ---- candidate intervals, one per lane: masses to both ends, the
+    //      distortion term a^2 M_a + b^2 M_b and the entropy term of the
+    //      right point (its mass: this interval's share plus the next one's)
     PhaseC& pc = sh.u.c;
-    for (int sl = tid; sl < kSlots; sl += kT) {
-        const uint16_t sc = sh.src[sl];
-        if (sc != kSrcNone) {
-            float v;
-            uint32_t cn;
-            double s1;
-            if (sc == kSrcMin) {
-                v = mn; cn = 0; s1 = 0.0;
-            } else if (sc == kSrcMax) {
-                v = mx; cn = 4096; s1 = total_s1;
-            } else if (sc < kSrcQnt) {
-                const int u = sc - kSrcUni;
-                v = sh.uval[u]; cn = sh.ucnt[u]; s1 = sh.us1[u];
-            } else {
-                const int q = sc - kSrcQnt;
-                v = sh.tval[q]; cn = sh.tcnt[q]; s1 = sh.ts1[q];
-            }
-            const int i0 = (sl >> 4) * kPS + (sl & 15);
-            pc.pval[i0] = v;
-            pc.pcnt[i0] = cn;
-            pc.ps1[i0] = s1;
+    const uint32_t d = tb.desc[tid];
+    double ma = 0.0, mb = 0.0, dterm = 0.0;
+    float bq = 0.0f;
+    bool zero_width = false;
+    if (d != kNoLane) {
+        const Point pa = sh.P[d & 0xffu];
+        const Point pb = sh.P[(d >> 8) & 0xffu];
+        const double A = pa.v, Bq = pb.v;
+        const double C = (double)(pb.cnt - pa.cnt);
+        const double wd = Bq - A;
+        mb = C;  // an interval between equal points carries the entries equal
+                 // to them (possible only at the closed maximum)
+        if (wd > 0.0) {
+            mb = (pb.s1 - pa.s1 - A * C) * recip(wd);
+            mb = fmin(fmax(mb, 0.0), C);
+        } else {
+            zero_width = true;
         }
+        ma = C - mb;
+        dterm = A * A * ma + Bq * Bq * mb;
+        bq = pb.v;
     }
-    __syncthreads();
-    // interval masses; an interval between two equal points carries the
-    // entries equal to that point (possible only at the closed maximum)
-    for (int sl = tid; sl < kSlots; sl += kT) {
-        if ((sl & 15) < 15 && sh.src[sl + 1] != kSrcNone) {
-            const int i0 = (sl >> 4) * kPS + (sl & 15);
-            const double a = pc.pval[i0], b = pc.pval[i0 + 1];
-            const double Cn = (double)(pc.pcnt[i0 + 1] - pc.pcnt[i0]);
-            double mbv = Cn;
-            if (b > a) {
-                const double S1 = pc.ps1[i0 + 1] - pc.ps1[i0];
-                mbv = (S1 - a * Cn) * recip(b - a);
-                mbv = fmin(fmax(mbv, 0.0), Cn);
-            }
-            pc.mb[i0] = mbv;
-            pc.ma[i0] = Cn - mbv;
-        }
+    const double ma_next = dpp_f64<kDppRowShl1>(0.0, ma);
+    {
+        const double mr = (d & (1u << 22)) ? mb : mb + ma_next;
+        pc.dterm[tid] = dterm;
+        pc.hterm[tid] = point_entropy(mr, sh.lg_c, sh.lg_inv);
+        pc.mr[tid] = mr;
+        pc.ma[tid] = ma;
+        pc.bv[tid] = bq;
     }
-    __syncthreads();
-    // point terms, then one 16-lane row per candidate: D = sum q^2 M - sum x^2
-    // and H = sum over distinct values of -pi log2 pi
+    const bool dup = __syncthreads_or(zero_width);
+
+    // ---- one lane per candidate: D = sum of terms - sum x^2 (threads
+    //      0..28), H = sum of point entropies (threads 64..92)
+    if (tid < kMaxCand) {
+        const uint32_t rd = tb.red[tid];
+        const uint32_t first = rd & 0xffu, n = rd >> 8;
+        double sum = 0.0;
 #pragma unroll
-    for (int round = 0; round < 2; ++round) {
-        const int sl = tid + round * kT;
-        const int c = sl >> 4, j = sl & 15;
-        double qm = 0.0, hb = 0.0;
-        if (sl < kSlots && sh.src[sl] != kSrcNone) {
-            const int i0 = c * kPS + j;
-            const bool has_right = j < 15 && sh.src[sl + 1] != kSrcNone;
-            double M = 0.0;
-            if (j > 0) M += pc.mb[i0 - 1];
-            if (has_right) M += pc.ma[i0];
-            const double q = pc.pval[i0];
-            qm = q * q * M;
-            if (j == 0 || pc.pval[i0 - 1] != pc.pval[i0]) {
-                double Mv = M;
-                for (int jj = j + 1; jj < 16 && sh.src[c * kMaxS + jj] != kSrcNone &&
-                                     pc.pval[c * kPS + jj] == pc.pval[i0];
-                     ++jj) {
-                    Mv += pc.mb[c * kPS + jj - 1];
-                    if (jj < 15 && sh.src[c * kMaxS + jj + 1] != kSrcNone) Mv += pc.ma[c * kPS + jj];
+        for (uint32_t i = 0; i < 15; ++i)
+            if (i < n) sum += pc.dterm[first + i];
+        Dout[tid * R + r] = mx > mn ? fmax(sum - sumsq, 0.0) : 0.0;
+    } else if (tid >= 64 && tid < 64 + kMaxCand) {
+        const int c = tid - 64;
+        const uint32_t rd = tb.red[c];
+        const uint32_t first = rd & 0xffu, n = rd >> 8;
+        double h = 0.0;
+        if (!dup) {  // every point distinct: one term per right point
+#pragma unroll
+            for (uint32_t i = 0; i < 15; ++i)
+                if (i < n) h += pc.hterm[first + i];
+            h += point_entropy(pc.ma[first], sh.lg_c, sh.lg_inv);
+        } else {     // merge the masses of equal consecutive points
+            double acc = pc.ma[first];
+            float val = mn;
+            for (uint32_t i = 0; i < n; ++i) {
+                const float b = pc.bv[first + i];
+                const double m = pc.mr[first + i];
+                if (b == val) {
+                    acc += m;
+                } else {
+                    h += point_entropy(acc, sh.lg_c, sh.lg_inv);
+                    acc = m;
+                    val = b;
                 }
-                const double pi = Mv * (1.0 / 4096.0);
-                if (pi > 0.0) hb = -pi * log2_unit(pi, sh.lg_c, sh.lg_inv);
             }
+            h += point_entropy(acc, sh.lg_c, sh.lg_inv);
         }
-        qm = row_sum_f64(qm);
-        hb = row_sum_f64(hb);
-        if (j == 15 && c < kMaxCand) {
-            double Dc = 0.0, Hc = 0.0;
-            if (mx > mn) {
-                Dc = qm - sumsq;
-                Hc = hb;
-            }
-            Dout[c * R + r] = fmax(Dc, 0.0);
-            Hout[c * R + r] = fmax(Hc, 0.0);
-        }
+        Hout[c * R + r] = mx > mn ? fmax(h, 0.0) : 0.0;
     }
 }
 
@@ -551,18 +567,46 @@ hipError_t launch_eval16(const void* x0, const void* x1, int64_t nb0, int64_t R,
             ucol[k][j] = (uint8_t)found;
         }
     if (nu != kNU || rt.n_stats != kNQ) return hipErrorInvalidValue;
-    // point sources: candidate 0 is {min, max}; then U_k, E_k for k = 3..16
-    for (int c = 0; c < kMaxCand; ++c) {
+    // Candidates: 0 = {min, max}; 1 + 2(k-3) = U_k, 2 + 2(k-3) = E_k.
+    // Point j of a k-point candidate in the point table.
+    auto point = [&](int c, int j) -> int {
         const int k = c == 0 ? 2 : 3 + (c - 1) / 2;
-        const bool uni = c > 0 && ((c - 1) & 1) == 0;
-        for (int j = 0; j < kMaxS; ++j) {
-            uint16_t v = kSrcNone;
-            if (j == 0) v = kSrcMin;
-            else if (j == k - 1) v = kSrcMax;
-            else if (j < k) v = uni ? (uint16_t)(kSrcUni + ucol[k][j]) : (uint16_t)(kSrcQnt + rt.col[k][j]);
-            tb.src[c * kMaxS + j] = v;
+        if (j == 0) return 0;
+        if (j == k - 1) return 1;
+        const bool uni = ((c - 1) & 1) == 0;
+        return uni ? kPU + ucol[k][j] : kPQ + rt.col[k][j];
+    };
+    auto cand = [](int k, bool uni) { return k == 2 ? 0 : (uni ? 1 : 2) + 2 * (k - 3); };
+    // Rows of 16 lanes, each holding the intervals (k - 1 per candidate) of
+    // whole candidates: {U16, {min,max}}, {E16}, {U/E k, U/E 18 - k} for
+    // k = 15..10, {U9, E9}.
+    int rows[kRows][2];
+    int nr = 0;
+    rows[nr][0] = cand(16, true);  rows[nr][1] = cand(2, true); ++nr;
+    rows[nr][0] = cand(16, false); rows[nr][1] = -1; ++nr;
+    for (int k = 15; k >= 10; --k) {
+        rows[nr][0] = cand(k, true);  rows[nr][1] = cand(18 - k, true); ++nr;
+        rows[nr][0] = cand(k, false); rows[nr][1] = cand(18 - k, false); ++nr;
+    }
+    rows[nr][0] = cand(9, true); rows[nr][1] = cand(9, false); ++nr;
+    if (nr != kRows) return hipErrorInvalidValue;
+    for (int l = 0; l < kT; ++l) tb.desc[l] = kNoLane;
+    int placed = 0;
+    for (int row = 0; row < kRows; ++row) {
+        int lane = 16 * row;
+        for (int h = 0; h < 2; ++h) {
+            const int c = rows[row][h];
+            if (c < 0) continue;
+            const int k = c == 0 ? 2 : 3 + (c - 1) / 2;
+            if (lane + (k - 1) > 16 * (row + 1)) return hipErrorInvalidValue;
+            tb.red[c] = (uint16_t)(lane | ((k - 1) << 8));
+            for (int j = 0; j < k - 1; ++j, ++lane)
+                tb.desc[lane] = (uint32_t)point(c, j) | ((uint32_t)point(c, j + 1) << 8) |
+                                (j == 0 ? 1u << 21 : 0u) | (j == k - 2 ? 1u << 22 : 0u);
+            ++placed;
         }
     }
+    if (placed != kMaxCand) return hipErrorInvalidValue;
     for (int i = 0; i < 32; ++i) {
         const double c = 1.0 + (double)(2 * i + 1) / 64.0;
         tb.lg_c[i] = log2(c);
