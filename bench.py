@@ -71,6 +71,65 @@ def load_traffic(kernel, sha):
     return k.get("bytes_per_launch")
 
 
+def copy_bandwidth(torch, nbytes=1 << 30, reps=5):
+    """Device-to-device copy rate on this GPU (read + write bytes per second),
+    the practical ceiling the HBM-bound kernels are compared with."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    times = []
+    for _ in range(reps):
+        ev[0].record()
+        dst.copy_(src)
+        ev[1].record()
+        torch.cuda.synchronize()
+        times.append(ev[0].elapsed_time(ev[1]))
+    del src, dst
+    return 2.0 * nbytes / (float(np.median(times)) * 1e-3) / 1e9
+
+
+def decode_latency(torch, kvq, W, steps=1000, warmup=20):
+    """Small-launch regime: 512 blocks of one decode step (batch 64 x 8 KV
+    heads x 32 new tokens x 128, fp16 Student-t).  The previous batch is
+    admitted by bisection to give lambda_prev; each measured step admits the
+    next batch with one projected subgradient step from the running lambda.
+    Per-call times are HIP events; the step time is wall clock around
+    eval -> solve (synchronising) -> quantize_pack -> synchronize."""
+    w = W.DECODE_ADMIT_FP16
+    prev = [torch.from_numpy(h).cuda() for h in W.generate(w, which=0)]
+    cur = [torch.from_numpy(h).cuda() for h in W.generate(w, which=1)]
+    plan = kvq.kvq_plan_blocks(cur, w.tokens_per_block, w.dims_per_block, w.s)
+    buf = kvq.allocate(plan)
+    st = torch.cuda.current_stream()
+    lam, _ = kvq.admit(plan, prev, buf, w.B, kvq.KVQ_BISECT, w.iters, w.eta, 0.0,
+                       w.extra["prev_seed"], st)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    step_us, per = [], {"eval": [], "solve": [], "quantize_pack": []}
+    for i in range(warmup + steps):
+        t0 = time.perf_counter()
+        ev[0].record(st)
+        kvq.kvq_eval_candidates(plan, cur, buf["D"], buf["H"], buf["stats"], buf["workspace"], st)
+        ev[1].record(st)
+        lam, rate = kvq.kvq_solve_lambda(plan, buf["D"], buf["H"], buf["stats"], w.B, kvq.KVQ_SUBGRAD,
+                                         w.iters, w.eta, lam, buf["choice"], buf["codebook"],
+                                         buf["m"], buf["off"], buf["workspace"], st)
+        ev[2].record(st)
+        kvq.kvq_quantize_pack(plan, cur, buf["codebook"], buf["m"], buf["off"], w.seed,
+                              buf["codes"], stream=st)
+        ev[3].record(st)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        if i >= warmup:
+            step_us.append((t1 - t0) * 1e6)
+            for j, k in enumerate(per):
+                per[k].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)
+    q = lambda v: {"p50": float(np.percentile(v, 50)), "p90": float(np.percentile(v, 90))}
+    return {"workload": w.name, "steps": steps, "step_us": q(step_us),
+            "calls_us": {k: q(v) for k, v in per.items()}, "lambda_final": lam}
+
+
 def cpu_baseline(w, tensors, target_s=10.0):
     """The oracle, as it stands, on the first blocks of the workload: eval,
     bisection, quantize+pack and decode, on all host cores."""
@@ -113,6 +172,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="long_context_kv_fp16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the copy-bandwidth and decode-latency measurements")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a device-to-device copy of BYTES (reference for HBM "
                          "byte counters) and exit")
@@ -194,6 +255,11 @@ def main():
     traffic = load_traffic(dom, sha)
     value = w.input_bytes / (ms_per_step * 1e-3) / 1e9
     admit_ms = per["eval"] + per["quantize_pack"]
+    extras = {}
+    if not a.no_extras:
+        log("measuring copy bandwidth and decode-step latency")
+        extras["copy_GBps"] = copy_bandwidth(torch)
+        extras["decode_admission_latency"] = decode_latency(torch, kvq, W)
     rec = {
         "metric": "KV GB/s quantized (fp16 in) and % of HBM roofline at 32-token blocks",
         "value": value, "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
@@ -211,12 +277,19 @@ def main():
         "kernels_ms": per,
         "eval_plus_quantize": {"ms": admit_ms,
                                "kv_GBps": w.input_bytes / (admit_ms * 1e-3) / 1e9,
+                               "elements_per_s": w.n_entries / (admit_ms * 1e-3),
                                "frac_of_hbm": (alg["eval"] + alg["quantize_pack"]) /
                                               (admit_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "lambda": lam, "rate_bits_per_entry": rate,
         "packed_bits_per_entry": 32.0 * words_total / w.n_entries,
         "source_sha": sha,
     }
+    if extras:
+        rec["copy_GBps"] = extras["copy_GBps"]
+        rec["eval_plus_quantize"]["frac_of_copy"] = (alg["eval"] + alg["quantize_pack"]) / \
+            (admit_ms * 1e-3) / 1e9 / extras["copy_GBps"]
+        rec["roofline"]["frac_of_copy"] = achieved / extras["copy_GBps"]
+        rec["decode_admission_latency"] = extras["decode_admission_latency"]
     if not a.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(w, host)

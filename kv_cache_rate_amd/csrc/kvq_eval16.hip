@@ -42,7 +42,9 @@ namespace kvq {
 namespace {
 
 constexpr int kT = 256;            // threads per block
+constexpr int kW = kT / 64;        // waves per block
 constexpr int kPer = 16;           // entries per thread
+constexpr int kCL = 256;           // candidate-interval lanes
 constexpr int kNC = 1024;          // coarse bins
 constexpr int kMaxSlots = 144;     // every target and threshold bin fits
 constexpr int kFW = 32;            // per-key count words of a slot (64 x 16 bit)
@@ -56,7 +58,7 @@ constexpr int kRows = 15;          // 16-lane rows of candidate intervals
 constexpr uint32_t kNoSlot = 0xffffffffu, kClaim = 0xfffffffeu;
 constexpr uint32_t kCnt1 = 1u << 19;       // one entry in a packed (count, sum f) word
 constexpr uint32_t kLowF = kCnt1 - 1u;     // sum-of-f field
-constexpr uint32_t kNoLane = 0xffffffffu;  // lane without an interval
+constexpr uint32_t kNoLane = 0xffffu;      // lane without an interval
 constexpr int kDppRowShl1 = 0x101;         // row_shl:1, lane l reads lane l + 1
 
 struct Point {                     // a codepoint and the entries below it
@@ -73,11 +75,11 @@ struct PhaseB {                    // sweep 2 .. prefix finish
     uint32_t w[kMaxSlots * kSW];
 };
 struct PhaseC {                    // candidate intervals
-    double dterm[kT];
-    double hterm[kT];
-    double mr[kT];                 // mass at the interval's right point
-    double ma[kT];                 // mass the interval sends to its left point
-    float bv[kT];                  // right point
+    double dterm[kCL];
+    double hterm[kCL];
+    double mr[kCL];                // mass at the interval's right point
+    double ma[kCL];                // mass the interval sends to its left point
+    float bv[kCL];                 // right point
 };
 
 struct Shared {
@@ -91,10 +93,10 @@ struct Shared {
     uint16_t tbin[kNQ];
     uint16_t tloc[kNQ];
     uint16_t ukey[kNU];
-    double lg_c[32];
-    double lg_inv[32];
-    uint32_t wmin[kT / 64], wmax[kT / 64], wtot[kT / 64];
-    double wsq[kT / 64], wts1[kT / 64];
+    double lg_c[64];
+    double lg_inv[64];
+    uint32_t wmin[kW], wmax[kW], wtot[kW];
+    double wsq[kW], wts1[kW];
     uint32_t nslots;
 };
 
@@ -128,25 +130,33 @@ __device__ __forceinline__ double recip(double x) {
     return fma(r, e, r);
 }
 
-// log2 of x in (0, 1], relative error ~1e-15: x = m 2^e with m in [1, 2);
-// c = 1 + (2i + 1)/64 is the centre of the 1/32-wide cell of m, so
-// log2 m = log2 c + log1p(t)/ln 2 with t = (m - c)/c, |t| < 1/64, and a
-// degree-8 series for log1p.
+// a * b + c in fp64 with c a compile-time constant kept in a scalar register
+// (v_fma_f64 takes one scalar operand; otherwise the constant would be
+// copied into vector registers for every use).
+__device__ __forceinline__ double fma_sc(double a, double b, double c) {
+    double r;
+    asm("v_fma_f64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(c));
+    return r;
+}
+
+// log2 of x in (0, 1], relative error ~1e-16: x = m 2^e with m in [1, 2);
+// c = 1 + (2i + 1)/128 is the centre of the 1/64-wide cell i of m, so
+// log2 m = log2 c + log1p(t)/ln 2 with t = (m - c)/c, |t| < 2^-7, and the
+// log1p series to t^7 (truncation below 2^-56/8).
 __device__ __forceinline__ double log2_unit(double x, const double* lg_c, const double* lg_inv) {
-    int e;
-    double m = frexp(x, &e);  // [0.5, 1)
-    m *= 2.0;
-    e -= 1;
-    const int i = (int)((__double_as_longlong(m) >> 47) & 31);
-    const double c = 1.0 + (double)(2 * i + 1) * (1.0 / 64.0);
+    const double m = 2.0 * __builtin_amdgcn_frexp_mant(x);  // [1, 2)
+    const int e = __builtin_amdgcn_frexp_exp(x) - 1;
+    const uint32_t mhi = (uint32_t)((uint64_t)__double_as_longlong(m) >> 32);
+    const int i = (int)((mhi >> 14) & 63u);
+    // c: m's exponent and top 6 mantissa bits, then the half-cell bit
+    const double c = __longlong_as_double((long long)((uint64_t)((mhi & 0xffffc000u) | 0x2000u) << 32));
     const double t = (m - c) * lg_inv[i];
-    double p = -1.0 / 8.0;
-    p = fma(p, t, 1.0 / 7.0);
-    p = fma(p, t, -1.0 / 6.0);
-    p = fma(p, t, 1.0 / 5.0);
-    p = fma(p, t, -1.0 / 4.0);
-    p = fma(p, t, 1.0 / 3.0);
-    p = fma(p, t, -1.0 / 2.0);
+    double p = 1.0 / 7.0;
+    p = fma_sc(p, t, -1.0 / 6.0);
+    p = fma_sc(p, t, 1.0 / 5.0);
+    p = fma_sc(p, t, -1.0 / 4.0);
+    p = fma_sc(p, t, 1.0 / 3.0);
+    p = fma(p, t, -0.5);
     p = fma(p, t, 1.0);
     const double l1p = p * t;
     return ((double)e + lg_c[i]) + l1p * 1.4426950408889634;  // 1/ln 2
@@ -154,7 +164,7 @@ __device__ __forceinline__ double log2_unit(double x, const double* lg_c, const 
 
 // -pi log2 pi of a point holding mass m of the 4096 entries.
 __device__ __forceinline__ double point_entropy(double m, const double* lg_c, const double* lg_inv) {
-    const double pi = m * (1.0 / 4096.0);
+    const double pi = __builtin_amdgcn_ldexp(m, -12);
     return pi > 0.0 ? -pi * log2_unit(pi, lg_c, lg_inv) : 0.0;
 }
 
@@ -198,10 +208,10 @@ struct Eval16Tables {
     uint8_t unum[kNU];              // numerator of distinct fraction u
     uint8_t uden[kNU];              // denominator
     uint16_t red[kMaxCand];         // candidate c: first lane | interval count << 8
-    uint32_t desc[kT];              // lane: left point | right point << 8 |
-                                    //   first << 21 | last << 22, or kNoLane
-    double lg_c[32];                // log2(1 + (2i+1)/64)
-    double lg_inv[32];              // 1 / (1 + (2i+1)/64)
+    uint16_t desc[kCL];             // lane: left point | right point << 8, or kNoLane
+                                    //   (a candidate's last interval ends at point 1)
+    double lg_c[64];                // log2(1 + (2i+1)/128)
+    double lg_inv[64];              // 1 / (1 + (2i+1)/128)
 };
 
 __global__ void __launch_bounds__(kT, 5)
@@ -217,7 +227,7 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     const __half* src = r < nb0 ? x0 + r * 4096 : x1 + (r - nb0) * 4096;
 
     // ---- load: thread owns entries [8 tid, 8 tid + 8) and [2048 + 8 tid, ...)
-    uint32_t hw[8];
+    uint32_t hw[kPer / 2];
     {
         const uint4 a = reinterpret_cast<const uint4*>(src)[tid];
         const uint4 b = reinterpret_cast<const uint4*>(src)[256 + tid];
@@ -225,11 +235,12 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         hw[4] = b.x; hw[5] = b.y; hw[6] = b.z; hw[7] = b.w;
     }
     reinterpret_cast<uint4*>(sh.u.a.cnt)[tid] = make_uint4(0u, 0u, 0u, 0u);
-    if (tid < 32) {
+    if (tid < 64) {
         sh.lg_c[tid] = tb.lg_c[tid];
         sh.lg_inv[tid] = tb.lg_inv[tid];
     }
     if (tid == 0) sh.nslots = 0u;
+    const uint32_t d = tid < kCL ? tb.desc[tid] : kNoLane;  // this lane's candidate interval
     __syncthreads();
 
     // ---- sweep 1 (two entries per 32-bit word): canonical -0, keys,
@@ -260,7 +271,7 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     {
         const uint32_t kmin = wave_min_u32_dpp(min((uint32_t)kmin2.x, (uint32_t)kmin2.y));
         const uint32_t kmax = wave_max_u32_dpp(max((uint32_t)kmax2.x, (uint32_t)kmax2.y));
-        const double sqw = wave_last_f64(wave_scan_add_f64(sq));
+        const double sqw = wave_sum_f64(sq);
         if (lane == 0) {
             sh.wmin[wave] = kmin;
             sh.wmax[wave] = kmax;
@@ -268,8 +279,12 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         }
     }
     __syncthreads();
-    const uint32_t kmin = min(min(sh.wmin[0], sh.wmin[1]), min(sh.wmin[2], sh.wmin[3]));
-    const uint32_t kmax = max(max(sh.wmax[0], sh.wmax[1]), max(sh.wmax[2], sh.wmax[3]));
+    uint32_t kmin = sh.wmin[0], kmax = sh.wmax[0];
+#pragma unroll
+    for (int w = 1; w < kW; ++w) {
+        kmin = min(kmin, sh.wmin[w]);
+        kmax = max(kmax, sh.wmax[w]);
+    }
     const double sumsq = (sh.wsq[0] + sh.wsq[1]) + (sh.wsq[2] + sh.wsq[3]);
     const float mn = key_value(kmin);
     const float mx = key_value(kmax);
@@ -296,10 +311,13 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         }
         __syncthreads();
         const int wv = __builtin_amdgcn_readfirstlane(wave);
-        const uint32_t oc = (wv > 0 ? sh.wtot[0] : 0u) + (wv > 1 ? sh.wtot[1] : 0u) +
-                            (wv > 2 ? sh.wtot[2] : 0u);
-        const double os = ((wv > 0 ? sh.wts1[0] : 0.0) + (wv > 1 ? sh.wts1[1] : 0.0)) +
-                          (wv > 2 ? sh.wts1[2] : 0.0);
+        uint32_t oc = 0;
+        double os = 0.0;
+#pragma unroll
+        for (int w = 0; w < kW - 1; ++w) {
+            oc += w < wv ? sh.wtot[w] : 0u;
+            os += w < wv ? sh.wts1[w] : 0.0;
+        }
         const uint32_t base_c = oc + ic - ct;
         const double base_s = os + (is - st);
         uint32_t runc = 0, runa = 0;
@@ -327,10 +345,15 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     //      128..198: find the bin, read its prefix, claim a slot
     if (tid < kNQ) {
         const uint32_t rank = (uint32_t)tb.rt.rank[tid];
-        uint32_t lo = 0;  // last bin with prefix count <= rank
+        // last bin with prefix count <= rank: 4-way search, the three
+        // probes of a step are independent reads
+        uint32_t lo = 0;
 #pragma unroll
-        for (uint32_t half = kNC / 2; half; half >>= 1)
-            if (sh.u.a.cnt[lo + half] <= rank) lo += half;
+        for (uint32_t step = kNC / 4; step; step >>= 2) {
+            const uint32_t c1 = sh.u.a.cnt[lo + step], c2 = sh.u.a.cnt[lo + 2 * step],
+                           c3 = sh.u.a.cnt[lo + 3 * step];
+            lo += step * ((c1 <= rank ? 1u : 0u) + (c2 <= rank ? 1u : 0u) + (c3 <= rank ? 1u : 0u));
+        }
         const uint32_t pc = sh.u.a.cnt[lo];
         sh.tbin[tid] = (uint16_t)lo;
         sh.tloc[tid] = (uint16_t)(rank - pc);
@@ -462,7 +485,7 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     //      distortion term a^2 M_a + b^2 M_b and the entropy term of the
     //      right point (its mass: this interval's share plus the next one's)
     PhaseC& pc = sh.u.c;
-    const uint32_t d = tb.desc[tid];
+    const bool last = ((d >> 8) & 0xffu) == 1u;  // right point is the maximum
     double ma = 0.0, mb = 0.0, dterm = 0.0;
     float bq = 0.0f;
     bool zero_width = false;
@@ -485,8 +508,8 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         bq = pb.v;
     }
     const double ma_next = dpp_f64<kDppRowShl1>(0.0, ma);
-    {
-        const double mr = (d & (1u << 22)) ? mb : mb + ma_next;
+    if (tid < kCL) {
+        const double mr = last ? mb : mb + ma_next;
         pc.dterm[tid] = dterm;
         pc.hterm[tid] = point_entropy(mr, sh.lg_c, sh.lg_inv);
         pc.mr[tid] = mr;
@@ -503,7 +526,7 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         double sum = 0.0;
 #pragma unroll
         for (uint32_t i = 0; i < 15; ++i)
-            if (i < n) sum += pc.dterm[first + i];
+            sum += i < n ? pc.dterm[first + i] : 0.0;  // first + 14 < kCL
         Dout[tid * R + r] = mx > mn ? fmax(sum - sumsq, 0.0) : 0.0;
     } else if (tid >= 64 && tid < 64 + kMaxCand) {
         const int c = tid - 64;
@@ -513,7 +536,7 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         if (!dup) {  // every point distinct: one term per right point
 #pragma unroll
             for (uint32_t i = 0; i < 15; ++i)
-                if (i < n) h += pc.hterm[first + i];
+                h += i < n ? pc.hterm[first + i] : 0.0;
             h += point_entropy(pc.ma[first], sh.lg_c, sh.lg_inv);
         } else {     // merge the masses of equal consecutive points
             double acc = pc.ma[first];
@@ -590,7 +613,7 @@ hipError_t launch_eval16(const void* x0, const void* x1, int64_t nb0, int64_t R,
     }
     rows[nr][0] = cand(9, true); rows[nr][1] = cand(9, false); ++nr;
     if (nr != kRows) return hipErrorInvalidValue;
-    for (int l = 0; l < kT; ++l) tb.desc[l] = kNoLane;
+    for (int l = 0; l < kCL; ++l) tb.desc[l] = (uint16_t)kNoLane;
     int placed = 0;
     for (int row = 0; row < kRows; ++row) {
         int lane = 16 * row;
@@ -601,14 +624,13 @@ hipError_t launch_eval16(const void* x0, const void* x1, int64_t nb0, int64_t R,
             if (lane + (k - 1) > 16 * (row + 1)) return hipErrorInvalidValue;
             tb.red[c] = (uint16_t)(lane | ((k - 1) << 8));
             for (int j = 0; j < k - 1; ++j, ++lane)
-                tb.desc[lane] = (uint32_t)point(c, j) | ((uint32_t)point(c, j + 1) << 8) |
-                                (j == 0 ? 1u << 21 : 0u) | (j == k - 2 ? 1u << 22 : 0u);
+                tb.desc[lane] = (uint16_t)(point(c, j) | (point(c, j + 1) << 8));
             ++placed;
         }
     }
     if (placed != kMaxCand) return hipErrorInvalidValue;
-    for (int i = 0; i < 32; ++i) {
-        const double c = 1.0 + (double)(2 * i + 1) / 64.0;
+    for (int i = 0; i < 64; ++i) {
+        const double c = 1.0 + (double)(2 * i + 1) / 128.0;
         tb.lg_c[i] = log2(c);
         tb.lg_inv[i] = 1.0 / c;
     }

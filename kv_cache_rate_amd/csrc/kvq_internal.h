@@ -160,6 +160,26 @@ __device__ __forceinline__ uint64_t dpp_u64(uint64_t old, uint64_t v) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// row_shr with bound_ctrl: lanes whose source falls outside the row read 0
+// (no `old` operand, so no register has to be cleared first).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_zero_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_zero_f64(double v) {
+    const uint64_t x = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = dpp_zero_u32<CTRL>((uint32_t)x);
+    const uint32_t hi = dpp_zero_u32<CTRL>((uint32_t)(x >> 32));
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_zero_u64(uint64_t x) {
+    const uint32_t lo = dpp_zero_u32<CTRL>((uint32_t)x);
+    const uint32_t hi = dpp_zero_u32<CTRL>((uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ uint32_t wave_scan_add_u32(uint32_t v) {
     v += dpp_u32<kDppRowShr1>(0u, v);
@@ -171,19 +191,19 @@ __device__ __forceinline__ uint32_t wave_scan_add_u32(uint32_t v) {
     return v;
 }
 __device__ __forceinline__ double wave_scan_add_f64(double v) {
-    v += dpp_f64<kDppRowShr1>(0.0, v);
-    v += dpp_f64<kDppRowShr2>(0.0, v);
-    v += dpp_f64<kDppRowShr4>(0.0, v);
-    v += dpp_f64<kDppRowShr8>(0.0, v);
+    v += dpp_zero_f64<kDppRowShr1>(v);
+    v += dpp_zero_f64<kDppRowShr2>(v);
+    v += dpp_zero_f64<kDppRowShr4>(v);
+    v += dpp_zero_f64<kDppRowShr8>(v);
     v += dpp_f64<kDppBcast15, 0xA>(0.0, v);
     v += dpp_f64<kDppBcast31, 0xC>(0.0, v);
     return v;
 }
 __device__ __forceinline__ uint64_t wave_scan_add_u64(uint64_t v) {
-    v += dpp_u64<kDppRowShr1>(0ull, v);
-    v += dpp_u64<kDppRowShr2>(0ull, v);
-    v += dpp_u64<kDppRowShr4>(0ull, v);
-    v += dpp_u64<kDppRowShr8>(0ull, v);
+    v += dpp_zero_u64<kDppRowShr1>(v);
+    v += dpp_zero_u64<kDppRowShr2>(v);
+    v += dpp_zero_u64<kDppRowShr4>(v);
+    v += dpp_zero_u64<kDppRowShr8>(v);
     v += dpp_u64<kDppBcast15, 0xA>(0ull, v);
     v += dpp_u64<kDppBcast31, 0xC>(0ull, v);
     return v;
@@ -219,11 +239,25 @@ __device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
 }
 // Sum over each 16-lane row; the row total lands in the row's lane 15.
 __device__ __forceinline__ double row_sum_f64(double v) {
-    v += dpp_f64<kDppRowShr1>(0.0, v);
-    v += dpp_f64<kDppRowShr2>(0.0, v);
-    v += dpp_f64<kDppRowShr4>(0.0, v);
-    v += dpp_f64<kDppRowShr8>(0.0, v);
+    v += dpp_zero_f64<kDppRowShr1>(v);
+    v += dpp_zero_f64<kDppRowShr2>(v);
+    v += dpp_zero_f64<kDppRowShr4>(v);
+    v += dpp_zero_f64<kDppRowShr8>(v);
     return v;
+}
+// Wave-wide sum, wave-uniform result: row sums, then the four row totals
+// added in row order.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v = row_sum_f64(v);
+    const uint64_t x = (uint64_t)__double_as_longlong(v);
+    double t[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 16 * k + 15);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 16 * k + 15);
+        t[k] = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+    }
+    return (t[0] + t[1]) + (t[2] + t[3]);
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
