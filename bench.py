@@ -35,10 +35,20 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_sources_sha():
+# Source files each timed call's kernels are built from (the recorded HBM
+# traffic of a kernel is used only while these files are unchanged).
+KERNEL_SOURCES = {
+    "eval": ("kvq_eval16.hip", "kvq_internal.h"),
+    "solve": ("kvq_solve.hip", "kvq_internal.h"),
+    "quantize_pack": ("kvq_quant.hip", "kvq_internal.h"),
+    "dequantize": ("kvq_quant.hip", "kvq_internal.h"),
+}
+
+
+def kernel_sources_sha(files=None):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "kv_cache_rate_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(files or os.listdir(csrc)):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -252,7 +262,7 @@ def main():
     dom = max(per, key=per.get)
     achieved = alg[dom] / (per[dom] * 1e-3) / 1e9
     sha = kernel_sources_sha()
-    traffic = load_traffic(dom, sha)
+    traffic = load_traffic(dom, kernel_sources_sha(KERNEL_SOURCES[dom]))
     value = w.input_bytes / (ms_per_step * 1e-3) / 1e9
     admit_ms = per["eval"] + per["quantize_pack"]
     extras = {}
@@ -283,6 +293,7 @@ def main():
         "lambda": lam, "rate_bits_per_entry": rate,
         "packed_bits_per_entry": 32.0 * words_total / w.n_entries,
         "source_sha": sha,
+        "kernel_source_sha": {k: kernel_sources_sha(v) for k, v in KERNEL_SOURCES.items()},
     }
     if extras:
         rec["copy_GBps"] = extras["copy_GBps"]

@@ -30,7 +30,7 @@
  *   - Arguments are validated on the host before any launch; a failed check
  *     returns KVQ_EINVAL or KVQ_ENOSPC and launches nothing.  Calls are
  *     asynchronous on the given stream (KVQ_OK means "enqueued"), except
- *     kvq_solve_lambda, which synchronises the stream once to return lambda,
+ *     kvq_solve_lambda, which synchronises the stream to return lambda,
  *     the rate and the device status word (non-finite input found by
  *     kvq_eval_candidates is reported there as KVQ_ENONFINITE).
  *   - kvq_last_error() returns a thread-local text for the last failure.
@@ -178,7 +178,9 @@ kvq_status kvq_eval_candidates(const kvq_plan* p, const kvq_tensor* t, int32_t n
    the chosen distinct-alphabet points), codebook[R][s] (fp32, unused slots
    0), m[R] (levels), word_off[R+1] (exclusive scan of ceil(d_r w_r / 32),
    w_r = ceil(log2 m_r)); *rate_bits_per_entry_out (host) is the modelled
-   rate sum_r d_r H_r / sum_r d_r of the choice.  Synchronises stream s once.
+   rate sum_r d_r H_r / sum_r d_r of the choice.  Synchronises stream s at
+   the end; KVQ_BISECT also waits once after the lambda = 0 probe, which
+   decides whether the bracket passes are launched.
    Errors: KVQ_ENONFINITE (from eval), KVQ_EINFEASIBLE, KVQ_EINVAL. */
 kvq_status kvq_solve_lambda(const kvq_plan* p, const double* D, const double* H,
                             const float* stats, double B_bits_per_entry, int32_t mode,

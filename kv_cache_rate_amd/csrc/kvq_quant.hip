@@ -170,14 +170,16 @@ quantize4096_kernel(const void* __restrict__ x0, const void* __restrict__ x1, in
                     int s, const float* __restrict__ codebook, const uint8_t* __restrict__ m_in,
                     const uint64_t* __restrict__ off, uint32_t k0, uint32_t k1,
                     uint32_t* __restrict__ codes) {
-    __shared__ float q[kMaxS];
-    __shared__ float inv[kMaxS];  // 2^24 / (q[i+1] - q[i])
+    __shared__ float q[kMaxS + 1];
+    __shared__ float inv[kMaxS];  // 2^24 / (q[i+1] - q[i]); 0 at the last point
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x;
     const int m = min(max((int)m_in[r], 1), s);
-    if (tid < kMaxS) q[tid] = tid < m ? codebook[r * s + tid] : __builtin_huge_valf();
+    if (tid <= kMaxS) q[tid] = tid < m ? codebook[r * s + tid] : __builtin_huge_valf();
     __syncthreads();
-    if (tid + 1 < m) inv[tid] = 0x1p24f / (q[tid + 1] - q[tid]);
+    // slot m-1 (the maximum) faces +inf: its inverse width is 0, so an entry
+    // equal to the maximum keeps code m-1 and needs no clamp below
+    if (tid < m) inv[tid] = 0x1p24f / (q[tid + 1] - q[tid]);
     __syncthreads();
     const int w = code_width(m);
     if (w == 0) return;
@@ -211,11 +213,13 @@ quantize4096_kernel(const void* __restrict__ x0, const void* __restrict__ x1, in
             o = (*reinterpret_cast<const float*>(qb + o + 16) <= xv) ? o + 16 : o;
             o = (*reinterpret_cast<const float*>(qb + o + 8) <= xv) ? o + 8 : o;
             o = (*reinterpret_cast<const float*>(qb + o + 4) <= xv) ? o + 4 : o;
-            const int i = min((int)(o >> 2), m - 2);
+            // o = 4 i: q[i] <= x < q[i+1] (i = m-1 only for x equal to the maximum)
+            const float qi = *reinterpret_cast<const float*>(qb + o);
+            const float iv = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(inv) + o);
             // p 2^24 against the 24-bit draw (word >> 8): u < p without scaling u;
             // p outside [0, 1] by round-off decides the same way as its clamp
-            const float p24 = (xv - q[i]) * inv[i];
-            const uint32_t code = (uint32_t)i + ((float)(wd[e] >> 8) < p24 ? 1u : 0u);
+            const float p24 = (xv - qi) * iv;
+            const uint32_t code = (o >> 2) + ((float)(wd[e] >> 8) < p24 ? 1u : 0u);
             bits |= code << (w * e);
         }
         store_bytes(out + w * ch, bits, w);

@@ -29,7 +29,9 @@ constexpr int kSolveThreads = 256;
 constexpr int kScanPer = 4;
 constexpr int kScanTile = kSolveThreads * kScanPer;
 
-enum Phase : int32_t { kPhaseDouble = 0, kPhaseDouble2 = 1, kPhaseMulti = 2, kPhaseSubgrad = 10 };
+enum Phase : int32_t {
+    kPhaseDouble = 0, kPhaseDouble2 = 1, kPhaseMulti = 2, kPhaseZero = 3, kPhaseSubgrad = 10
+};
 
 // Objective D + (lambda * d) * H, evaluated without contraction.
 __device__ __forceinline__ double objective(double Dv, double Hv, double lamd) {
@@ -57,15 +59,15 @@ __global__ void solve_init_kernel(WsHeader* h, int mode, double lam_in, unsigned
     h->bits_left = iters;
     h->rate_final = 0;
     for (int j = 0; j < kMaxLam + 8; ++j) h->sums[j] = 0ull;
-    if (mode == KVQ_SUBGRAD) {
+    if (mode == KVQ_SUBGRAD) {  // blocks are chosen at lam_in by the final pass
         h->phase = kPhaseSubgrad;
+        h->nlam = 0;
+        h->lam_final = lam_in;
+        h->done = 1;
+    } else {                    // first probe: lambda = 0 alone
+        h->phase = kPhaseZero;
         h->nlam = 1;
-        h->lam[0] = lam_in;
-    } else {
-        h->phase = kPhaseDouble;
-        h->nlam = kMaxLam;
         h->lam[0] = 0.0;
-        for (int j = 1; j < kMaxLam; ++j) h->lam[j] = ldexp(1.0, j - 1);
     }
 }
 
@@ -89,25 +91,26 @@ __global__ void solve_select_kernel(WsHeader* h) {
     if (threadIdx.x != 0 || h->done) return;
     const unsigned long long B = h->Btot_fx;
     switch (h->phase) {
-    case kPhaseSubgrad:
-        h->lam_final = h->lam[0];
-        h->done = 1;
-        break;
-    case kPhaseDouble: {
+    case kPhaseZero:
         if (h->sums[0] <= B) {
             h->lam_final = 0.0;
             h->done = 1;
-            break;
+        } else {  // bracket doubling: 2^0 .. 2^62 in one pass
+            h->phase = kPhaseDouble;
+            h->nlam = kMaxLam - 1;
+            for (int j = 0; j < kMaxLam - 1; ++j) h->lam[j] = ldexp(1.0, j);
         }
+        break;
+    case kPhaseDouble: {
         int first = -1;
-        for (int j = 1; j < kMaxLam; ++j)
+        for (int j = 0; j < kMaxLam - 1; ++j)
             if (h->sums[j] <= B) {
                 first = j;
                 break;
             }
-        if (first > 0) {
+        if (first >= 0) {
             h->hi = h->lam[first];
-            h->lo = first == 1 ? 0.0 : h->lam[first - 1];
+            h->lo = first == 0 ? 0.0 : h->lam[first - 1];
             setup_multisection(h);
         } else {
             h->phase = kPhaseDouble2;
@@ -517,9 +520,8 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
     const unsigned long long Btot_fx =
         Bfx >= 18446744073709551615.0 ? ~0ull : (unsigned long long)floor(Bfx);
     hipLaunchKernelGGL(solve_init_kernel, dim3(1), dim3(64), 0, st, h, mode, lam_in, Btot_fx, iters);
-    const int passes = mode == KVQ_SUBGRAD ? 1 : 2 + (iters + 5) / 6;
     const unsigned grid = (unsigned)((R + kSolveThreads - 1) / kSolveThreads);
-    for (int ps = 0; ps < passes; ++ps) {
+    auto rates_pass = [&]() {
         if (p.search == KVQ_GRIDS) {
             hipLaunchKernelGGL(rates_grids_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, R,
                                p.n_cand, (double)n, shift, h);
@@ -528,6 +530,20 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
                                p.alphabet_m, p.s, n, shift, h);
         }
         hipLaunchKernelGGL(solve_select_kernel, dim3(1), dim3(64), 0, st, h);
+    };
+    if (mode == KVQ_BISECT) {
+        // lambda = 0 first; the bracket passes run only when it is infeasible
+        rates_pass();
+        int32_t done = 0;
+        hipError_t e = hipMemcpyAsync(&done, &h->done, sizeof done, hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return e;
+        if (!done) {
+            // doubling (2^0..2^62), the 2^63 / 2^64 pass if needed, then
+            // multisection passes of up to 6 halvings each
+            const int passes = 2 + (iters + 5) / 6;
+            for (int ps = 0; ps < passes; ++ps) rates_pass();
+        }
     }
     if (p.search == KVQ_GRIDS) {
         hipLaunchKernelGGL(final_grids_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, stats, R,
