@@ -20,6 +20,7 @@ ecasq      candidate codebooks, closed-form scoring, dual solve
 exact_dp   quantile alphabet, pair statistics, brute force and pair-state DP
 philox     Philox4x32-10 counter-based generator
 codes      stochastic interpolation, fixed-width packing, decode
+ans        rANS entropy coding of each block's symbol stream
 pipeline   the whole admission pass for one configuration
 
 Parity status: every function is pinned by ``tests/test_oracle_*.py``
@@ -27,4 +28,4 @@ Parity status: every function is pinned by ``tests/test_oracle_*.py``
 implementation); none is "parity unpinned".
 """
 
-from . import blocks, ecasq, exact_dp, philox, codes, pipeline  # noqa: F401
+from . import blocks, ecasq, exact_dp, philox, codes, ans, pipeline  # noqa: F401
