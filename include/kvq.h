@@ -209,6 +209,42 @@ kvq_status kvq_dequantize(const kvq_plan* p, const uint32_t* codes, const float*
                           const uint8_t* m, const uint64_t* word_off, float* xhat,
                           hipStream_t s);
 
+/* ---- Entropy coding of the symbol stream (Implementation notes: the stored
+   symbol stream is arithmetic-coded).  Each block's codes are rANS-coded
+   (Duda, arXiv:1311.2540) with the block's own symbol counts as the model:
+   k = ceil(log2 d_r), frequencies = counts with 2^k - d_r added to the most
+   frequent symbol (lowest index among equals); 32-bit states in
+   [2^16, 2^32), 16-bit words; 8 interleaved states, state i coding entries
+   i, i + 8, ...; a block is f_0..f_{m_r - 1}, the 8 final states as (hi,
+   lo), then the words emitted at steps 0, 1, ... (state order within a
+   step), all 16-bit little-endian, zero-filled to a 32-bit boundary.  Block
+   byte offsets (exclusive scan, R + 1 entries) are the stored block lengths. */
+
+/* Buffer sizes for plan p (host only): the encoder's scratch and the
+   largest possible coded stream, in bytes. */
+kvq_status kvq_ans_sizes(const kvq_plan* p, uint64_t* scratch_bytes, uint64_t* stream_bytes);
+
+/* Code the fixed-width codes of kvq_quantize_pack (codes, m, word_off as
+   written by kvq_quantize_pack / kvq_solve_lambda).  scratch and stream are
+   device buffers (4-byte aligned) of at least the kvq_ans_sizes bytes;
+   block_off[R + 1] (device) receives the byte offset of each block in
+   stream; *total_bytes_out (host) the stream's length.  Uses workspace's
+   status word and scan area.  Synchronises stream s once.
+   Errors: KVQ_ENOSPC (buffers smaller than kvq_ans_sizes, or a block
+   outgrew its scratch region), KVQ_EINVAL. */
+kvq_status kvq_ans_encode(const kvq_plan* p, const uint32_t* codes, const uint8_t* m,
+                          const uint64_t* word_off, void* scratch, uint64_t scratch_bytes,
+                          void* stream, uint64_t stream_bytes, uint64_t* block_off,
+                          void* workspace, uint64_t* total_bytes_out, hipStream_t s);
+
+/* Decode the coded stream and write each block's codepoints, fp32
+   xhat[r][t] = codebook[r][symbol] (decode before attention).  A block
+   whose states do not end at 2^16 (a damaged stream) sets a bit in the
+   workspace status word.  Asynchronous on stream s. */
+kvq_status kvq_ans_decode(const kvq_plan* p, const void* stream, const uint64_t* block_off,
+                          const float* codebook, const uint8_t* m, float* xhat, void* workspace,
+                          hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

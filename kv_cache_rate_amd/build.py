@@ -22,7 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
 ARCH = "gfx950"
 
-SOURCES = ["kvq_host.cpp", "kvq_eval.hip", "kvq_eval16.hip", "kvq_solve.hip", "kvq_quant.hip"]
+SOURCES = ["kvq_host.cpp", "kvq_eval.hip", "kvq_eval16.hip", "kvq_solve.hip", "kvq_quant.hip",
+           "kvq_ans.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -298,4 +298,56 @@ kvq_status kvq_dequantize(const kvq_plan* p, const uint32_t* codes, const float*
     return ok();
 }
 
+kvq_status kvq_ans_sizes(const kvq_plan* p, uint64_t* scratch_bytes, uint64_t* stream_bytes) {
+    if (!valid_plan(p)) return fail(KVQ_EINVAL, "invalid plan");
+    if (!scratch_bytes || !stream_bytes) return fail(KVQ_EINVAL, "null host pointer");
+    const uint64_t b = 4u * p->max_code_words + (uint64_t)p->n_blocks * kvq::ans_margin_bytes(p->d_block);
+    *scratch_bytes = b;
+    *stream_bytes = b;
+    return ok();
+}
+
+kvq_status kvq_ans_encode(const kvq_plan* p, const uint32_t* codes, const uint8_t* m,
+                          const uint64_t* word_off, void* scratch, uint64_t scratch_bytes, void* stream,
+                          uint64_t stream_bytes, uint64_t* block_off, void* workspace,
+                          uint64_t* total_bytes_out, hipStream_t s) {
+    if (!valid_plan(p)) return fail(KVQ_EINVAL, "invalid plan");
+    if (!m || !word_off || !scratch || !stream || !block_off || !workspace || (!codes && p->max_code_words))
+        return fail(KVQ_EINVAL, "null device pointer");
+    if (!total_bytes_out) return fail(KVQ_EINVAL, "null host pointer");
+    uint64_t need = 0, need2 = 0;
+    kvq_ans_sizes(p, &need, &need2);
+    if (scratch_bytes < need || stream_bytes < need2)
+        return fail(KVQ_ENOSPC, "entropy-coding buffers need %llu bytes each (kvq_ans_sizes)",
+                    (unsigned long long)need);
+    if ((((uintptr_t)scratch) | ((uintptr_t)stream)) & 3u) return fail(KVQ_EINVAL, "buffers must be 4-byte aligned");
+    hipError_t e = kvq::launch_ws_reset(workspace, s);
+    if (e != hipSuccess) return hip_fail(e, "ws_reset");
+    e = kvq::launch_ans_encode(codes, m, word_off, p->n_blocks, p->d_block, p->s, (uint16_t*)scratch,
+                               (uint8_t*)stream, block_off, workspace, s);
+    if (e != hipSuccess) return hip_fail(e, "entropy-coding launch");
+    kvq::WsHeader hdr;
+    uint64_t total = 0;
+    e = hipMemcpyAsync(&hdr, workspace, sizeof hdr, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(&total, block_off + p->n_blocks, sizeof total, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "entropy-coding sync");
+    if (hdr.status & kvq::kStatusAnsOverflow) return fail(KVQ_ENOSPC, "a coded block outgrew its scratch region");
+    *total_bytes_out = total;
+    return ok();
+}
+
+kvq_status kvq_ans_decode(const kvq_plan* p, const void* stream, const uint64_t* block_off,
+                          const float* codebook, const uint8_t* m, float* xhat, void* workspace,
+                          hipStream_t s) {
+    if (!valid_plan(p)) return fail(KVQ_EINVAL, "invalid plan");
+    if (!stream || !block_off || !codebook || !m || !xhat || !workspace)
+        return fail(KVQ_EINVAL, "null device pointer");
+    if (((uintptr_t)stream) & 3u) return fail(KVQ_EINVAL, "stream must be 4-byte aligned");
+    hipError_t e = kvq::launch_ans_decode((const uint8_t*)stream, block_off, codebook, m, p->n_blocks,
+                                          p->d_block, p->s, xhat, workspace, s);
+    if (e != hipSuccess) return hip_fail(e, "entropy-decoding launch");
+    return ok();
+}
+
 }  // extern "C"

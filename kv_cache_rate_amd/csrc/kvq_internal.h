@@ -21,6 +21,8 @@ constexpr int kMaxLam = 64;                       // multipliers per solve pass
 
 // Device status bits (workspace header).
 constexpr uint32_t kStatusNonFinite = 1u;
+constexpr uint32_t kStatusAnsOverflow = 2u;  // an entropy-coded block outgrew its region
+constexpr uint32_t kStatusAnsCorrupt = 4u;   // a decoded block's states did not return to 2^16
 
 // Fixed header at the start of the caller's workspace.  All solve state lives
 // here so the whole bracket search runs on the device without host syncs.
@@ -302,5 +304,15 @@ hipError_t launch_quantize(const Geom& g, int64_t R, int s, const float* codeboo
 hipError_t launch_dequantize(int64_t R, int n, int s, const uint32_t* codes,
                              const float* codebook, const uint8_t* m, const uint64_t* off,
                              float* xhat, hipStream_t st);
+// off[0] = 0 and off[1..R] = sizes -> exclusive prefix sums (tile sums in ws)
+hipError_t launch_offsets_scan(uint64_t* off, int64_t R, void* ws, hipStream_t st);
+// entropy coding (kvq_ans.hip): per-block scratch margin, encode, decode
+__host__ __device__ uint64_t ans_margin_bytes(int n);
+hipError_t launch_ans_encode(const uint32_t* codes, const uint8_t* m, const uint64_t* word_off,
+                             int64_t R, int n, int s, uint16_t* scratch, uint8_t* stream,
+                             uint64_t* block_off, void* ws, hipStream_t st);
+hipError_t launch_ans_decode(const uint8_t* stream, const uint64_t* block_off, const float* codebook,
+                             const uint8_t* m, int64_t R, int n, int s, float* xhat, void* ws,
+                             hipStream_t st);
 
 }  // namespace kvq

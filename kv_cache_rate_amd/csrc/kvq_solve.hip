@@ -552,6 +552,13 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
         hipLaunchKernelGGL(final_dp_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, stats, R,
                            p.alphabet_m, p.s, p.s, n, shift, h, choice, codebook, m, off);
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_offsets_scan(off, R, ws, st);
+}
+
+hipError_t launch_offsets_scan(uint64_t* off, int64_t R, void* ws, hipStream_t st) {
+    if (R == 0) return hipSuccess;
     const int64_t tiles = (R + kScanTile - 1) / kScanTile;
     uint64_t* tile_sums = (uint64_t*)((char*)ws + kWsHeaderBytes);
     hipLaunchKernelGGL(scan_tiles_kernel, dim3((unsigned)tiles), dim3(kSolveThreads), 0, st, off, R,

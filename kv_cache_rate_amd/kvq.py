@@ -29,7 +29,8 @@ KVQ_BISECT = 0
 KVQ_SUBGRAD = 1
 
 EXPORTED = ("kvq_status_string", "kvq_last_error", "kvq_plan_blocks", "kvq_eval_candidates",
-            "kvq_solve_lambda", "kvq_quantize_pack", "kvq_dequantize")
+            "kvq_solve_lambda", "kvq_quantize_pack", "kvq_dequantize", "kvq_ans_sizes",
+            "kvq_ans_encode", "kvq_ans_decode")
 
 
 class KvqTensor(ctypes.Structure):
@@ -97,6 +98,13 @@ def lib():
                                         vp, vp, vp, u64, vp, u64, vp]
         L.kvq_dequantize.restype = i32
         L.kvq_dequantize.argtypes = [ctypes.POINTER(KvqPlan), vp, vp, vp, vp, vp, vp]
+        L.kvq_ans_sizes.restype = i32
+        L.kvq_ans_sizes.argtypes = [ctypes.POINTER(KvqPlan), ctypes.POINTER(u64), ctypes.POINTER(u64)]
+        L.kvq_ans_encode.restype = i32
+        L.kvq_ans_encode.argtypes = [ctypes.POINTER(KvqPlan), vp, vp, vp, vp, u64, vp, u64, vp, vp,
+                                     ctypes.POINTER(u64), vp]
+        L.kvq_ans_decode.restype = i32
+        L.kvq_ans_decode.argtypes = [ctypes.POINTER(KvqPlan), vp, vp, vp, vp, vp, vp, vp]
         _LIB = L
     return _LIB
 
@@ -199,6 +207,37 @@ def kvq_quantize_pack(plan, tensors, codebook, m, word_off, seed, codes, capacit
 def kvq_dequantize(plan, codes, codebook, m, word_off, xhat, stream=None):
     _check(lib().kvq_dequantize(ctypes.byref(plan), _ptr(codes), _ptr(codebook), _ptr(m),
                                 _ptr(word_off), _ptr(xhat), _stream(stream)))
+
+
+def kvq_ans_sizes(plan):
+    """Returns ``(scratch_bytes, stream_bytes)``."""
+    a, b = ctypes.c_uint64(0), ctypes.c_uint64(0)
+    _check(lib().kvq_ans_sizes(ctypes.byref(plan), ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def kvq_ans_encode(plan, codes, m, word_off, scratch, stream, block_off, workspace, stream_obj=None):
+    """Returns the coded stream's length in bytes."""
+    total = ctypes.c_uint64(0)
+    _check(lib().kvq_ans_encode(ctypes.byref(plan), _ptr(codes), _ptr(m), _ptr(word_off), _ptr(scratch),
+                                int(scratch.numel() * scratch.element_size()), _ptr(stream),
+                                int(stream.numel() * stream.element_size()), _ptr(block_off),
+                                _ptr(workspace), ctypes.byref(total), _stream(stream_obj)))
+    return total.value
+
+
+def kvq_ans_decode(plan, stream, block_off, codebook, m, xhat, workspace, stream_obj=None):
+    _check(lib().kvq_ans_decode(ctypes.byref(plan), _ptr(stream), _ptr(block_off), _ptr(codebook),
+                                _ptr(m), _ptr(xhat), _ptr(workspace), _stream(stream_obj)))
+
+
+def allocate_ans(plan, device="cuda"):
+    """Device buffers for kvq_ans_encode / kvq_ans_decode."""
+    import torch
+    sb, tb = kvq_ans_sizes(plan)
+    return {"scratch": torch.empty(max(4, sb), dtype=torch.uint8, device=device),
+            "stream": torch.empty(max(4, tb), dtype=torch.uint8, device=device),
+            "block_off": torch.empty(plan.n_blocks + 1, dtype=torch.int64, device=device)}
 
 
 # ---------------------------------------------------------------------------

@@ -121,6 +121,27 @@ def test_calls_validate_before_launch(L):
     assert Lb.kvq_dequantize(ctypes.byref(p), 8, None, 8, 8, 8, None) == kvq.KVQ_EINVAL
 
 
+def test_entropy_coding_sizes_and_validation(L):
+    """kvq_ans_sizes: 4 bytes per fixed-width word plus a per-block margin
+    (table, final states, and the coder's slack); encode and decode refuse
+    null pointers and short buffers on the host."""
+    t = np.zeros((2, 4, 64, 128), dtype=np.float16)
+    p = kvq.kvq_plan_blocks([t], 32, 128, 16)
+    sb, tb = kvq.kvq_ans_sizes(p)
+    margin = 128 + 4 * ((4096 + 63) // 64)
+    assert sb == tb == 4 * p.max_code_words + p.n_blocks * margin
+    Lb = kvq.lib()
+    total = ctypes.c_uint64(0)
+    assert Lb.kvq_ans_encode(ctypes.byref(p), 8, 8, 8, 8, sb, 8, tb, 8, None, ctypes.byref(total),
+                             None) == kvq.KVQ_EINVAL
+    assert Lb.kvq_ans_encode(ctypes.byref(p), 8, 8, 8, 8, sb - 1, 8, tb, 8, 8, ctypes.byref(total),
+                             None) == kvq.KVQ_ENOSPC
+    assert "kvq_ans_sizes" in kvq.last_error()
+    assert Lb.kvq_ans_encode(ctypes.byref(p), 8, 8, 8, 8, sb, 8, tb, 8, 8, None, None) == kvq.KVQ_EINVAL
+    assert Lb.kvq_ans_decode(ctypes.byref(p), None, 8, 8, 8, 8, 8, None) == kvq.KVQ_EINVAL
+    assert Lb.kvq_ans_decode(ctypes.byref(p), 10, 8, 8, 8, 8, 8, None) == kvq.KVQ_EINVAL  # unaligned
+
+
 def test_xcd_block_mapping_is_a_bijection():
     """Host-side check of the workgroup -> block mapping used by the scoring
     kernels (XCD x owns a contiguous range of blocks)."""
