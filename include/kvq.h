@@ -189,6 +189,20 @@ kvq_status kvq_solve_lambda(const kvq_plan* p, const double* D, const double* H,
                             float* codebook, uint8_t* m, uint64_t* word_off,
                             void* workspace, hipStream_t s);
 
+/* kvq_solve_lambda with each block's distortion weighted: block r chooses
+   argmin w_r D_r + lambda d_r H_r (the page's optional weighting of D_r by
+   attention sensitivity, Implementation notes); the budget and the
+   multiplier search are unchanged.  weight: device fp64 [R], finite and
+   > 0 (other values give unspecified choices); NULL means every w_r = 1,
+   i.e. exactly kvq_solve_lambda.  KVQ_GRIDS only (KVQ_EINVAL otherwise). */
+kvq_status kvq_solve_lambda_weighted(const kvq_plan* p, const double* D, const double* H,
+                                     const double* weight, const float* stats,
+                                     double B_bits_per_entry, int32_t mode, int32_t iters,
+                                     double eta, double* lambda_io,
+                                     double* rate_bits_per_entry_out, int32_t* choice,
+                                     float* codebook, uint8_t* m, uint64_t* word_off,
+                                     void* workspace, hipStream_t s);
+
 /* Unbiased stochastic interpolation of every entry on its block's codebook
    and fixed-width packing (Key formulas (3); Implementation notes).  The
    draw of entry t of block r is Philox4x32-10 with key (seed lo, seed hi),

@@ -237,7 +237,17 @@ kvq_status kvq_solve_lambda(const kvq_plan* p, const double* D, const double* H,
                             double B, int32_t mode, int32_t iters, double eta, double* lambda_io,
                             double* rate_out, int32_t* choice, float* codebook, uint8_t* m,
                             uint64_t* word_off, void* workspace, hipStream_t s) {
+    return kvq_solve_lambda_weighted(p, D, H, nullptr, stats, B, mode, iters, eta, lambda_io, rate_out,
+                                     choice, codebook, m, word_off, workspace, s);
+}
+
+kvq_status kvq_solve_lambda_weighted(const kvq_plan* p, const double* D, const double* H,
+                                     const double* weight, const float* stats, double B, int32_t mode,
+                                     int32_t iters, double eta, double* lambda_io, double* rate_out,
+                                     int32_t* choice, float* codebook, uint8_t* m, uint64_t* word_off,
+                                     void* workspace, hipStream_t s) {
     if (!valid_plan(p)) return fail(KVQ_EINVAL, "invalid plan");
+    if (weight && p->search != KVQ_GRIDS) return fail(KVQ_EINVAL, "distortion weights need KVQ_GRIDS");
     if (!D || !H || !stats || !choice || !codebook || !m || !word_off || !workspace)
         return fail(KVQ_EINVAL, "null device pointer");
     if (!lambda_io || !rate_out) return fail(KVQ_EINVAL, "null host pointer");
@@ -249,8 +259,8 @@ kvq_status kvq_solve_lambda(const kvq_plan* p, const double* D, const double* H,
         return fail(KVQ_EINVAL, "subgradient needs finite lambda >= 0 and finite eta");
     kvq::RankTable rt;
     rank_table(*p, rt);
-    hipError_t e = kvq::launch_solve(*p, rt, D, H, stats, B, mode, iters, lam_in, choice, codebook, m,
-                                     word_off, workspace, s);
+    hipError_t e = kvq::launch_solve(*p, rt, D, H, weight, stats, B, mode, iters, lam_in, choice,
+                                     codebook, m, word_off, workspace, s);
     if (e != hipSuccess) return hip_fail(e, "solve launch");
     kvq::WsHeader hdr;
     e = hipMemcpyAsync(&hdr, workspace, sizeof hdr, hipMemcpyDeviceToHost, s);

@@ -295,7 +295,8 @@ hipError_t launch_eval_alphabet(const Geom& g, int64_t R, int alpha_m, double* D
                                 float* stats, void* ws, hipStream_t st);
 hipError_t launch_ws_reset(void* ws, hipStream_t st);
 hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
-                        const double* H, const float* stats, double B, int mode, int iters,
+                        const double* H, const double* wgt, const float* stats, double B,
+                        int mode, int iters,
                         double lam_in, int32_t* choice, float* codebook, uint8_t* m,
                         uint64_t* off, void* ws, hipStream_t st);
 hipError_t launch_quantize(const Geom& g, int64_t R, int s, const float* codebook,

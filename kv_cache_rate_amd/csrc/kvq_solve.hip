@@ -160,18 +160,20 @@ __global__ void solve_select_kernel(WsHeader* h) {
 // ---------------------------------------------------------------- grids ----
 
 __global__ void __launch_bounds__(kSolveThreads)
-rates_grids_kernel(const double* __restrict__ D, const double* __restrict__ H, int64_t R, int C,
-                   double d, int shift, WsHeader* h) {
+rates_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
+                   const double* __restrict__ wgt, int64_t R, int C, double d, int shift,
+                   WsHeader* h) {
     __shared__ unsigned long long part[kSolveThreads / 64][kMaxLam];
     const int nlam = h->nlam;
     if (h->done || nlam == 0) return;
     const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     double Dr[kMaxCand], Hr[kMaxCand];
     if (r < R) {
+        const double wr = wgt ? wgt[r] : 1.0;  // distortion weight (1: exact identity)
 #pragma unroll
         for (int c = 0; c < kMaxCand; ++c) {
             if (c < C) {
-                Dr[c] = D[c * R + r];
+                Dr[c] = wr * D[c * R + r];
                 Hr[c] = H[c * R + r];
             }
         }
@@ -236,7 +238,8 @@ __device__ int build_grid_codebook(int c, const float* st, int64_t stride, const
 
 __global__ void __launch_bounds__(kSolveThreads)
 final_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
-                   const float* __restrict__ stats, int64_t R, int C, int s, int n, int shift,
+                   const double* __restrict__ wgt, const float* __restrict__ stats, int64_t R,
+                   int C, int s, int n, int shift,
                    RankTable rt, WsHeader* h, int32_t* __restrict__ choice,
                    float* __restrict__ codebook, uint8_t* __restrict__ m_out,
                    uint64_t* __restrict__ off) {
@@ -255,10 +258,11 @@ final_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
         const double lamd = h->lam_final * d;
         const double* Dr = D + r;
         const double* Hr = H + r;
-        double best = objective(Dr[0], Hr[0], lamd);
+        const double wr = wgt ? wgt[r] : 1.0;
+        double best = objective(wr * Dr[0], Hr[0], lamd);
         int bc = 0;
         for (int c = 1; c < C; ++c) {
-            const double o = objective(Dr[c * R], Hr[c * R], lamd);
+            const double o = objective(wr * Dr[c * R], Hr[c * R], lamd);
             if (o < best) {
                 best = o;
                 bc = c;
@@ -508,7 +512,8 @@ scan_add_kernel(uint64_t* off, int64_t R, const uint64_t* tile_sums) {
 // ----------------------------------------------------------------- host ----
 
 hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D, const double* H,
-                        const float* stats, double B, int mode, int iters, double lam_in,
+                        const double* wgt, const float* stats, double B, int mode, int iters,
+                        double lam_in,
                         int32_t* choice, float* codebook, uint8_t* m, uint64_t* off, void* ws,
                         hipStream_t st) {
     WsHeader* h = (WsHeader*)ws;
@@ -523,8 +528,8 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
     const unsigned grid = (unsigned)((R + kSolveThreads - 1) / kSolveThreads);
     auto rates_pass = [&]() {
         if (p.search == KVQ_GRIDS) {
-            hipLaunchKernelGGL(rates_grids_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, R,
-                               p.n_cand, (double)n, shift, h);
+            hipLaunchKernelGGL(rates_grids_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, wgt,
+                               R, p.n_cand, (double)n, shift, h);
         } else {
             hipLaunchKernelGGL(rates_dp_kernel, dim3((unsigned)R), dim3(64), 0, st, D, H, stats, R,
                                p.alphabet_m, p.s, n, shift, h);
@@ -546,8 +551,8 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
         }
     }
     if (p.search == KVQ_GRIDS) {
-        hipLaunchKernelGGL(final_grids_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, stats, R,
-                           p.n_cand, p.s, n, shift, rt, h, choice, codebook, m, off);
+        hipLaunchKernelGGL(final_grids_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, wgt, stats,
+                           R, p.n_cand, p.s, n, shift, rt, h, choice, codebook, m, off);
     } else {
         hipLaunchKernelGGL(final_dp_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, stats, R,
                            p.alphabet_m, p.s, p.s, n, shift, h, choice, codebook, m, off);

@@ -29,7 +29,8 @@ KVQ_BISECT = 0
 KVQ_SUBGRAD = 1
 
 EXPORTED = ("kvq_status_string", "kvq_last_error", "kvq_plan_blocks", "kvq_eval_candidates",
-            "kvq_solve_lambda", "kvq_quantize_pack", "kvq_dequantize", "kvq_ans_sizes",
+            "kvq_solve_lambda", "kvq_solve_lambda_weighted", "kvq_quantize_pack", "kvq_dequantize",
+            "kvq_ans_sizes",
             "kvq_ans_encode", "kvq_ans_decode")
 
 
@@ -93,6 +94,10 @@ def lib():
         L.kvq_solve_lambda.argtypes = [ctypes.POINTER(KvqPlan), vp, vp, vp, f64, i32, i32, f64,
                                        ctypes.POINTER(f64), ctypes.POINTER(f64), vp, vp, vp, vp,
                                        vp, vp]
+        L.kvq_solve_lambda_weighted.restype = i32
+        L.kvq_solve_lambda_weighted.argtypes = [ctypes.POINTER(KvqPlan), vp, vp, vp, vp, f64, i32, i32,
+                                                f64, ctypes.POINTER(f64), ctypes.POINTER(f64), vp, vp,
+                                                vp, vp, vp, vp]
         L.kvq_quantize_pack.restype = i32
         L.kvq_quantize_pack.argtypes = [ctypes.POINTER(KvqPlan), ctypes.POINTER(KvqTensor), i32,
                                         vp, vp, vp, u64, vp, u64, vp]
@@ -192,6 +197,19 @@ def kvq_solve_lambda(plan, D, H, stats, B, mode, iters, eta, lam, choice, codebo
                                   iters, float(eta), ctypes.byref(lam_io), ctypes.byref(rate),
                                   _ptr(choice), _ptr(codebook), _ptr(m), _ptr(word_off),
                                   _ptr(workspace), _stream(stream)))
+    return lam_io.value, rate.value
+
+
+def kvq_solve_lambda_weighted(plan, D, H, weight, stats, B, mode, iters, eta, lam, choice, codebook,
+                              m, word_off, workspace, stream=None):
+    """Returns ``(lambda, rate_bits_per_entry)``; ``weight`` is a device
+    fp64 [R] array (or None)."""
+    lam_io = ctypes.c_double(lam)
+    rate = ctypes.c_double(0.0)
+    _check(lib().kvq_solve_lambda_weighted(ctypes.byref(plan), _ptr(D), _ptr(H), _ptr(weight), _ptr(stats),
+                                           float(B), mode, iters, float(eta), ctypes.byref(lam_io),
+                                           ctypes.byref(rate), _ptr(choice), _ptr(codebook), _ptr(m),
+                                           _ptr(word_off), _ptr(workspace), _stream(stream)))
     return lam_io.value, rate.value
 
 

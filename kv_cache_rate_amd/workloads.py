@@ -230,3 +230,19 @@ def reduced(w, layers):
     finish)."""
     ts = tuple((nm, (layers,) + shp[1:]) for nm, shp in w.tensors)
     return Workload(**{**w.__dict__, "tensors": ts, "name": w.name + f"_{layers}l"})
+
+
+def sensitivity_weights(w, sigma=0.5):
+    """Per-block distortion weights standing in for attention sensitivity
+    measured on a calibration batch (no model or calibration data exists
+    here): one log-normal(0, sigma) weight per (tensor, outer index, head),
+    shared by that head's token chunks and feature groups, seeded from the
+    workload.  Returned in block order (tensor, outer, head, chunk, group)
+    as fp64."""
+    rng = np.random.default_rng(np.random.SeedSequence(2000 + w.index))
+    out = []
+    for _, (o, h, t, d) in w.tensors:
+        per_head = rng.lognormal(0.0, sigma, size=(o, h))
+        reps = (t // w.tokens_per_block) * (d // w.dims_per_block)
+        out.append(np.repeat(per_head.reshape(-1), reps))
+    return np.concatenate(out).astype(np.float64)

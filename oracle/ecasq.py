@@ -154,14 +154,18 @@ def eval_block(x, s):
     return D, H, stats, cands
 
 
-def choose(D, H, d, lam):
+def choose(D, H, d, lam, w=None):
     """Per-block argmin of D + lambda d H (ties to the lowest index).
 
     ``D``, ``H`` are ``[R, C]``; ``d`` is the block length (scalar or [R]).
-    The objective is evaluated as D + ((lambda * d) * H) in fp64.
+    The objective is evaluated as D + ((lambda * d) * H) in fp64.  With
+    per-block weights ``w`` ([R], the page's optional attention-sensitivity
+    weighting of D_r, Implementation notes) it is (w_r D) + ((lambda d) H).
     """
     D = np.asarray(D, dtype=np.float64)
     H = np.asarray(H, dtype=np.float64)
+    if w is not None:
+        D = np.asarray(w, dtype=np.float64)[:, None] * D
     scale = np.float64(lam) * np.asarray(d, dtype=np.float64)
     if np.ndim(scale):
         scale = scale[:, None]
@@ -180,7 +184,7 @@ class Infeasible(Exception):
     """No multiplier up to 2**64 meets the budget."""
 
 
-def solve_bisect(D, H, d, B, iters=40):
+def solve_bisect(D, H, d, B, iters=40, w=None):
     """Bisection on the multiplier until sum_r d_r H_r <= B * sum_r d_r.
 
     Bracket: lambda = 0 if it is already feasible; otherwise lo = 0, hi = 1
@@ -195,7 +199,7 @@ def solve_bisect(D, H, d, B, iters=40):
     probes = []
 
     def rate(lam):
-        c = choose(D, H, dr, lam)
+        c = choose(D, H, dr, lam, w)
         rt = total_rate(H, dr, c)
         probes.append((lam, rt))
         return rt, c
@@ -221,7 +225,7 @@ def solve_bisect(D, H, d, B, iters=40):
     return hi, ch, rh, Btot, probes
 
 
-def subgrad_step(D, H, d, B, lam_prev, eta):
+def subgrad_step(D, H, d, B, lam_prev, eta, w=None):
     """One decode-time dual step.
 
     The blocks are chosen at the known multiplier ``lam_prev``; the modelled
@@ -231,7 +235,7 @@ def subgrad_step(D, H, d, B, lam_prev, eta):
     """
     R = np.asarray(D).shape[0]
     dr = np.broadcast_to(np.asarray(d, dtype=np.float64), (R,))
-    c = choose(D, H, dr, lam_prev)
+    c = choose(D, H, dr, lam_prev, w)
     rbar = total_rate(H, dr, c) / math.fsum(dr.tolist())
     lam_next = max(0.0, float(lam_prev) + float(eta) * (rbar - float(B)))
     return c, rbar, lam_next

@@ -83,9 +83,12 @@ def eval_exact(blocks, m_alpha, smax, processes=None):
 
 
 def run(blocks, *, search="grids", s=16, alphabet_m=12, B=2.0, mode="bisect",
-        iters=40, lam_prev=0.0, eta=1e-3, seed=0, quantize=True, processes=None):
+        iters=40, lam_prev=0.0, eta=1e-3, seed=0, quantize=True, processes=None, weights=None):
     """Admission of ``blocks`` ([R, n] fp64).  Returns a dict of every
-    intermediate and final result (see the keys below)."""
+    intermediate and final result (see the keys below).  ``weights`` ([R])
+    weights each block's distortion in the dual choice (grid search only)."""
+    if weights is not None and search != "grids":
+        raise ValueError("distortion weights apply to the grid search")
     R, n = blocks.shape
     d = float(n)
     out = {"n": n, "R": R}
@@ -110,11 +113,11 @@ def run(blocks, *, search="grids", s=16, alphabet_m=12, B=2.0, mode="bisect",
         raise ValueError(search)
 
     if mode == "bisect":
-        lam, choice, rate, Btot, probes = ecasq.solve_bisect(Dt, Ht, d, B, iters)
+        lam, choice, rate, Btot, probes = ecasq.solve_bisect(Dt, Ht, d, B, iters, weights)
         out.update(lam=lam, choice=choice, rate_bits=rate, B_total=Btot, probes=probes,
                    rate_per_entry=rate / (d * R))
     elif mode == "subgrad":
-        choice, rbar, lam_next = ecasq.subgrad_step(Dt, Ht, d, B, lam_prev, eta)
+        choice, rbar, lam_next = ecasq.subgrad_step(Dt, Ht, d, B, lam_prev, eta, weights)
         out.update(lam=lam_next, lam_used=lam_prev, choice=choice, rate_per_entry=rbar,
                    rate_bits=rbar * d * R)
     else:

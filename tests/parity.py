@@ -29,9 +29,10 @@ def to_cuda(arrays):
 
 
 def run_gpu(tensors, *, tokens_per_block, dims_per_block, s, search, alphabet_m=12, B, mode,
-            iters=40, eta=1e-3, lam=0.0, seed=0, dequant=True, tensors_dev=None):
+            iters=40, eta=1e-3, lam=0.0, seed=0, dequant=True, tensors_dev=None, weights=None):
     """Run plan -> eval -> solve -> quantize -> dequantize through the C ABI
-    and return every output as numpy."""
+    and return every output as numpy (``weights``: per-block distortion
+    weights, solved with kvq_solve_lambda_weighted)."""
     import torch
     from kv_cache_rate_amd import kvq
     dev = tensors_dev if tensors_dev is not None else to_cuda(tensors)
@@ -40,7 +41,17 @@ def run_gpu(tensors, *, tokens_per_block, dims_per_block, s, search, alphabet_m=
                                alphabet_m if sm else 0)
     buf = kvq.allocate(plan, dequant=dequant)
     md = kvq.KVQ_BISECT if mode == "bisect" else kvq.KVQ_SUBGRAD
-    lam_out, rate = kvq.admit(plan, dev, buf, B, md, iters, eta, lam, seed, dequant=dequant)
+    if weights is None:
+        lam_out, rate = kvq.admit(plan, dev, buf, B, md, iters, eta, lam, seed, dequant=dequant)
+    else:
+        wd = torch.from_numpy(np.ascontiguousarray(weights, dtype=np.float64)).cuda()
+        kvq.kvq_eval_candidates(plan, dev, buf["D"], buf["H"], buf["stats"], buf["workspace"])
+        lam_out, rate = kvq.kvq_solve_lambda_weighted(plan, buf["D"], buf["H"], wd, buf["stats"], B, md,
+                                                      iters, eta, lam, buf["choice"], buf["codebook"],
+                                                      buf["m"], buf["off"], buf["workspace"])
+        kvq.kvq_quantize_pack(plan, dev, buf["codebook"], buf["m"], buf["off"], seed, buf["codes"])
+        if dequant:
+            kvq.kvq_dequantize(plan, buf["codes"], buf["codebook"], buf["m"], buf["off"], buf["xhat"])
     torch.cuda.synchronize()
     out = {k: v.cpu().numpy() for k, v in buf.items() if k != "workspace"}
     if sm == kvq.KVQ_GRIDS:  # candidate-major on the device; block-major here
@@ -56,11 +67,11 @@ def run_gpu(tensors, *, tokens_per_block, dims_per_block, s, search, alphabet_m=
 
 
 def run_oracle(tensors, *, tokens_per_block, dims_per_block, s, search, alphabet_m=12, B, mode,
-               iters=40, eta=1e-3, lam=0.0, seed=0, processes=None):
+               iters=40, eta=1e-3, lam=0.0, seed=0, processes=None, weights=None):
     b = oblocks.partition(tensors, tokens_per_block, dims_per_block)
     out = pipeline.run(b, search=search, s=s, alphabet_m=alphabet_m, B=B, mode=mode, iters=iters,
                        lam_prev=lam, eta=eta, seed=seed,
-                       processes=processes or pipeline.default_processes())
+                       processes=processes or pipeline.default_processes(), weights=weights)
     out["blocks"] = b
     return out
 
@@ -103,14 +114,15 @@ def compare_tables(g, o, search):
     return rep
 
 
-def compare_choice(g, o, lam, d):
+def compare_choice(g, o, lam, d, weights=None):
     """Codebooks identical by value except documented ties.  Returns
     (mask of blocks whose codebooks agree, tie count, max tie gap)."""
     R = g["m"].shape[0]
     agree = np.zeros(R, dtype=bool)
     ties = 0
     max_gap = 0.0
-    obj = o["D"] + (lam * d) * o["H"]
+    Dw = o["D"] if weights is None else np.asarray(weights, dtype=np.float64)[:, None] * o["D"]
+    obj = Dw + (lam * d) * o["H"]
     for r in range(R):
         mg = int(g["m"][r])
         Qg = g["codebook"][r, :mg].astype(np.float64)
@@ -163,7 +175,7 @@ def compare_codes(g, o, agree, seed):
 LAM_RTOL = 1e-6
 
 
-def full_compare(g, o, search, seed, B=None, mode="bisect", lam_used_gpu=None):
+def full_compare(g, o, search, seed, B=None, mode="bisect", lam_used_gpu=None, weights=None):
     """Compare a GPU run with an oracle run on the same inputs.
 
     The two bisections replay the same probes; they can part only where a
@@ -183,7 +195,7 @@ def full_compare(g, o, search, seed, B=None, mode="bisect", lam_used_gpu=None):
             rep["lam_path_divergence"] = 1
     rep["lam"] = g["lam"]
     lam_used = o["lam"] if mode == "bisect" else o["lam_used"]
-    agree, ties, gap = compare_choice(g, o, lam_used, d)
+    agree, ties, gap = compare_choice(g, o, lam_used, d, weights)
     rep["ties"] = ties
     rep["max_tie_gap"] = gap
     assert np.array_equal(g["m"], o["m"]) or ties > 0

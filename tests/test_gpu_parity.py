@@ -184,3 +184,26 @@ def test_deterministic_repeat():
     for k in ("D", "H", "stats", "codebook", "m", "off", "codes", "xhat"):
         assert np.array_equal(a[k], b[k]), k
     assert a["lam"] == b["lam"]
+
+
+# ------------------------------------------------ weighted distortion ---
+
+@pytest.mark.parametrize("name", ["tiny_k_fp32", "prefill_kv_fp16"])
+def test_weighted_distortion(name):
+    """Per-(tensor, head) log-normal distortion weights (a stand-in for
+    attention sensitivity from a calibration batch) through
+    kvq_solve_lambda_weighted; the bisection, choices and codes must match
+    the oracle's weighted solve, and the weights must move the allocation."""
+    from oracle import ecasq
+    w = W.BY_NAME[name]
+    B = 1.0 if name == "tiny_k_fp32" else 1.5  # budgets that bind (lambda > 0)
+    x = W.generate(w)
+    wt = W.sensitivity_weights(w)
+    kw = _kw(w, B=B)
+    g = parity.run_gpu(x, **kw, weights=wt)
+    o = parity.run_oracle(x, **kw, weights=wt)
+    rep = parity.full_compare(g, o, "grids", w.seed, B, "bisect", weights=wt)
+    _say(f"{name} weighted report {rep}")
+    assert o["lam"] > 0.0
+    plain = ecasq.choose(o["D"], o["H"], float(o["n"]), o["lam"])
+    assert np.any(plain != o["choice"])

@@ -159,3 +159,56 @@ def test_two_block_mechanism():
     assert rate <= rate4
     assert ks[choice[0]] < ks[choice[1]]
     assert D[0, choice[0]] + D[1, choice[1]] < D[0, c4] + D[1, c4]
+
+
+# ------------------------------------------------ weighted distortion ---
+
+def _tables(rng, R=40, C=9):
+    D = rng.uniform(0.1, 10.0, size=(R, C))
+    H = rng.uniform(0.0, 4.0, size=(R, C))
+    return D, H
+
+
+def test_unit_weights_are_the_unweighted_problem(rng):
+    D, H = _tables(rng)
+    w = np.ones(D.shape[0])
+    for lam in (0.0, 1e-3, 0.37, 5.0):
+        assert np.array_equal(ecasq.choose(D, H, 64.0, lam, w), ecasq.choose(D, H, 64.0, lam))
+    a = ecasq.solve_bisect(D, H, 64.0, 1.5, 30, w)
+    b = ecasq.solve_bisect(D, H, 64.0, 1.5, 30)
+    assert a[0] == b[0] and np.array_equal(a[1], b[1])
+
+
+def test_weight_scaling_is_a_multiplier_scaling(rng):
+    """argmin (4w) D + lam d H = argmin w D + (lam / 4) d H exactly (powers of
+    two scale every rounded term exactly)."""
+    D, H = _tables(rng)
+    w = rng.lognormal(0.0, 0.5, size=D.shape[0])
+    for lam in (1e-3, 0.37, 5.0):
+        assert np.array_equal(ecasq.choose(D, H, 64.0, lam, 4.0 * w),
+                              ecasq.choose(D, H, 64.0, lam / 4.0, w))
+
+
+def test_heavier_weight_never_raises_a_blocks_distortion(rng):
+    """Exchange argument: w' > w implies D(choice at w') <= D(choice at w)."""
+    D, H = _tables(rng, R=200)
+    w = rng.lognormal(0.0, 0.5, size=200)
+    for lam in (0.01, 0.2, 1.0):
+        c1 = ecasq.choose(D, H, 64.0, lam, w)
+        c2 = ecasq.choose(D, H, 64.0, lam, 1.7 * w)
+        r = np.arange(200)
+        assert np.all(D[r, c2] <= D[r, c1])
+
+
+def test_weighted_bisection_is_feasible_and_tight(rng):
+    D, H = _tables(rng, R=60)
+    w = rng.lognormal(0.0, 0.5, size=60)
+    lam, c, rate, Btot, probes = ecasq.solve_bisect(D, H, 64.0, 1.2, 40, w)
+    assert rate <= Btot
+    assert np.array_equal(c, ecasq.choose(D, H, 64.0, lam, w))
+    # the closest probe below lambda was infeasible, within the bracket width
+    lo = max((p for p, r in probes if p < lam), default=0.0)
+    assert dict(probes)[lo] > Btot
+    assert lam - lo <= 2.0 ** -40 * max(1.0, 2.0 * lam)
+    below = ecasq.choose(D, H, 64.0, lo, w)
+    assert ecasq.total_rate(H, 64.0, below) > Btot
