@@ -259,6 +259,27 @@ kvq_status kvq_ans_decode(const kvq_plan* p, const void* stream, const uint64_t*
                           const float* codebook, const uint8_t* m, float* xhat, void* workspace,
                           hipStream_t s);
 
+/* ---- Decode attention over the quantized cache (Implementation notes:
+   decode before attention; the decode runs inside the attention kernel, so
+   only codes and codebooks are read).  For one new query per query head,
+   o = sum_t softmax_t(scale q . k_t) v_t over every cached token, k_t and v_t
+   the stored codepoints.  The plan must hold K (tensor 0) and V (tensor 1)
+   [outer, heads, tokens, 128] cut into head x 32-token blocks; query head g
+   reads KV head g / G, G = q_heads / heads in {1, 2, 4}.  fp32 arithmetic. */
+
+/* Bytes of the split-partials workspace for q_heads query heads (host). */
+kvq_status kvq_decode_attention_workspace(const kvq_plan* p, int32_t q_heads, uint64_t* bytes);
+
+/* codes, codebook, m, word_off: as written by kvq_solve_lambda and
+   kvq_quantize_pack for plan p.  q: device fp32 [outer][q_heads][128];
+   out: device fp32 [outer][q_heads][128]; work: device, at least the
+   kvq_decode_attention_workspace bytes.  Asynchronous on stream s.
+   Errors: KVQ_EINVAL (shape, group), KVQ_ENOSPC (workspace). */
+kvq_status kvq_decode_attention(const kvq_plan* p, const uint32_t* codes, const float* codebook,
+                                const uint8_t* m, const uint64_t* word_off, const float* q,
+                                int32_t q_heads, float scale, float* out, void* work,
+                                uint64_t work_bytes, hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

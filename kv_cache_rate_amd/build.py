@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libkvq.so")
 ARCH = "gfx950"
 
 SOURCES = ["kvq_host.cpp", "kvq_eval.hip", "kvq_eval16.hip", "kvq_solve.hip", "kvq_quant.hip",
-           "kvq_ans.hip"]
+           "kvq_ans.hip", "kvq_attn.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

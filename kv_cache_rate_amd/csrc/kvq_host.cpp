@@ -360,4 +360,46 @@ kvq_status kvq_ans_decode(const kvq_plan* p, const void* stream, const uint64_t*
     return ok();
 }
 
+static kvq_status attention_shape(const kvq_plan* p, int32_t q_heads, int& group) {
+    if (!valid_plan(p)) return fail(KVQ_EINVAL, "invalid plan");
+    if (p->n_tensors != 2) return fail(KVQ_EINVAL, "decode attention needs the K and V tensors");
+    if (p->tokens_per_block != 32 || p->dims_per_block != 128 || p->shape[0][3] != 128)
+        return fail(KVQ_EINVAL, "decode attention supports head x 32-token blocks of head_dim 128");
+    const int64_t heads = p->shape[0][1];
+    if (q_heads <= 0 || q_heads % heads) return fail(KVQ_EINVAL, "query heads must be a multiple of KV heads");
+    group = (int)(q_heads / heads);
+    if (group != 1 && group != 2 && group != 4)
+        return fail(KVQ_EINVAL, "query heads per KV head must be 1, 2 or 4 (got %d)", group);
+    return ok();
+}
+
+kvq_status kvq_decode_attention_workspace(const kvq_plan* p, int32_t q_heads, uint64_t* bytes) {
+    int group = 0;
+    kvq_status st = attention_shape(p, q_heads, group);
+    if (st) return st;
+    if (!bytes) return fail(KVQ_EINVAL, "null host pointer");
+    *bytes = kvq::attn_workspace_bytes(p->shape[0][0], (int)p->shape[0][1], (int)(p->shape[0][2] / 32), group);
+    return ok();
+}
+
+kvq_status kvq_decode_attention(const kvq_plan* p, const uint32_t* codes, const float* codebook,
+                                const uint8_t* m, const uint64_t* word_off, const float* q,
+                                int32_t q_heads, float scale, float* out, void* work,
+                                uint64_t work_bytes, hipStream_t s) {
+    int group = 0;
+    kvq_status st = attention_shape(p, q_heads, group);
+    if (st) return st;
+    if (!codebook || !m || !word_off || !q || !out || !work || (!codes && p->max_code_words))
+        return fail(KVQ_EINVAL, "null device pointer");
+    if (!isfinite(scale)) return fail(KVQ_EINVAL, "scale must be finite");
+    uint64_t need = 0;
+    kvq_decode_attention_workspace(p, q_heads, &need);
+    if (work_bytes < need) return fail(KVQ_ENOSPC, "attention workspace needs %llu bytes", (unsigned long long)need);
+    hipError_t e = kvq::launch_decode_attention(codes, codebook, m, word_off, p->tensor_blocks[0], p->shape[0][0],
+                                                (int)p->shape[0][1], (int)(p->shape[0][2] / 32), p->s, group, q,
+                                                scale, out, work, s);
+    if (e != hipSuccess) return hip_fail(e, "decode attention launch");
+    return ok();
+}
+
 }  // extern "C"

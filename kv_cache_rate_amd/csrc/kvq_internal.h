@@ -312,6 +312,12 @@ __host__ __device__ uint64_t ans_margin_bytes(int n);
 hipError_t launch_ans_encode(const uint32_t* codes, const uint8_t* m, const uint64_t* word_off,
                              int64_t R, int n, int s, uint16_t* scratch, uint8_t* stream,
                              uint64_t* block_off, void* ws, hipStream_t st);
+// decode attention over the quantized cache (kvq_attn.hip)
+uint64_t attn_workspace_bytes(int64_t outer, int heads, int chunks, int group);
+hipError_t launch_decode_attention(const uint32_t* codes, const float* codebook, const uint8_t* m,
+                                   const uint64_t* word_off, int64_t nbK, int64_t outer, int heads,
+                                   int chunks, int s, int group, const float* q, float scale,
+                                   float* out, void* work, hipStream_t st);
 hipError_t launch_ans_decode(const uint8_t* stream, const uint64_t* block_off, const float* codebook,
                              const uint8_t* m, int64_t R, int n, int s, float* xhat, void* ws,
                              hipStream_t st);

@@ -31,7 +31,8 @@ KVQ_SUBGRAD = 1
 EXPORTED = ("kvq_status_string", "kvq_last_error", "kvq_plan_blocks", "kvq_eval_candidates",
             "kvq_solve_lambda", "kvq_solve_lambda_weighted", "kvq_quantize_pack", "kvq_dequantize",
             "kvq_ans_sizes",
-            "kvq_ans_encode", "kvq_ans_decode")
+            "kvq_ans_encode", "kvq_ans_decode", "kvq_decode_attention_workspace",
+            "kvq_decode_attention")
 
 
 class KvqTensor(ctypes.Structure):
@@ -108,6 +109,11 @@ def lib():
         L.kvq_ans_encode.restype = i32
         L.kvq_ans_encode.argtypes = [ctypes.POINTER(KvqPlan), vp, vp, vp, vp, u64, vp, u64, vp, vp,
                                      ctypes.POINTER(u64), vp]
+        L.kvq_decode_attention_workspace.restype = i32
+        L.kvq_decode_attention_workspace.argtypes = [ctypes.POINTER(KvqPlan), i32, ctypes.POINTER(u64)]
+        L.kvq_decode_attention.restype = i32
+        L.kvq_decode_attention.argtypes = [ctypes.POINTER(KvqPlan), vp, vp, vp, vp, vp, i32,
+                                           ctypes.c_float, vp, vp, u64, vp]
         L.kvq_ans_decode.restype = i32
         L.kvq_ans_decode.argtypes = [ctypes.POINTER(KvqPlan), vp, vp, vp, vp, vp, vp, vp]
         _LIB = L
@@ -247,6 +253,19 @@ def kvq_ans_encode(plan, codes, m, word_off, scratch, stream, block_off, workspa
 def kvq_ans_decode(plan, stream, block_off, codebook, m, xhat, workspace, stream_obj=None):
     _check(lib().kvq_ans_decode(ctypes.byref(plan), _ptr(stream), _ptr(block_off), _ptr(codebook),
                                 _ptr(m), _ptr(xhat), _ptr(workspace), _stream(stream_obj)))
+
+
+def kvq_decode_attention_workspace(plan, q_heads):
+    b = ctypes.c_uint64(0)
+    _check(lib().kvq_decode_attention_workspace(ctypes.byref(plan), int(q_heads), ctypes.byref(b)))
+    return b.value
+
+
+def kvq_decode_attention(plan, codes, codebook, m, word_off, q, q_heads, scale, out, work, stream=None):
+    _check(lib().kvq_decode_attention(ctypes.byref(plan), _ptr(codes), _ptr(codebook), _ptr(m),
+                                      _ptr(word_off), _ptr(q), int(q_heads), float(scale), _ptr(out),
+                                      _ptr(work), int(work.numel() * work.element_size()),
+                                      _stream(stream)))
 
 
 def allocate_ans(plan, device="cuda"):

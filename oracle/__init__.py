@@ -21,6 +21,7 @@ exact_dp   quantile alphabet, pair statistics, brute force and pair-state DP
 philox     Philox4x32-10 counter-based generator
 codes      stochastic interpolation, fixed-width packing, decode
 ans        rANS entropy coding of each block's symbol stream
+attention  decode attention over the decoded cache
 pipeline   the whole admission pass for one configuration
 
 Parity status: every function is pinned by ``tests/test_oracle_*.py``
@@ -28,4 +29,4 @@ Parity status: every function is pinned by ``tests/test_oracle_*.py``
 implementation); none is "parity unpinned".
 """
 
-from . import blocks, ecasq, exact_dp, philox, codes, ans, pipeline  # noqa: F401
+from . import blocks, ecasq, exact_dp, philox, codes, ans, attention, pipeline  # noqa: F401

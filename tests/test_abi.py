@@ -142,6 +142,23 @@ def test_entropy_coding_sizes_and_validation(L):
     assert Lb.kvq_ans_decode(ctypes.byref(p), 10, 8, 8, 8, 8, 8, None) == kvq.KVQ_EINVAL  # unaligned
 
 
+def test_decode_attention_validation(L):
+    """Shapes the attention kernel does not take are refused on the host."""
+    k = np.zeros((1, 8, 256, 128), dtype=np.float16)
+    p = kvq.kvq_plan_blocks([k, k], 32, 128, 16)
+    assert kvq.kvq_decode_attention_workspace(p, 32) == 1 * 8 * 4 * 1 * (128 + 2) * 4
+    Lb = kvq.lib()
+    b = ctypes.c_uint64(0)
+    assert Lb.kvq_decode_attention_workspace(ctypes.byref(p), 24, ctypes.byref(b)) == kvq.KVQ_EINVAL
+    assert Lb.kvq_decode_attention_workspace(ctypes.byref(p), 20, ctypes.byref(b)) == kvq.KVQ_EINVAL
+    p1 = kvq.kvq_plan_blocks([k], 32, 128, 16)
+    assert Lb.kvq_decode_attention_workspace(ctypes.byref(p1), 8, ctypes.byref(b)) == kvq.KVQ_EINVAL
+    p2 = kvq.kvq_plan_blocks([k, k], 16, 128, 16)
+    assert Lb.kvq_decode_attention_workspace(ctypes.byref(p2), 8, ctypes.byref(b)) == kvq.KVQ_EINVAL
+    assert Lb.kvq_decode_attention(ctypes.byref(p), 8, 8, 8, 8, 8, 32, ctypes.c_float(0.1), 8, 8,
+                                   10, None) == kvq.KVQ_ENOSPC
+
+
 def test_xcd_block_mapping_is_a_bijection():
     """Host-side check of the workgroup -> block mapping used by the scoring
     kernels (XCD x owns a contiguous range of blocks)."""
