@@ -13,13 +13,13 @@
 // count in tensor 1.
 //
 // Kernel 1: a workgroup takes (o, h, split of 16 chunks).  Thread (slot j,
-// feature group f) owns token j of every chunk and features 16f..16f+15; it
-// decodes its 16 K and 16 V entries per chunk, finishes the G dot products
-// with its 7 partners by xor shuffles, and keeps a running maximum, sum of
-// weights and weighted V sum (online softmax) per query head.  The 32 token
-// slots are merged by log-sum-exp (shuffles inside a wave, LDS across the
-// 4 waves) into one partial per query head and split.  Kernel 2 merges the
-// splits and divides.
+// feature group f) owns tokens j and j + 16 of every chunk and features
+// 8f..8f+7; it decodes its 8 K and 8 V entries per token, finishes the G dot
+// products with its 15 partners by xor shuffles, and keeps a running
+// maximum, sum of weights and weighted V sum (online softmax) per query
+// head.  The 16 token slots are merged by log-sum-exp (shuffles inside a
+// wave, LDS across the 4 waves) into one partial per query head and split.
+// Kernel 2 merges the splits and divides.
 #include <math.h>
 
 #include "kvq_internal.h"
@@ -33,34 +33,22 @@ constexpr int kChunkSplit = 16;           // chunks (32-token blocks) per workgr
 constexpr int kHD = 128;                  // head dim
 constexpr int kTB = 32;                   // tokens per block
 
-// 16 codes of width w starting at bit 16 w t of a block's code stream.
-__device__ __forceinline__ void codes16(const uint32_t* cw, int w, int t, uint32_t out[16]) {
-    if (w == 0) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) out[i] = 0u;
-        return;
-    }
-    const uint32_t bit = 16u * (uint32_t)w * (uint32_t)t;
-    const uint32_t q = bit >> 5, sh = bit & 31u;  // sh is 0 or 16
+// The 8 codes of width w of entries 8u .. 8u + 7 of a block's code stream
+// (8 w <= 32 bits, so one funnel shift gathers them).
+__device__ __forceinline__ uint32_t codes8(const uint32_t* cw, uint32_t nwords, int w, int u) {
+    if (w == 0) return 0u;
+    const uint32_t byte = (uint32_t)w * (uint32_t)u;  // w bytes per 8 codes
+    const uint32_t q = byte >> 2, sh = 8u * (byte & 3u);
     const uint32_t a = cw[q];
-    const uint32_t b = (sh + 16u * (uint32_t)w > 32u) ? cw[q + 1] : 0u;
-    const uint32_t c = (sh + 16u * (uint32_t)w > 64u) ? cw[q + 2] : 0u;
-    const uint64_t lo = ((uint64_t)b << 32) | a;
-    const uint32_t mask = (1u << w) - 1u;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const uint32_t p = sh + (uint32_t)(w * i);  // < 16 + 60
-        const uint32_t v = p < 32u ? (uint32_t)(lo >> p)
-                                   : (p < 64u ? (uint32_t)((((uint64_t)c << 32) | b) >> (p - 32u))
-                                              : (c >> (p - 64u)));
-        out[i] = v & mask;
-    }
+    const uint32_t b = (sh + 8u * (uint32_t)w > 32u && q + 1 < nwords) ? cw[q + 1] : 0u;
+    return (uint32_t)((((uint64_t)b << 32) | a) >> sh);
 }
 
-__device__ __forceinline__ float xor_sum8(float v) {
+__device__ __forceinline__ float xor_sum16(float v) {
     v += __shfl_xor(v, 1, 64);
     v += __shfl_xor(v, 2, 64);
     v += __shfl_xor(v, 4, 64);
+    v += __shfl_xor(v, 8, 64);
     return v;
 }
 
@@ -75,11 +63,12 @@ attn_split_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ 
     __shared__ float cb[2][kChunkSplit][kMaxS];
     __shared__ int wdt[2][kChunkSplit];
     __shared__ uint64_t wof[2][kChunkSplit];
+    __shared__ uint32_t nwd[2][kChunkSplit];
     __shared__ float xm[4][G], xl[4][G];
     __shared__ float xa[4][G][kHD];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int j = tid >> 3, f = tid & 7;
+    const int j = tid >> 4, f = tid & 15;
     const int sp = blockIdx.x, h = blockIdx.y, o = blockIdx.z;
     const int c0 = sp * kChunkSplit, c1 = min(c0 + kChunkSplit, chunks);
     const int64_t rbase = ((int64_t)o * heads + h) * chunks;
@@ -94,72 +83,76 @@ attn_split_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ 
             if (k == 0) {
                 wdt[t][c] = code_width(mm);
                 wof[t][c] = word_off[r];
+                nwd[t][c] = (uint32_t)(word_off[r + 1] - word_off[r]);
             }
         }
     }
-    float qv[G][16];
+    float qv[G][8];
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            qv[g][i] = scale * q[((int64_t)o * heads * G + h * G + g) * kHD + 16 * f + i];
+        for (int i = 0; i < 8; ++i)
+            qv[g][i] = scale * q[((int64_t)o * heads * G + h * G + g) * kHD + 8 * f + i];
     __syncthreads();
-    float mx[G], sl[G], acc[G][16];
+    float mx[G], sl[G], acc[G][8];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         mx[g] = -__builtin_huge_valf();
         sl[g] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[g][i] = 0.0f;
+        for (int i = 0; i < 8; ++i) acc[g][i] = 0.0f;
     }
     for (int c = 0; c < c1 - c0; ++c) {
-        uint32_t ck[16], cv[16];
-        codes16(codes + wof[0][c], wdt[0][c], tid, ck);
-        codes16(codes + wof[1][c], wdt[1][c], tid, cv);
-        float sc[G];
+        const int wk = wdt[0][c], wv = wdt[1][c];
+        const uint32_t mk = (1u << wk) - 1u, mv = (1u << wv) - 1u;
 #pragma unroll
-        for (int g = 0; g < G; ++g) sc[g] = 0.0f;
+        for (int half = 0; half < 2; ++half) {
+            const int u = 16 * (j + 16 * half) + f;  // 8-entry group of token j + 16 half
+            const uint32_t kc = codes8(codes + wof[0][c], nwd[0][c], wk, u);
+            float sc[G];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float kv = cb[0][c][ck[i]];
+            for (int g = 0; g < G; ++g) sc[g] = 0.0f;
 #pragma unroll
-            for (int g = 0; g < G; ++g) sc[g] = fmaf(qv[g][i], kv, sc[g]);
-        }
+            for (int i = 0; i < 8; ++i) {
+                const float kv = cb[0][c][(kc >> (wk * i)) & mk];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float sg = xor_sum8(sc[g]);
-            const float mn = fmaxf(mx[g], sg);
-            const float corr = __expf(mx[g] - mn);
-            const float p = __expf(sg - mn);
-            mx[g] = mn;
-            sl[g] = fmaf(sl[g], corr, p);
+                for (int g = 0; g < G; ++g) sc[g] = fmaf(qv[g][i], kv, sc[g]);
+            }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[g][i] *= corr;
-            sc[g] = p;
-        }
+            for (int g = 0; g < G; ++g) {
+                const float sg = xor_sum16(sc[g]);
+                if (sg > mx[g]) {  // new maximum: rescale the running sums
+                    const float corr = __expf(mx[g] - sg);
+                    mx[g] = sg;
+                    sl[g] *= corr;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float vv = cb[1][c][cv[i]];
+                    for (int i = 0; i < 8; ++i) acc[g][i] *= corr;
+                }
+                sc[g] = __expf(sg - mx[g]);
+                sl[g] += sc[g];
+            }
+            const uint32_t vc = codes8(codes + wof[1][c], nwd[1][c], wv, u);
 #pragma unroll
-            for (int g = 0; g < G; ++g) acc[g][i] = fmaf(sc[g], vv, acc[g][i]);
+            for (int i = 0; i < 8; ++i) {
+                const float vv = cb[1][c][(vc >> (wv * i)) & mv];
+#pragma unroll
+                for (int g = 0; g < G; ++g) acc[g][i] = fmaf(sc[g], vv, acc[g][i]);
+            }
         }
     }
-    // merge the 8 token slots of the wave (lanes 8j' + f share f)
+    // merge the 4 token slots of the wave (lanes 16j' + f share f)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         float M = mx[g];
-        M = fmaxf(M, __shfl_xor(M, 8, 64));
         M = fmaxf(M, __shfl_xor(M, 16, 64));
         M = fmaxf(M, __shfl_xor(M, 32, 64));
         const float e = mx[g] == -__builtin_huge_valf() ? 0.0f : __expf(mx[g] - M);
         float L = sl[g] * e;
-        L += __shfl_xor(L, 8, 64);
         L += __shfl_xor(L, 16, 64);
         L += __shfl_xor(L, 32, 64);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 8; ++i) {
             float a = acc[g][i] * e;
-            a += __shfl_xor(a, 8, 64);
             a += __shfl_xor(a, 16, 64);
             a += __shfl_xor(a, 32, 64);
             acc[g][i] = a;
@@ -168,9 +161,9 @@ attn_split_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ 
             xm[wave][g] = M;
             xl[wave][g] = L;
         }
-        if (lane < 8) {
+        if (lane < 16) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) xa[wave][g][16 * f + i] = acc[g][i];
+            for (int i = 0; i < 8; ++i) xa[wave][g][8 * f + i] = acc[g][i];
         }
     }
     __syncthreads();
