@@ -140,6 +140,84 @@ def decode_latency(torch, kvq, W, steps=1000, warmup=20):
             "calls_us": {k: q(v) for k, v in per.items()}, "lambda_final": lam}
 
 
+def extensions(torch, kvq, W, w, plan, dev, buf, stream):
+    """The rows beyond the admission step, measured on the same cache after
+    the timed steps (not part of `value`): entropy-coded size and coding
+    times, fused decode attention vs torch's fp16 attention on the
+    uncompressed cache, and a decode stream's multiplier trace."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            ev[0].record(stream)
+            fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]))
+        return float(np.median(ts))
+
+    out = {}
+    # entropy coding of the symbol stream (rANS, per-block models)
+    ab = kvq.allocate_ans(plan)
+    total = [0]
+
+    def enc():
+        total[0] = kvq.kvq_ans_encode(plan, buf["codes"], buf["m"], buf["off"], ab["scratch"], ab["stream"],
+                                      ab["block_off"], buf["workspace"], stream)
+    t_enc = timed(enc)
+    t_dec = timed(lambda: kvq.kvq_ans_decode(plan, ab["stream"], ab["block_off"], buf["codebook"], buf["m"],
+                                             buf["xhat"], buf["workspace"], stream))
+    out["entropy_coding"] = {"coded_bits_per_entry": 8.0 * total[0] / w.n_entries,
+                             "fixed_width_bits_per_entry": 32.0 * float(buf["off"][-1].item()) / w.n_entries,
+                             "encode_ms_incl_sync": t_enc, "decode_ms": t_dec}
+    del ab
+    # decode attention over the quantized cache, 4 query heads per KV head
+    if plan.n_tensors == 2 and plan.tokens_per_block == 32 and plan.dims_per_block == 128:
+        L, Hk, T, D = dev[0].shape
+        Hq = 4 * Hk
+        g = torch.Generator(device="cuda").manual_seed(5)
+        q = torch.randn(L, Hq, D, device="cuda", dtype=torch.float32, generator=g)
+        o = torch.empty_like(q)
+        work = torch.empty(kvq.kvq_decode_attention_workspace(plan, Hq), dtype=torch.uint8, device="cuda")
+        t_att = timed(lambda: kvq.kvq_decode_attention(plan, buf["codes"], buf["codebook"], buf["m"], buf["off"],
+                                                       q, Hq, 1.0 / np.sqrt(D), o, work, stream))
+        qh = q.to(dev[0].dtype).view(L, Hq, 1, D)
+        t_sdpa = timed(lambda: torch.nn.functional.scaled_dot_product_attention(qh, dev[0], dev[1],
+                                                                                enable_gqa=True))
+        out["decode_attention"] = {"query_heads": Hq, "tokens": T, "layers": L, "fused_quantized_ms": t_att,
+                                   "torch_sdpa_fp16_uncompressed_ms": t_sdpa,
+                                   "codes_GB": 4.0 * float(buf["off"][-1].item()) / 1e9}
+    return out
+
+
+def decode_stream(torch, kvq, W, steps=200, batches=16):
+    """Decode stream: every step admits a fresh 512-block batch (Student-t
+    decode workload, one batch per step from its own seed) with one
+    subgradient step from the running multiplier; returns the multiplier
+    and rate trace.  The first multiplier comes from bisection on batch 0."""
+    w = W.DECODE_ADMIT_FP16
+    data = []
+    for b in range(batches):
+        rng = np.random.default_rng(np.random.SeedSequence(3000 + b))
+        (_, shp), = w.tensors
+        data.append([torch.from_numpy(rng.standard_t(5.0, size=shp).astype(np.float16)).cuda()])
+    plan = kvq.kvq_plan_blocks(data[0], w.tokens_per_block, w.dims_per_block, w.s)
+    buf = kvq.allocate(plan)
+    lam, _ = kvq.admit(plan, data[0], buf, w.B, kvq.KVQ_BISECT, w.iters, w.eta, 0.0, 0)
+    lams, rates = [lam], []
+    for t in range(steps):
+        lam, rate = kvq.admit(plan, data[(t + 1) % batches], buf, w.B, kvq.KVQ_SUBGRAD, w.iters, w.eta, lam,
+                              t + 1)
+        lams.append(lam)
+        rates.append(rate)
+    return {"steps": steps, "eta": w.eta, "B": w.B, "lambda_first": lams[:6], "lambda_last": lams[-1],
+            "rate_mean_last_100": float(np.mean(rates[-100:])),
+            "rate_min_max_last_100": [float(np.min(rates[-100:])), float(np.max(rates[-100:]))]}
+
+
 def cpu_baseline(w, tensors, target_s=10.0):
     """The oracle, as it stands, on the first blocks of the workload: eval,
     bisection, quantize+pack and decode, on all host cores."""
@@ -270,6 +348,9 @@ def main():
         log("measuring copy bandwidth and decode-step latency")
         extras["copy_GBps"] = copy_bandwidth(torch)
         extras["decode_admission_latency"] = decode_latency(torch, kvq, W)
+        log("measuring entropy coding, decode attention and a decode stream")
+        extras["extensions"] = extensions(torch, kvq, W, w, plan, dev, buf, stream)
+        extras["extensions"]["decode_stream"] = decode_stream(torch, kvq, W)
     rec = {
         "metric": "KV GB/s quantized (fp16 in) and % of HBM roofline at 32-token blocks",
         "value": value, "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
@@ -301,6 +382,7 @@ def main():
             (admit_ms * 1e-3) / 1e9 / extras["copy_GBps"]
         rec["roofline"]["frac_of_copy"] = achieved / extras["copy_GBps"]
         rec["decode_admission_latency"] = extras["decode_admission_latency"]
+        rec["extensions"] = extras["extensions"]
     if not a.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(w, host)

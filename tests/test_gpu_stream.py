@@ -1,0 +1,51 @@
+"""Decode stream: repeated admission of fresh decode batches with one
+projected subgradient step per batch (page "Rate-adaptive KV-cache
+quantizer", Implementation notes: lambda is updated every N generated
+tokens and its convergence recorded; Key formulas (4)).
+
+The GPU and the oracle each start from their own bisection on batch 0 and
+then follow their own multiplier; every step's modelled rate and next
+multiplier must agree (relative 1e-6: the two rate sums differ only by
+round-off of the score tables), and the trace is the recorded lambda
+convergence.
+"""
+
+import numpy as np
+import pytest
+
+from kv_cache_rate_amd import workloads as W
+
+from . import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _batch(b):
+    w = W.DECODE_ADMIT_FP16
+    rng = np.random.default_rng(np.random.SeedSequence(3000 + b))
+    (_, shp), = w.tensors
+    return [rng.standard_t(5.0, size=shp).astype(np.float16)]
+
+
+def test_lambda_trace_matches_the_oracle():
+    w = W.DECODE_ADMIT_FP16
+    kw = dict(tokens_per_block=w.tokens_per_block, dims_per_block=w.dims_per_block, s=w.s,
+              search="grids", B=w.B, iters=w.iters, eta=w.eta, dequant=False)
+    g = parity.run_gpu(_batch(0), mode="bisect", seed=0, **kw)
+    o = parity.run_oracle(_batch(0), mode="bisect", seed=0, **{k: v for k, v in kw.items() if k != "dequant"})
+    lg, lo = g["lam"], o["lam"]
+    assert abs(lg - lo) <= 1e-6 * max(abs(lo), 1e-300)
+    trace = [(lg, lo)]
+    for t in range(1, 7):
+        x = _batch(t)
+        g = parity.run_gpu(x, mode="subgrad", seed=t, lam=lg, **kw)
+        o = parity.run_oracle(x, mode="subgrad", seed=t, lam=lo,
+                              **{k: v for k, v in kw.items() if k != "dequant"})
+        assert g["rate_per_entry"] == pytest.approx(o["rate_per_entry"], rel=1e-6)
+        lg, lo = g["lam"], o["lam"]
+        assert lg == pytest.approx(lo, rel=1e-6, abs=1e-12)
+        trace.append((lg, lo))
+        print(f"[gpu-stream] step {t}: rate {g['rate_per_entry']:.6f} lambda {lg:.9f} (oracle {lo:.9f})",
+              flush=True)
+    # the multiplier moves against the rate error: lambda_t - lambda_{t-1} = eta (Rbar - B)
+    assert len(trace) == 7
