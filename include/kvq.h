@@ -68,6 +68,7 @@ typedef int32_t kvq_status;
 /* multiplier update (kvq_solve_lambda.mode) */
 #define KVQ_BISECT 0  /* bracket doubling then `iters` halvings; feasible end */
 #define KVQ_SUBGRAD 1 /* choose at lambda_io, then one projected step */
+#define KVQ_BISECT_GREEDY 2 /* KVQ_BISECT, then the greedy post-pass (grids) */
 
 #define KVQ_MAX_TENSORS 2
 #define KVQ_MAX_S 16
@@ -171,6 +172,15 @@ kvq_status kvq_eval_candidates(const kvq_plan* p, const kvq_tensor* t, int32_t n
    KVQ_BISECT: lambda = 0 if sum_r d_r H_r(argmin D) <= B sum_r d_r; else the
      bracket [0,1] doubles up to 2^64 until feasible, then `iters` halvings
      (iters <= 63); the feasible end is returned in *lambda_io (host).
+   KVQ_BISECT_GREEDY: KVQ_BISECT, then the remaining budget is spent
+     greedily (page "Joint Tucker-rank and residual-bit KV allocator",
+     Implementation notes: swap candidates with the best distortion
+     reduction per added bit): while some block has a candidate with more
+     bits and less distortion whose added bits fit the remainder, the block
+     with the largest (D_cur - D_c) / (d_r H_c - d_r H_cur) switches (ties:
+     lowest block, then lowest candidate).  lambda is the bisection's;
+     the rate returned is the filled one.  KVQ_GRIDS only.  Upgrades that
+     fit the slack beyond the workspace pool: KVQ_ENOSPC.
    KVQ_SUBGRAD: blocks are chosen at *lambda_io (host, input); then
      *lambda_io <- max(0, lambda + eta (Rbar - B)) with Rbar the modelled
      bits per entry.

@@ -199,8 +199,7 @@ kvq_status kvq_plan_blocks(const kvq_tensor* t, int32_t nt, const kvq_block_spec
     p.codebook_bytes = (size_t)R * p.s * sizeof(float);
     p.m_bytes = (size_t)R;
     p.offsets_bytes = (size_t)(R + 1) * sizeof(uint64_t);
-    const int64_t tiles = (R + 1023) / 1024 + 1;
-    p.workspace_bytes = (kvq::kWsHeaderBytes + (size_t)tiles * sizeof(uint64_t) + 255) & ~(size_t)255;
+    p.workspace_bytes = kvq::ws_pool_offset(R) + (size_t)kvq::kGreedyPool * 8;
     p.max_code_words = (uint64_t)R * (((uint64_t)n * kvq::code_width(max_levels) + 31) / 32);
     // fixed point for exact rate sums: total <= n_entries * log2(levels) bits
     const double max_rate = (double)p.n_entries * (double)kvq::code_width(max_levels) + 1.0;
@@ -251,9 +250,12 @@ kvq_status kvq_solve_lambda_weighted(const kvq_plan* p, const double* D, const d
     if (!D || !H || !stats || !choice || !codebook || !m || !word_off || !workspace)
         return fail(KVQ_EINVAL, "null device pointer");
     if (!lambda_io || !rate_out) return fail(KVQ_EINVAL, "null host pointer");
-    if (mode != KVQ_BISECT && mode != KVQ_SUBGRAD) return fail(KVQ_EINVAL, "unknown mode %d", mode);
+    if (mode != KVQ_BISECT && mode != KVQ_SUBGRAD && mode != KVQ_BISECT_GREEDY)
+        return fail(KVQ_EINVAL, "unknown mode %d", mode);
+    if (mode == KVQ_BISECT_GREEDY && p->search != KVQ_GRIDS)
+        return fail(KVQ_EINVAL, "the greedy post-pass needs KVQ_GRIDS");
     if (!isfinite(B) || B < 0.0) return fail(KVQ_EINVAL, "budget must be finite and >= 0");
-    if (mode == KVQ_BISECT && (iters < 0 || iters > 63)) return fail(KVQ_EINVAL, "iters must be 0..63");
+    if (mode != KVQ_SUBGRAD && (iters < 0 || iters > 63)) return fail(KVQ_EINVAL, "iters must be 0..63");
     const double lam_in = *lambda_io;
     if (mode == KVQ_SUBGRAD && (!isfinite(lam_in) || lam_in < 0.0 || !isfinite(eta)))
         return fail(KVQ_EINVAL, "subgradient needs finite lambda >= 0 and finite eta");
@@ -271,6 +273,8 @@ kvq_status kvq_solve_lambda_weighted(const kvq_plan* p, const double* D, const d
     if (hdr.err == KVQ_EINFEASIBLE)
         return fail(KVQ_EINFEASIBLE, "no lambda <= 2^64 brings the rate under %g bits/entry", B);
     if (hdr.err) return fail(KVQ_EINVAL, "solver state error %d", hdr.err);
+    if (hdr.pool_overflow)
+        return fail(KVQ_ENOSPC, "greedy post-pass: more than %u upgrades fit the slack", kvq::kGreedyPool);
     const double rbar = ldexp((double)hdr.rate_final, -p->rate_shift) / (double)p->n_entries;
     *rate_out = rbar;
     if (mode == KVQ_SUBGRAD) {

@@ -41,8 +41,18 @@ struct WsHeader {
     uint64_t Btot_fx;    // budget in the same fixed point
     double lam[kMaxLam + 8];
     unsigned long long sums[kMaxLam + 8];
+    uint32_t pool_n;          // greedy post-pass: upgrades collected
+    uint32_t pool_overflow;   // 1 if they exceeded the pool
+    uint32_t swaps;           // upgrades applied
+    uint32_t pad1;
 };
 constexpr size_t kWsHeaderBytes = 4096;
+constexpr uint32_t kGreedyPool = 16384;  // (block, candidate) pairs in the workspace pool
+// workspace = header, scan tile sums, greedy pool (8 bytes per pair)
+__host__ __device__ inline size_t ws_pool_offset(int64_t R) {
+    const int64_t tiles = (R + 1023) / 1024 + 1;
+    return (kWsHeaderBytes + (size_t)tiles * sizeof(uint64_t) + 255) & ~(size_t)255;
+}
 static_assert(sizeof(WsHeader) <= kWsHeaderBytes, "workspace header");
 
 // Block geometry as the kernels see it (passed by value).

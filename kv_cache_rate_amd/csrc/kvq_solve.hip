@@ -59,6 +59,9 @@ __global__ void solve_init_kernel(WsHeader* h, int mode, double lam_in, unsigned
     h->bits_left = iters;
     h->rate_final = 0;
     for (int j = 0; j < kMaxLam + 8; ++j) h->sums[j] = 0ull;
+    h->pool_n = 0;
+    h->pool_overflow = 0;
+    h->swaps = 0;
     if (mode == KVQ_SUBGRAD) {  // blocks are chosen at lam_in by the final pass
         h->phase = kPhaseSubgrad;
         h->nlam = 0;
@@ -509,6 +512,132 @@ scan_add_kernel(uint64_t* off, int64_t R, const uint64_t* tile_sums) {
     }
 }
 
+// ------------------------------------------------------- greedy fill ----
+// Post-pass after bisection (page "Joint Tucker-rank and residual-bit KV
+// allocator", Implementation notes: swap candidates with the best distortion
+// reduction per added byte).  Bits are the fixed-point rates of the bisection
+// (rate_fx), so the slack and every step are exact integers.
+
+__device__ __forceinline__ double wdist(const double* D, const double* wgt, int64_t R, int64_t r, int c) {
+    return (wgt ? wgt[r] : 1.0) * D[c * R + r];
+}
+
+// Every (block, candidate) upgrade that fits the slack left by the final
+// pass (the slack only shrinks, so later steps draw from this pool).
+__global__ void __launch_bounds__(kSolveThreads)
+greedy_pool_kernel(const double* __restrict__ D, const double* __restrict__ H,
+                   const double* __restrict__ wgt, int64_t R, int C, double d, int shift,
+                   WsHeader* h, const int32_t* __restrict__ choice, uint2* __restrict__ pool) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= R || h->err) return;
+    const int cur = choice[r];
+    if (cur < 0) return;
+    const unsigned long long slack = h->Btot_fx - h->rate_final;
+    const unsigned long long rc = rate_fx(d, H[cur * R + r], shift);
+    const double dc = wdist(D, wgt, R, r, cur);
+    for (int c = 0; c < C; ++c) {
+        const unsigned long long rn = rate_fx(d, H[c * R + r], shift);
+        if (rn > rc && rn - rc <= slack && dc - wdist(D, wgt, R, r, c) > 0.0) {
+            const uint32_t i = atomicAdd(&h->pool_n, 1u);
+            if (i < kGreedyPool) pool[i] = make_uint2((uint32_t)r, (uint32_t)c);
+            else h->pool_overflow = 1u;
+        }
+    }
+}
+
+// One workgroup applies upgrades one at a time: the best efficiency
+// (D_cur - D_c) / (d H_c - d H_cur) among pool entries that still improve
+// their block and fit; ties to the lowest block, then candidate.  The chosen
+// block's codebook, level count and word count are rebuilt in place.
+__global__ void __launch_bounds__(kSolveThreads)
+greedy_apply_kernel(const double* __restrict__ D, const double* __restrict__ H,
+                    const double* __restrict__ wgt, const float* __restrict__ stats, int64_t R,
+                    int s, int n, int shift, RankTable rt, WsHeader* h, int32_t* choice,
+                    float* __restrict__ codebook, uint8_t* __restrict__ m_out,
+                    uint64_t* __restrict__ off, const uint2* __restrict__ pool) {
+    __shared__ double be[kSolveThreads];
+    __shared__ uint32_t bi[kSolveThreads];
+    __shared__ unsigned long long slack;
+    __shared__ int found;
+    const int tid = threadIdx.x;
+    if (h->err || h->pool_overflow) return;
+    const uint32_t np = min(h->pool_n, kGreedyPool);
+    if (np == 0) return;
+    const double d = (double)n;
+    if (tid == 0) slack = h->Btot_fx - h->rate_final;
+    __syncthreads();
+    for (uint32_t step = 0; step < np * (uint32_t)kMaxCand; ++step) {
+        double best = -1.0;
+        uint32_t bidx = 0xffffffffu;
+        for (uint32_t i = tid; i < np; i += kSolveThreads) {
+            const uint2 e = pool[i];
+            const int64_t r = e.x;
+            const int c = (int)e.y;
+            const int cur = __hip_atomic_load(&choice[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const double hc = H[c * R + r], hu = H[cur * R + r];
+            const unsigned long long rn = rate_fx(d, hc, shift), ru = rate_fx(d, hu, shift);
+            const double dd = wdist(D, wgt, R, r, cur) - wdist(D, wgt, R, r, c);
+            if (rn > ru && rn - ru <= slack && dd > 0.0) {
+                const double eff = dd / (d * hc - d * hu);
+                // larger efficiency first; then lower block, lower candidate
+                const bool take = eff > best ||
+                                  (eff == best && (r < (int64_t)pool[bidx].x ||
+                                                   (r == (int64_t)pool[bidx].x && c < (int)pool[bidx].y)));
+                if (take) {
+                    best = eff;
+                    bidx = i;
+                }
+            }
+        }
+        be[tid] = best;
+        bi[tid] = bidx;
+        __syncthreads();
+        for (int w = kSolveThreads / 2; w > 0; w >>= 1) {
+            if (tid < w) {
+                const double eb = be[tid + w];
+                const uint32_t ib = bi[tid + w];
+                bool take = false;
+                if (ib != 0xffffffffu) {
+                    if (bi[tid] == 0xffffffffu || eb > be[tid]) {
+                        take = true;
+                    } else if (eb == be[tid]) {
+                        const uint2 a = pool[bi[tid]], b = pool[ib];
+                        take = b.x < a.x || (b.x == a.x && b.y < a.y);
+                    }
+                }
+                if (take) {
+                    be[tid] = eb;
+                    bi[tid] = ib;
+                }
+            }
+            __syncthreads();
+        }
+        if (tid == 0) {
+            found = bi[0] != 0xffffffffu;
+            if (found) {
+                const uint2 e = pool[bi[0]];
+                const int64_t r = e.x;
+                const int c = (int)e.y;
+                const int cur = __hip_atomic_load(&choice[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const unsigned long long rn = rate_fx(d, H[c * R + r], shift);
+                const unsigned long long ru = rate_fx(d, H[cur * R + r], shift);
+                slack -= rn - ru;
+                h->rate_final += rn - ru;
+                h->swaps += 1u;
+                __hip_atomic_store(&choice[r], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                float q[kMaxS];
+                const int m = build_grid_codebook(c, stats + r, R, rt, n, q);
+                m_out[r] = (uint8_t)m;
+                for (int j = 0; j < s; ++j) codebook[r * s + j] = j < m ? q[j] : 0.0f;
+                off[r + 1] = ((uint64_t)n * (uint64_t)code_width(m) + 31u) / 32u;
+            }
+        }
+        __threadfence();
+        __syncthreads();
+        if (!found) break;
+    }
+}
+
 // ----------------------------------------------------------------- host ----
 
 hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D, const double* H,
@@ -536,7 +665,7 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
         }
         hipLaunchKernelGGL(solve_select_kernel, dim3(1), dim3(64), 0, st, h);
     };
-    if (mode == KVQ_BISECT) {
+    if (mode == KVQ_BISECT || mode == KVQ_BISECT_GREEDY) {
         // lambda = 0 first; the bracket passes run only when it is infeasible
         rates_pass();
         int32_t done = 0;
@@ -556,6 +685,13 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
     } else {
         hipLaunchKernelGGL(final_dp_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, stats, R,
                            p.alphabet_m, p.s, p.s, n, shift, h, choice, codebook, m, off);
+    }
+    if (mode == KVQ_BISECT_GREEDY && p.search == KVQ_GRIDS) {
+        uint2* pool = (uint2*)((char*)ws + ws_pool_offset(R));
+        hipLaunchKernelGGL(greedy_pool_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, wgt, R,
+                           p.n_cand, (double)n, shift, h, choice, pool);
+        hipLaunchKernelGGL(greedy_apply_kernel, dim3(1), dim3(kSolveThreads), 0, st, D, H, wgt, stats, R,
+                           p.s, n, shift, rt, h, choice, codebook, m, off, pool);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

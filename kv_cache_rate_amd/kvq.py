@@ -27,6 +27,7 @@ KVQ_GRIDS = 0
 KVQ_EXACT_DP = 1
 KVQ_BISECT = 0
 KVQ_SUBGRAD = 1
+KVQ_BISECT_GREEDY = 2
 
 EXPORTED = ("kvq_status_string", "kvq_last_error", "kvq_plan_blocks", "kvq_eval_candidates",
             "kvq_solve_lambda", "kvq_solve_lambda_weighted", "kvq_quantize_pack", "kvq_dequantize",

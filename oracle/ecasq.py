@@ -42,6 +42,7 @@ Readings taken where the pages are silent (listed again in the design doc):
 """
 
 import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -239,3 +240,50 @@ def subgrad_step(D, H, d, B, lam_prev, eta, w=None):
     rbar = total_rate(H, dr, c) / math.fsum(dr.tolist())
     lam_next = max(0.0, float(lam_prev) + float(eta) * (rbar - float(B)))
     return c, rbar, lam_next
+
+
+def greedy_fill(D, H, d, Btot, choice, w=None):
+    """Post-pass after a feasible multiplier (the page "Joint Tucker-rank and
+    residual-bit KV allocator", Implementation notes: after the multiplier
+    search, improve the allocation by swapping candidates with the best
+    distortion reduction per added byte).
+
+    While some block has a candidate with more bits (dR > 0), less
+    (weighted) distortion (dD > 0) and dR no larger than the remaining
+    budget, switch the block with the largest dD / dR (fp64), ties to the
+    lowest block then the lowest candidate.  Rates are d H_{r,c} (fp64
+    products); the remaining budget and each dR are compared exactly
+    (rational arithmetic).  Returns ``(choice, rate_bits, swaps)``.
+    """
+    D = np.asarray(D, dtype=np.float64)
+    H = np.asarray(H, dtype=np.float64)
+    Dw = D if w is None else np.asarray(w, dtype=np.float64)[:, None] * D
+    R, C = D.shape
+    dr = float(d)
+    rates = dr * H                      # fp64 products, as the budget counts them
+    ch = np.array(choice, dtype=np.int64).copy()
+    rows = np.arange(R)
+    slack = Fraction(float(Btot)) - sum(Fraction(float(v)) for v in rates[rows, ch])
+    swaps = []
+    while True:
+        cur_r = rates[rows, ch][:, None]
+        cur_d = Dw[rows, ch][:, None]
+        dR = rates - cur_r              # fp64 screen; exact check below
+        dD = cur_d - Dw
+        ok = (dR > 0) & (dD > 0) & (dR <= float(slack) * (1 + 1e-12) + 1e-300)
+        best = None
+        for r, c in zip(*np.nonzero(ok)):
+            exact = Fraction(float(rates[r, c])) - Fraction(float(rates[r, ch[r]]))
+            if exact <= 0 or exact > slack:
+                continue
+            e = (Dw[r, ch[r]] - Dw[r, c]) / (rates[r, c] - rates[r, ch[r]])
+            key = (e, -int(r), -int(c))
+            if best is None or key > best[0]:
+                best = (key, int(r), int(c), exact)
+        if best is None:
+            break
+        _, r, c, exact = best
+        swaps.append((r, int(ch[r]), c))
+        ch[r] = c
+        slack -= exact
+    return ch, total_rate(H, dr, ch), swaps

@@ -112,10 +112,16 @@ def run(blocks, *, search="grids", s=16, alphabet_m=12, B=2.0, mode="bisect",
     else:
         raise ValueError(search)
 
-    if mode == "bisect":
+    if mode in ("bisect", "bisect_greedy"):
         lam, choice, rate, Btot, probes = ecasq.solve_bisect(Dt, Ht, d, B, iters, weights)
         out.update(lam=lam, choice=choice, rate_bits=rate, B_total=Btot, probes=probes,
                    rate_per_entry=rate / (d * R))
+        if mode == "bisect_greedy":
+            if search != "grids":
+                raise ValueError("the greedy post-pass applies to the grid search")
+            choice, rate, swaps = ecasq.greedy_fill(Dt, Ht, d, Btot, choice, weights)
+            out.update(choice=choice, rate_bits=rate, rate_per_entry=rate / (d * R), swaps=swaps,
+                       choice_bisect=out["choice"], rate_bits_bisect=out["rate_bits"])
     elif mode == "subgrad":
         choice, rbar, lam_next = ecasq.subgrad_step(Dt, Ht, d, B, lam_prev, eta, weights)
         out.update(lam=lam_next, lam_used=lam_prev, choice=choice, rate_per_entry=rbar,

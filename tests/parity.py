@@ -40,7 +40,8 @@ def run_gpu(tensors, *, tokens_per_block, dims_per_block, s, search, alphabet_m=
     plan = kvq.kvq_plan_blocks(dev, tokens_per_block, dims_per_block, s, sm,
                                alphabet_m if sm else 0)
     buf = kvq.allocate(plan, dequant=dequant)
-    md = kvq.KVQ_BISECT if mode == "bisect" else kvq.KVQ_SUBGRAD
+    md = {"bisect": kvq.KVQ_BISECT, "subgrad": kvq.KVQ_SUBGRAD,
+          "bisect_greedy": kvq.KVQ_BISECT_GREEDY}[mode]
     if weights is None:
         lam_out, rate = kvq.admit(plan, dev, buf, B, md, iters, eta, lam, seed, dequant=dequant)
     else:

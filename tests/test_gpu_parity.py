@@ -207,3 +207,29 @@ def test_weighted_distortion(name):
     assert o["lam"] > 0.0
     plain = ecasq.choose(o["D"], o["H"], float(o["n"]), o["lam"])
     assert np.any(plain != o["choice"])
+
+
+# --------------------------------------------------- greedy post-pass ---
+
+@pytest.mark.parametrize("name,B,iters", [("tiny_k_fp32", 1.0, 40), ("tiny_k_fp32", 1.2, 6),
+                                          ("prefill_kv_fp16", 1.5, 10), ("decode_admit_fp16", 2.0, 40)])
+def test_greedy_fill(name, B, iters):
+    """KVQ_BISECT_GREEDY: bisection, then the remaining budget spent on the
+    upgrades with the best distortion reduction per added bit.  Choices,
+    codebooks, offsets and codes must equal the oracle's greedy (its slack
+    is exact rational arithmetic, the GPU's fixed point at 2^-rate_shift
+    bits; no decision here lies within that of a boundary)."""
+    w = W.BY_NAME[name]
+    x = W.generate(w)
+    kw = _kw(w, B=B, mode="bisect_greedy", iters=iters)
+    g = parity.run_gpu(x, **kw)
+    o = parity.run_oracle(x, **kw)
+    _say(f"{name} B={B} iters={iters}: lambda {g['lam']!r} swaps {len(o['swaps'])} "
+         f"rate {g['rate_per_entry']:.6f} (bisection {o['rate_bits_bisect'] / (o['n'] * o['R']):.6f})")
+    assert g["lam"] == o["lam"]
+    assert np.array_equal(g["choice"].astype(np.int64), o["choice"])
+    assert g["rate_per_entry"] == pytest.approx(o["rate_per_entry"], rel=1e-12)
+    assert g["rate_per_entry"] <= B + 1e-12
+    assert np.array_equal(g["off"], o["offsets"])
+    agree = np.ones(o["R"], dtype=bool)
+    assert parity.compare_codes(g, o, agree, w.seed) <= o["near"]

@@ -212,3 +212,38 @@ def test_weighted_bisection_is_feasible_and_tight(rng):
     assert lam - lo <= 2.0 ** -40 * max(1.0, 2.0 * lam)
     below = ecasq.choose(D, H, 64.0, lo, w)
     assert ecasq.total_rate(H, 64.0, below) > Btot
+
+
+# --------------------------------------------------- greedy post-pass ---
+
+def test_greedy_fill_hand_example():
+    """Three blocks, d = 1.  Budget 4.0; bisection picks (H, D) = (1, 10)
+    for every block (rate 3).  Slack 1.0.  Upgrades: block 0 to (1.5, 6)
+    saves 4 for 0.5 bits (8 per bit); block 1 to (2, 5) saves 5 for 1 bit
+    (5 per bit); block 2 to (1.25, 9) saves 1 for 0.25 (4 per bit).
+    Greedy: block 0 (8/bit, slack 0.5 left), then block 2 (0.25 <= 0.5,
+    slack 0.25); block 1's step (1 bit) no longer fits."""
+    H = np.array([[1.0, 1.5], [1.0, 2.0], [1.0, 1.25]])
+    D = np.array([[10.0, 6.0], [10.0, 5.0], [10.0, 9.0]])
+    ch, rate, swaps = ecasq.greedy_fill(D, H, 1.0, 4.0, np.zeros(3, dtype=int))
+    assert swaps == [(0, 0, 1), (2, 0, 1)]
+    assert ch.tolist() == [1, 0, 1] and rate == 3.75
+
+
+def test_greedy_fill_properties(rng):
+    for trial in range(20):
+        R, C = 30, 8
+        H = np.sort(rng.uniform(0.0, 4.0, size=(R, C)), axis=1)
+        D = np.sort(rng.uniform(0.1, 10.0, size=(R, C)), axis=1)[:, ::-1].copy()
+        B = rng.uniform(0.8, 2.5)
+        lam, c0, r0, Btot, _ = ecasq.solve_bisect(D, H, 64.0, B, 30)
+        c1, r1, swaps = ecasq.greedy_fill(D, H, 64.0, Btot, c0)
+        r = np.arange(R)
+        assert r1 <= Btot                                  # still within budget
+        assert D[r, c1].sum() <= D[r, c0].sum()           # never worse
+        slack = Btot - r1
+        rates = 64.0 * H
+        up = (rates - rates[r, c1][:, None] > 0) & (D[r, c1][:, None] - D > 0)
+        assert not np.any(up & (rates - rates[r, c1][:, None] <= slack * (1 - 1e-12)))  # maximal
+        eff = [(D[b, a] - D[b, c]) / (rates[b, c] - rates[b, a]) for b, a, c in swaps]
+        assert all(x > 0 for x in eff)
