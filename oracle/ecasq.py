@@ -185,12 +185,39 @@ class Infeasible(Exception):
     """No multiplier up to 2**64 meets the budget."""
 
 
-def solve_bisect(D, H, d, B, iters=40, w=None):
-    """Bisection on the multiplier until sum_r d_r H_r <= B * sum_r d_r.
+def bisect_multiplier(rate_at, Btot, iters=40):
+    """Bisection on the multiplier for any per-multiplier allocation.
 
-    Bracket: lambda = 0 if it is already feasible; otherwise lo = 0, hi = 1
-    and hi doubles (lo following) while infeasible, up to 2**64; then
-    ``iters`` halvings.  The feasible end ``hi`` is returned with its choice.
+    ``rate_at(lam)`` returns ``(rate_bits_total, choice)`` of the blocks'
+    minimisers at ``lam``.  Bracket: lambda = 0 if it is already feasible;
+    otherwise lo = 0, hi = 1 and hi doubles (lo following) while infeasible,
+    up to 2**64; then ``iters`` halvings.  The feasible end ``hi`` is
+    returned with its choice and rate: ``(lam, choice, rate_bits_total)``.
+    """
+    r0, c0 = rate_at(0.0)
+    if r0 <= Btot:
+        return 0.0, c0, r0
+    lo, hi = 0.0, 1.0
+    while True:
+        rh, ch = rate_at(hi)
+        if rh <= Btot:
+            break
+        if hi >= 2.0 ** 64:
+            raise Infeasible("budget below the least-entropy allocation")
+        lo, hi = hi, hi * 2.0
+    for _ in range(iters):
+        mid = (lo + hi) / 2.0
+        rm, cm = rate_at(mid)
+        if rm <= Btot:
+            hi, rh, ch = mid, rm, cm
+        else:
+            lo = mid
+    return hi, ch, rh
+
+
+def solve_bisect(D, H, d, B, iters=40, w=None):
+    """Bisection on the multiplier until sum_r d_r H_r <= B * sum_r d_r, over
+    the candidate tables ``D``, ``H`` ([R, C]); see :func:`bisect_multiplier`.
     Returns ``(lam, choice, rate_bits_total, B_total, probes)`` where
     ``probes`` lists every (lambda, rate) evaluated, in order.
     """
@@ -205,25 +232,8 @@ def solve_bisect(D, H, d, B, iters=40, w=None):
         probes.append((lam, rt))
         return rt, c
 
-    r0, c0 = rate(0.0)
-    if r0 <= Btot:
-        return 0.0, c0, r0, Btot, probes
-    lo, hi = 0.0, 1.0
-    while True:
-        rh, ch = rate(hi)
-        if rh <= Btot:
-            break
-        if hi >= 2.0 ** 64:
-            raise Infeasible("budget below the least-entropy allocation")
-        lo, hi = hi, hi * 2.0
-    for _ in range(iters):
-        mid = (lo + hi) / 2.0
-        rm, cm = rate(mid)
-        if rm <= Btot:
-            hi, rh, ch = mid, rm, cm
-        else:
-            lo = mid
-    return hi, ch, rh, Btot, probes
+    lam, choice, rt = bisect_multiplier(rate, Btot, iters)
+    return lam, choice, rt, Btot, probes
 
 
 def subgrad_step(D, H, d, B, lam_prev, eta, w=None):

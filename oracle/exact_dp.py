@@ -8,14 +8,17 @@ minimum, maximum and quantiles; the Mathematical statement scores a codebook
 by the closed-form interpolation distortion and the entropy of expected
 frequencies (Key formulas (3)).
 
-Reading taken here: the alphabet is the sorted distinct set of the m = 12
-order statistics at ranks j (n-1)/11 rounded half up (j = 0..11); a
+Reading taken here: the alphabet is the sorted distinct set of the M
+order statistics at ranks j (n-1)/(M-1) rounded half up (j = 0..M-1; M = 12
+for the feature-group workload, up to 32 for the larger alphabets); a
 candidate is any subset S of the alphabet that contains its minimum and
-maximum and has 2 <= |S| <= s (s = 8).  The definition of the minimiser is
-brute force over all such subsets (:func:`brute_force_tables` + argmin, ties
-to the first subset in the order (size, lexicographic index tuple)).  The
+maximum and has 2 <= |S| <= s.  The definition of the minimiser is brute
+force over all such subsets (:func:`brute_force_tables` + argmin, ties to
+the first subset in the order (size, lexicographic index tuple)).  The
 pair-state dynamic program (:func:`dp_minimise`) is a second, independent
-route to the same minimum and is pinned to brute force in the tests.
+route to the same minimum and is pinned to brute force in the tests; it is
+the route used where brute force is out of reach (large M and s), with
+:func:`solve_bisect_dp` running the bisection on its minimisers.
 
 Decomposition used by both (an exact regrouping of the per-entry sums of
 Key formulas (3)): every entry of the block falls in exactly one interval
@@ -121,42 +124,115 @@ def _h(p):
     return -p * math.log2(p) if p > 0 else 0.0
 
 
+def _h_array(P):
+    """-p log2 p elementwise (0 where p <= 0)."""
+    P = np.asarray(P, dtype=np.float64)
+    out = np.zeros_like(P)
+    pos = P > 0
+    out[pos] = -P[pos] * np.log2(P[pos])
+    return out
+
+
 def dp_minimise(Dp, ML, MR, n, d, lam, smax):
     """Pair-state dynamic program for min_S D(S) + lam d H(S).
 
     State (c, i, j): best cost of a chain that starts at point 0, has c
     points and ends with the two points i < j; the cost holds the distortion
     of every closed interval and the entropy term of every point before j
-    (the frequency of q_j needs both of its neighbours).  Returns
-    ``(best_value, best_subset)``.
+    (the frequency of q_j needs both of its neighbours):
+
+        f_2[0, l]     = Dp[0, l] + w h(ML[0, l] / n)
+        f_{c+1}[j, l] = min_{i < j} (f_c[i, j] + Dp[j, l]) + w h((MR[i, j] + ML[j, l]) / n)
+        value         = min_{c, i} f_c[i, m-1] + w h(MR[i, m-1] / n)
+
+    with w = lam d and h(p) = -p log2 p.  Chains that reached the last point
+    are complete and are not extended.  Ties go to the lowest i, and across
+    completions to the smallest c, then the lowest i.  Each layer is
+    evaluated for all (i, j, l) at once.  Returns ``(best_value,
+    best_subset)``.
     """
     m = Dp.shape[0]
     if m == 1:
         return 0.0, (0,)
     w = lam * d
     INF = math.inf
-    # f[(i, j)] for the current count c, with the chain stored for the argmin.
-    f = {}
-    for l in range(1, m):
-        f[(0, l)] = (Dp[0, l] + w * _h(ML[0, l] / n), (0, l))
+    idx = np.arange(m)
+    # valid transitions i < j < l, j not the last point
+    valid = (idx[:, None, None] < idx[None, :, None]) & (idx[None, :, None] < idx[None, None, :])
+    valid &= (idx[None, :, None] < m - 1)
+    # the entropy term of point j given both neighbours i and l
+    hmid = w * _h_array((MR[:, :, None] + ML[None, :, :]) / n)
+    f = np.full((m, m), INF)
+    f[0, 1:] = Dp[0, 1:] + w * _h_array(ML[0, 1:] / n)
+    parents = []          # parents[t][j, l]: the i chosen when (j, l) was reached
     best = (INF, None)
     c = 2
     while True:
-        for (i, j), (v, chain) in f.items():
-            if j == m - 1:
-                tot = v + w * _h(MR[i, j] / n)
+        for i in range(m - 1):
+            if f[i, m - 1] < INF:
+                tot = f[i, m - 1] + w * _h(MR[i, m - 1] / n)
                 if tot < best[0]:
-                    best = (tot, chain)
+                    best = (tot, _chain(parents, i, m - 1))
         if c == min(smax, m):
             break
-        g = {}
-        for (i, j), (v, chain) in f.items():
-            if j == m - 1:
-                continue
-            for l in range(j + 1, m):
-                cand = v + Dp[j, l] + w * _h((MR[i, j] + ML[j, l]) / n)
-                if (j, l) not in g or cand < g[(j, l)][0]:
-                    g[(j, l)] = (cand, chain + (l,))
-        f = g
+        T = np.where(valid & (f[:, :, None] < INF), (f[:, :, None] + Dp[None, :, :]) + hmid, INF)
+        par = np.argmin(T, axis=0)        # first minimum: lowest i
+        f = np.min(T, axis=0)
+        parents.append(par)
         c += 1
     return best
+
+
+def _chain(parents, i, j):
+    """Indices of the chain whose last two points are (i, j), rebuilt from
+    the parent tables of the layers that led to it."""
+    out = [j, i]
+    for par in reversed(parents):
+        i, j = int(par[i, j]), i
+        out.append(i)
+    return tuple(reversed(out))
+
+
+def _dp_rate_chunk(args):
+    pairs, n, lam, smax = args
+    out = []
+    for Dp, ML, MR in pairs:
+        _, S = dp_minimise(Dp, ML, MR, n, float(n), lam, smax)
+        out.append((S, float(n) * subset_score(Dp, ML, MR, n, S)[1]))
+    return out
+
+
+def solve_bisect_dp(pairs, n, B, smax, iters=40, processes=None):
+    """The bisection of :func:`ecasq.bisect_multiplier` with every block's
+    exact minimiser (:func:`dp_minimise`) at each probed multiplier.
+
+    ``pairs`` lists (Dp, ML, MR) per block.  Returns ``(lam, subsets,
+    rate_bits_total, B_total, probes)``; the rate of a choice is
+    sum_r n H_r(S_r) summed exactly (math.fsum).  ``processes`` > 1 spreads
+    the blocks of each probe over a process pool (same results).
+    """
+    from multiprocessing import get_context
+    from .ecasq import bisect_multiplier
+    R = len(pairs)
+    d = float(n)
+    Btot = float(B) * math.fsum([d] * R)
+    probes = []
+    nchunk = max(1, min(R, 4 * (processes or 1)))
+    bounds = np.linspace(0, R, nchunk + 1).astype(int)
+    chunks = [pairs[bounds[k]:bounds[k + 1]] for k in range(nchunk)]
+    pool = get_context("fork").Pool(processes) if processes and processes > 1 and R > 1 else None
+    try:
+        def rate(lam):
+            args = [(c, n, lam, smax) for c in chunks]
+            res = pool.map(_dp_rate_chunk, args) if pool else [_dp_rate_chunk(a) for a in args]
+            flat = [e for part in res for e in part]
+            rt = math.fsum([t for _, t in flat])
+            probes.append((lam, rt))
+            return rt, [S for S, _ in flat]
+
+        lam, subs, rt = bisect_multiplier(rate, Btot, iters)
+    finally:
+        if pool:
+            pool.close()
+            pool.join()
+    return lam, subs, rt, Btot, probes

@@ -50,6 +50,30 @@ def _eval_exact_chunk(args):
     return out
 
 
+def _eval_pairs_chunk(args):
+    blocks, m_alpha = args
+    R, n = blocks.shape
+    out = []
+    for r in range(R):
+        x = blocks[r]
+        raw = np.sort(x)[exact_dp.alphabet_ranks(n, m_alpha)]
+        A = np.unique(raw)
+        out.append((raw, A) + exact_dp.pair_stats(x, A))
+    return out
+
+
+# Exact search: brute force over the subsets while there are at most this
+# many per block, the pair-state DP beyond (both give the same minimiser).
+EXACT_BRUTE_MAX = 20000
+
+
+def n_subsets(m, smax):
+    """Endpoint-containing subsets of m points with 2..smax points."""
+    if m <= 2:
+        return 1
+    return sum(math.comb(m - 2, k) for k in range(0, min(smax, m) - 1))
+
+
 def _map(fn, chunks, processes):
     if processes and processes > 1 and len(chunks) > 1:
         with get_context("fork").Pool(processes) as pool:
@@ -82,6 +106,14 @@ def eval_exact(blocks, m_alpha, smax, processes=None):
     return [b for r in res for b in r]
 
 
+def eval_pairs(blocks, m_alpha, processes=None):
+    """Alphabet and pair statistics of every block (no subset tables)."""
+    processes = processes or 1
+    chunks = _split(blocks, processes * 4)
+    res = _map(_eval_pairs_chunk, [(c, m_alpha) for c in chunks], processes)
+    return [b for r in res for b in r]
+
+
 def run(blocks, *, search="grids", s=16, alphabet_m=12, B=2.0, mode="bisect",
         iters=40, lam_prev=0.0, eta=1e-3, seed=0, quantize=True, processes=None, weights=None):
     """Admission of ``blocks`` ([R, n] fp64).  Returns a dict of every
@@ -96,6 +128,11 @@ def run(blocks, *, search="grids", s=16, alphabet_m=12, B=2.0, mode="bisect",
         D, H, stats, books = eval_grids(blocks, s, processes)
         out.update(D=D, H=H, stats=stats, books=books)
         Dt, Ht = D, H
+    elif search == "exact_dp" and n_subsets(alphabet_m, s) > EXACT_BRUTE_MAX:
+        ev = eval_pairs(blocks, alphabet_m, processes)
+        out.update(alphabet_raw=np.stack([e[0] for e in ev]), alphabets=[e[1] for e in ev],
+                   pairs=[(e[2], e[3], e[4]) for e in ev], route="dp")
+        Dt = Ht = None
     elif search == "exact_dp":
         ev = eval_exact(blocks, alphabet_m, s, processes)
         Cmax = max(len(e[7]) for e in ev)
@@ -112,7 +149,14 @@ def run(blocks, *, search="grids", s=16, alphabet_m=12, B=2.0, mode="bisect",
     else:
         raise ValueError(search)
 
-    if mode in ("bisect", "bisect_greedy"):
+    if out.get("route") == "dp":
+        if mode != "bisect":
+            raise ValueError("the DP route runs the bisection")
+        lam, subs, rate, Btot, probes = exact_dp.solve_bisect_dp(out["pairs"], n, B, s, iters,
+                                                                 processes)
+        out.update(lam=lam, subsets_chosen=subs, rate_bits=rate, B_total=Btot, probes=probes,
+                   rate_per_entry=rate / (d * R))
+    elif mode in ("bisect", "bisect_greedy"):
         lam, choice, rate, Btot, probes = ecasq.solve_bisect(Dt, Ht, d, B, iters, weights)
         out.update(lam=lam, choice=choice, rate_bits=rate, B_total=Btot, probes=probes,
                    rate_per_entry=rate / (d * R))
@@ -136,6 +180,8 @@ def run(blocks, *, search="grids", s=16, alphabet_m=12, B=2.0, mode="bisect",
     for r in range(R):
         if search == "grids":
             Q = books[r][choice[r]]
+        elif out.get("route") == "dp":
+            Q = out["alphabets"][r][list(out["subsets_chosen"][r])]
         else:
             A = out["alphabets"][r]
             Q = A[list(out["subsets"][r][choice[r]])]
@@ -148,7 +194,9 @@ def run(blocks, *, search="grids", s=16, alphabet_m=12, B=2.0, mode="bisect",
     if search == "exact_dp":
         masks = np.zeros(R, dtype=np.int64)
         for r in range(R):
-            for idx in out["subsets"][r][choice[r]]:
+            S = (out["subsets_chosen"][r] if out.get("route") == "dp"
+                 else out["subsets"][r][choice[r]])
+            for idx in S:
                 masks[r] |= 1 << idx
         out["mask"] = masks
 

@@ -87,3 +87,65 @@ def test_dp_limited_size():
     val, S = exact_dp.dp_minimise(Dp, ML, MR, x.size, 4096.0, 0.0, 3)
     assert val == pytest.approx(Dt.min(), rel=1e-12)
     assert len(S) <= 3
+
+
+def _pairs(x, M):
+    A = exact_dp.alphabet(np.sort(x), M)
+    return A, exact_dp.pair_stats(x, A)
+
+
+@pytest.mark.parametrize("M,smax", [(32, 4), (32, 5), (20, 6), (16, 8)])
+def test_dp_equals_brute_force_larger_alphabets(M, smax):
+    """Alphabets of up to 32 quantiles: the DP's minimum and subset equal
+    brute force over every endpoint-containing subset with |S| <= smax."""
+    d = 4096.0
+    blocks = _blocks(3)
+    rng = np.random.default_rng(5)
+    skewed = np.round(rng.standard_t(3, size=4096), 2)   # heavy tails and ties
+    for x in list(blocks) + [skewed]:
+        A, (Dp, ML, MR) = _pairs(x, M)
+        Dt, Ht, S_list = exact_dp.brute_force_tables(Dp, ML, MR, x.size, smax)
+        for lam in (0.0, 2e-4, 5e-3, 0.2, 1e3):
+            obj = Dt + (lam * d) * Ht
+            bf = int(np.argmin(obj))
+            val, S = exact_dp.dp_minimise(Dp, ML, MR, x.size, d, lam, smax)
+            assert val == pytest.approx(obj[bf], rel=1e-12, abs=1e-12)
+            assert S == S_list[bf] or obj[S_list.index(S)] == pytest.approx(obj[bf], rel=1e-12)
+
+
+def test_dp_chain_is_rebuilt_correctly():
+    """The returned subset scores (by direct per-entry evaluation of its
+    codebook) to the returned DP value."""
+    x = _blocks(1)[0]
+    A, (Dp, ML, MR) = _pairs(x, 24)
+    for lam, smax in ((0.0, 16), (1e-3, 10), (0.05, 7)):
+        val, S = exact_dp.dp_minimise(Dp, ML, MR, x.size, 4096.0, lam, smax)
+        assert S[0] == 0 and S[-1] == A.size - 1 and list(S) == sorted(set(S)) and len(S) <= smax
+        D, H, _ = ecasq.score_codebook(x, A[list(S)])
+        assert val == pytest.approx(D + lam * 4096.0 * H, rel=1e-10)
+
+
+def test_bisection_over_dp_equals_bisection_over_brute_force():
+    """solve_bisect_dp (DP minimisers at every probe) returns the multiplier,
+    subsets and rate of ecasq.solve_bisect over the brute-force tables."""
+    blocks = _blocks(8)
+    M, smax = 14, 6
+    pairs, tables, subsets = [], [], []
+    for x in blocks:
+        A, pr = _pairs(x, M)
+        pairs.append(pr)
+        Dt, Ht, S_list = exact_dp.brute_force_tables(*pr, x.size, smax)
+        tables.append((Dt, Ht))
+        subsets.append(S_list)
+    C = max(t[0].size for t in tables)
+    Dtab = np.full((len(blocks), C), np.inf)
+    Htab = np.zeros((len(blocks), C))
+    for r, (Dt, Ht) in enumerate(tables):
+        Dtab[r, :Dt.size] = Dt
+        Htab[r, :Ht.size] = Ht
+    for B in (1.0, 1.7, 2.4):
+        lam, choice, rate, Btot, _ = ecasq.solve_bisect(Dtab, Htab, 4096.0, B, 40)
+        lam2, subs, rate2, Btot2, _ = exact_dp.solve_bisect_dp(pairs, 4096, B, smax, 40)
+        assert lam2 == lam and Btot2 == Btot
+        assert rate2 == pytest.approx(rate, rel=1e-13) and rate2 <= Btot
+        assert subs == [subsets[r][choice[r]] for r in range(len(blocks))]

@@ -48,6 +48,41 @@ def test_exact_dp_end_to_end():
         assert np.all(np.isin(Q, A))
 
 
+def test_exact_routes_agree(monkeypatch):
+    """The brute-force route and the pair-state DP route of the exact search
+    give the same multiplier, subsets, codebooks and codes (14-point
+    alphabet, |Q| <= 6: 1+12+66+220+495 = 794 subsets per block)."""
+    w = W.FEATURE_GROUP_EXACT_FP32
+    b = oblocks.partition(W.generate(w), w.tokens_per_block, w.dims_per_block)[:10]
+    assert pipeline.n_subsets(14, 6) == 794
+    assert pipeline.n_subsets(12, 8) == 848
+    res = {}
+    for route, limit in (("brute", 10 ** 9), ("dp", 0)):
+        monkeypatch.setattr(pipeline, "EXACT_BRUTE_MAX", limit)
+        res[route] = pipeline.run(b, search="exact_dp", s=6, alphabet_m=14, B=1.8, seed=3)
+    assert res["dp"]["route"] == "dp" and "route" not in res["brute"]
+    assert res["dp"]["lam"] == res["brute"]["lam"] > 0.0
+    assert np.array_equal(res["dp"]["mask"], res["brute"]["mask"])
+    assert res["dp"]["rate_bits"] == pytest.approx(res["brute"]["rate_bits"], rel=1e-13)
+    assert np.array_equal(res["dp"]["words"], res["brute"]["words"])
+
+
+def test_large_alphabet_dp_route():
+    """32-quantile alphabet, |Q| <= 16 (beyond brute force): the budget
+    holds, every codebook holds the alphabet's endpoints and at most 16 of
+    its points, and the masks name the codebook's points."""
+    w = W.FEATURE_GROUP_EXACT_FP32
+    b = oblocks.partition(W.generate(w), w.tokens_per_block, w.dims_per_block)[:6]
+    out = pipeline.run(b, search="exact_dp", s=16, alphabet_m=32, B=2.2, seed=0)
+    assert out["route"] == "dp"
+    assert out["lam"] > 0.0 and out["rate_bits"] <= 2.2 * b.size
+    for r in range(b.shape[0]):
+        A, Q = out["alphabets"][r], out["chosen"][r]
+        assert Q[0] == A[0] and Q[-1] == A[-1] and 2 <= Q.size <= 16
+        idx = [i for i in range(A.size) if int(out["mask"][r]) >> i & 1]
+        assert np.array_equal(A[idx], Q)
+
+
 def test_partition_order_and_canonical_zero():
     x = np.arange(2 * 3 * 64 * 32, dtype=np.float32).reshape(2, 3, 64, 32)
     b = oblocks.partition([x], 32, 16)
