@@ -218,6 +218,37 @@ def decode_stream(torch, kvq, W, steps=200, batches=16):
             "rate_min_max_last_100": [float(np.min(rates[-100:])), float(np.max(rates[-100:]))]}
 
 
+def exact_search(torch, kvq, W, reps=5):
+    """Exact codebook search on the feature-group tensor: the 12-quantile
+    alphabet with |Q| <= 8 and the 32-quantile alphabet with |Q| <= 16.
+    Medians of eval (HIP events) and of the solve call (host clock: it
+    synchronises), with the multiplier and modelled rate."""
+    out = {}
+    t = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in W.generate(W.FEATURE_GROUP_EXACT_FP32)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for w in (W.FEATURE_GROUP_EXACT_FP32, W.FEATURE_GROUP_EXACT_M32):
+        plan = kvq.kvq_plan_blocks(t, w.tokens_per_block, w.dims_per_block, w.s, kvq.KVQ_EXACT_DP,
+                                   w.alphabet_m)
+        buf = kvq.allocate(plan)
+        te, ts = [], []
+        for _ in range(reps + 1):
+            ev[0].record()
+            kvq.kvq_eval_candidates(plan, t, buf["D"], buf["H"], buf["stats"], buf["workspace"])
+            ev[1].record()
+            torch.cuda.synchronize()
+            te.append(ev[0].elapsed_time(ev[1]))
+            t0 = time.perf_counter()
+            lam, rate = kvq.kvq_solve_lambda(plan, buf["D"], buf["H"], buf["stats"], w.B, kvq.KVQ_BISECT,
+                                             w.iters, w.eta, 0.0, buf["choice"], buf["codebook"], buf["m"],
+                                             buf["off"], buf["workspace"])
+            ts.append(1e3 * (time.perf_counter() - t0))
+        out[w.name] = {"alphabet": w.alphabet_m, "max_levels": w.s, "blocks": plan.n_blocks,
+                       "pairs_per_block": plan.n_cand, "eval_ms": float(np.median(te[1:])),
+                       "solve_ms": float(np.median(ts[1:])), "lambda": lam, "rate_bits_per_entry": rate}
+        del buf
+    return out
+
+
 def cpu_baseline(w, tensors, target_s=10.0):
     """The oracle, as it stands, on the first blocks of the workload: eval,
     bisection, quantize+pack and decode, on all host cores."""
@@ -351,6 +382,7 @@ def main():
         log("measuring entropy coding, decode attention and a decode stream")
         extras["extensions"] = extensions(torch, kvq, W, w, plan, dev, buf, stream)
         extras["extensions"]["decode_stream"] = decode_stream(torch, kvq, W)
+        extras["extensions"]["exact_search"] = exact_search(torch, kvq, W)
     rec = {
         "metric": "KV GB/s quantized (fp16 in) and % of HBM roofline at 32-token blocks",
         "value": value, "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,

@@ -73,7 +73,7 @@ typedef int32_t kvq_status;
 #define KVQ_MAX_TENSORS 2
 #define KVQ_MAX_S 16
 #define KVQ_MAX_BLOCK 4096
-#define KVQ_MAX_ALPHABET 12
+#define KVQ_MAX_ALPHABET 32
 
 /* A KV tensor [outer, heads, tokens, dim] in device memory (caller-owned).
    Strides are in elements; every stride must be positive. */
@@ -92,7 +92,7 @@ typedef struct {
     int32_t dims_per_block;   /* head_dim, or the feature-group width */
     int32_t s;                /* codebook size limit |Q| <= s, 2..16 */
     int32_t search;           /* KVQ_GRIDS | KVQ_EXACT_DP */
-    int32_t alphabet_m;       /* KVQ_EXACT_DP alphabet size (<= 12); else 0 */
+    int32_t alphabet_m;       /* KVQ_EXACT_DP alphabet size (2..32); else 0 */
 } kvq_block_spec;
 
 /* Result of kvq_plan_blocks: block geometry and the byte size of every buffer
@@ -156,10 +156,12 @@ kvq_status kvq_plan_blocks(const kvq_tensor* t, int32_t n_tensors,
    KVQ_EXACT_DP: stats[R][alphabet_m] the alphabet order statistics (with
                repeats); with A the sorted distinct alphabet (m points) and
                pair p = index of (i < j) in row-major upper-triangle order of
-               a 12-point alphabet:
-               D[R][66]     distortion of the entries in [A_i, A_j)
+               an alphabet_m-point alphabet, P = plan.n_cand =
+               alphabet_m (alphabet_m - 1) / 2 pairs (pairs past the
+               distinct points hold 0):
+               D[R][P]      distortion of the entries in [A_i, A_j)
                             (closed at the last point) interpolated on A_i, A_j,
-               H[R][66][2]  their masses sent to A_i and to A_j (entries).
+               H[R][P][2]   their masses sent to A_i and to A_j (entries).
    workspace: plan.workspace_bytes of device memory; its status word is
    reset here and set when an entry is NaN or Inf (reported by
    kvq_solve_lambda).  Asynchronous on stream s. */

@@ -284,11 +284,12 @@ eval_alphabet_kernel(Geom g, int alpha_m, int NP, double* __restrict__ D, double
         ap2[tid] = p2;
     }
     __syncthreads();
-    if (tid < kPairs) {
-        // decode pair index -> (i, j)
-        int i = 0, rem = tid;
-        while (rem >= kAlpha - 1 - i) {
-            rem -= kAlpha - 1 - i;
+    const int P = n_pairs(alpha_m);
+    for (int p = tid; p < P; p += kEvalThreads) {
+        // decode pair index -> (i, j) of the alpha_m-point triangle
+        int i = 0, rem = p;
+        while (rem >= alpha_m - 1 - i) {
+            rem -= alpha_m - 1 - i;
             ++i;
         }
         const int j = i + 1 + rem;
@@ -311,9 +312,9 @@ eval_alphabet_kernel(Geom g, int alpha_m, int NP, double* __restrict__ D, double
             interval_terms((double)A[i], (double)A[j], Cn, p1hi - p1lo, p2hi - p2lo, Dp, ML, MR);
             Dp = fmax(Dp, 0.0);
         }
-        D[r * kPairs + tid] = Dp;
-        H[(r * kPairs + tid) * 2 + 0] = ML;
-        H[(r * kPairs + tid) * 2 + 1] = MR;
+        D[r * P + p] = Dp;
+        H[(r * P + p) * 2 + 0] = ML;
+        H[(r * P + p) * 2 + 1] = MR;
     }
 }
 

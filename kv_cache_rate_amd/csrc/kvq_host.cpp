@@ -147,7 +147,7 @@ kvq_status kvq_plan_blocks(const kvq_tensor* t, int32_t nt, const kvq_block_spec
     if (spec->search != KVQ_GRIDS && spec->search != KVQ_EXACT_DP)
         return fail(KVQ_EINVAL, "unknown search mode %d", spec->search);
     if (spec->search == KVQ_EXACT_DP && (spec->alphabet_m < 2 || spec->alphabet_m > KVQ_MAX_ALPHABET))
-        return fail(KVQ_EINVAL, "alphabet_m=%d outside 2..12", spec->alphabet_m);
+        return fail(KVQ_EINVAL, "alphabet_m=%d outside 2..%d", spec->alphabet_m, KVQ_MAX_ALPHABET);
     kvq_plan p;
     memset(&p, 0, sizeof p);
     p.dtype = t[0].dtype;
@@ -188,9 +188,9 @@ kvq_status kvq_plan_blocks(const kvq_tensor* t, int32_t nt, const kvq_block_spec
         p.H_bytes = p.D_bytes;
         max_levels = p.s;
     } else {
-        p.n_cand = kvq::kPairs;
+        p.n_cand = kvq::n_pairs(p.alphabet_m);
         p.n_stats = p.alphabet_m;
-        p.D_bytes = (size_t)R * kvq::kPairs * sizeof(double);
+        p.D_bytes = (size_t)R * p.n_cand * sizeof(double);
         p.H_bytes = 2 * p.D_bytes;
         max_levels = p.s < p.alphabet_m ? p.s : p.alphabet_m;
     }

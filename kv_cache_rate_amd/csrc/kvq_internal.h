@@ -15,8 +15,8 @@ constexpr int kMaxBlock = KVQ_MAX_BLOCK;          // entries per block
 constexpr int kMaxS = KVQ_MAX_S;                  // codebook size limit
 constexpr int kMaxCand = 1 + 2 * (kMaxS - 2);     // 29 grid candidates
 constexpr int kMaxStats = 80;                     // >= 73 distinct quantile ranks
-constexpr int kAlpha = KVQ_MAX_ALPHABET;          // 12
-constexpr int kPairs = kAlpha * (kAlpha - 1) / 2; // 66
+constexpr int kAlpha = KVQ_MAX_ALPHABET;             // 32
+constexpr int kMaxPairs = kAlpha * (kAlpha - 1) / 2; // 496
 constexpr int kMaxLam = 64;                       // multipliers per solve pass
 
 // Device status bits (workspace header).
@@ -284,9 +284,11 @@ __device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t R) {
     return x * q + (x < rem ? x : rem) + idx;
 }
 
-// Index of the pair (i < j) of a 12-point alphabet, row-major upper triangle.
-__host__ __device__ __forceinline__ int pair_index(int i, int j) {
-    return i * (2 * kAlpha - i - 1) / 2 + (j - i - 1);
+// Pairs (i < j) of an M-point alphabet, and the index of one in row-major
+// upper-triangle order.
+__host__ __device__ __forceinline__ int n_pairs(int M) { return M * (M - 1) / 2; }
+__host__ __device__ __forceinline__ int pair_index(int i, int j, int M) {
+    return i * (2 * M - i - 1) / 2 + (j - i - 1);
 }
 
 // Quantile-rank lookup: stats column of rank quantile_rank(j, k, n).

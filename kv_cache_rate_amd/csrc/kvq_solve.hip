@@ -294,145 +294,182 @@ final_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
 
 __device__ __forceinline__ double hbits(double p) { return p > 0.0 ? -p * log2(p) : 0.0; }
 
-// Pair-state dynamic program over the distinct alphabet A (m points):
-// f[i][j] is the best cost of a chain from point 0 whose last two points are
-// i < j, holding the distortion of its closed intervals and the entropy terms
-// of every point before j (a point's frequency needs both neighbours).
-// Rows are updated in place for descending j.  Returns the best objective and
-// the chain's bitmask.
-__device__ double dp_min(const double* Dp, const double* Mlr, int m, int smax, double inv_n,
-                         double w, uint32_t& best_mask) {
-    double f[kAlpha][kAlpha];
-    uint32_t mk[kAlpha][kAlpha];
+constexpr int kDpThreads = 256;
+
+// Pair-state dynamic program over the distinct alphabet A (m points, pairs
+// indexed in the M-point triangle), one workgroup per (block, multiplier):
+//   f_2[0][l]     = Dp(0,l) + w h(ML(0,l)/n)
+//   f_{c+1}[j][l] = min_{i<j} (f_c[i][j] + Dp(j,l)) + w h((MR(i,j) + ML(j,l))/n)
+//   best          = min over c, i of f_c[i][m-1] + w h(MR(i,m-1)/n)
+// with w = lambda n and h(p) = -p log2 p: f_c[i][j] is the best cost of a
+// chain from point 0 with c points ending in i < j, holding the distortion
+// of its closed intervals and the entropy of every point before j (a
+// point's frequency needs both neighbours).  Chains that reach the last
+// point are complete.  Ties: lowest i, and across completions the smallest
+// c, then the lowest i.  One thread per state (j, l) per layer, layers
+// double-buffered in LDS; the chain's points ride along as a bitmask.
+struct DpShared {
+    double Dp[kMaxPairs], ML[kMaxPairs], MR[kMaxPairs];
+    double f[2][kMaxPairs];
+    uint32_t mk[2][kMaxPairs];
+    float A[kAlpha];
+    int m;
+};
+
+__device__ uint32_t dp_block(DpShared& sh, const double* __restrict__ Dg, const double* __restrict__ Mg,
+                             const float* __restrict__ st, int M, int smax, int n, double w) {
+    const int tid = threadIdx.x;
+    const int P = n_pairs(M);
+    const double dn = (double)n;
     const double INF = __builtin_huge_val();
-    if (m <= 1) {
-        best_mask = 1u;
-        return 0.0;
+    for (int p = tid; p < P; p += blockDim.x) {
+        sh.Dp[p] = Dg[p];
+        sh.ML[p] = Mg[2 * p];
+        sh.MR[p] = Mg[2 * p + 1];
+        sh.f[0][p] = INF;
+        sh.mk[0][p] = 0u;
     }
-    for (int i = 0; i < kAlpha; ++i)
-        for (int j = 0; j < kAlpha; ++j) {
-            f[i][j] = INF;
-            mk[i][j] = 0u;
-        }
-    for (int l = 1; l < m; ++l) {
-        const int p = pair_index(0, l);
-        f[0][l] = Dp[p] + w * hbits(Mlr[2 * p] * inv_n);
-        mk[0][l] = 1u | (1u << l);
+    if (tid == 0) {
+        int m = 0;
+        for (int j = 0; j < M; ++j)
+            if (m == 0 || st[j] != sh.A[m - 1]) sh.A[m++] = st[j];
+        sh.m = m;
     }
-    double best = INF;
-    best_mask = 0u;
+    __syncthreads();
+    const int m = sh.m;
+    if (m <= 1) return 1u;
+    for (int l = 1 + tid; l < m; l += blockDim.x) {
+        const int p = pair_index(0, l, M);
+        sh.f[0][p] = sh.Dp[p] + w * hbits(sh.ML[p] / dn);
+        sh.mk[0][p] = 1u | (1u << l);
+    }
+    double best = INF;  // thread 0's running completion
+    uint32_t best_mask = 0u;
     const int cmax = smax < m ? smax : m;
+    int cur = 0;
     for (int c = 2;; ++c) {
-        for (int i = 0; i < m - 1; ++i) {
-            if (f[i][m - 1] < INF) {
-                const double tot = f[i][m - 1] + w * hbits(Mlr[2 * pair_index(i, m - 1) + 1] * inv_n);
-                if (tot < best) {
-                    best = tot;
-                    best_mask = mk[i][m - 1];
+        __syncthreads();
+        if (tid == 0) {
+            for (int i = 0; i < m - 1; ++i) {
+                const int p = pair_index(i, m - 1, M);
+                const double fv = sh.f[cur][p];
+                if (fv < INF) {
+                    const double tot = fv + w * hbits(sh.MR[p] / dn);
+                    if (tot < best) {
+                        best = tot;
+                        best_mask = sh.mk[cur][p];
+                    }
                 }
             }
         }
         if (c >= cmax) break;
-        for (int j = m - 2; j >= 1; --j) {
-            for (int l = m - 1; l > j; --l) {
-                const int pjl = pair_index(j, l);
-                const double mass_right = Mlr[2 * pjl];
-                double bv = INF;
-                uint32_t bm = 0u;
+        const int nx = cur ^ 1;
+        // states (j, l): 1 <= j <= m - 2, j < l <= m - 1; every other entry
+        // of the next layer is unreachable
+        for (int p = tid; p < P; p += blockDim.x) {
+            int j = 0, rem = p;
+            while (rem >= M - 1 - j) {
+                rem -= M - 1 - j;
+                ++j;
+            }
+            const int l = j + 1 + rem;
+            double bv = INF;
+            uint32_t bm = 0u;
+            if (j >= 1 && l < m) {
+                const double Djl = sh.Dp[p], MLjl = sh.ML[p];
                 for (int i = 0; i < j; ++i) {
-                    if (f[i][j] < INF) {
-                        const double v = f[i][j] +
-                                         w * hbits((Mlr[2 * pair_index(i, j) + 1] + mass_right) * inv_n);
+                    const int q = pair_index(i, j, M);
+                    const double fv = sh.f[cur][q];
+                    if (fv < INF) {
+                        const double v = (fv + Djl) + w * hbits((sh.MR[q] + MLjl) / dn);
                         if (v < bv) {
                             bv = v;
-                            bm = mk[i][j];
+                            bm = sh.mk[cur][q];
                         }
                     }
                 }
-                f[j][l] = bv < INF ? bv + Dp[pjl] : INF;
-                mk[j][l] = bm | (1u << l);
             }
+            sh.f[nx][p] = bv;
+            sh.mk[nx][p] = bv < INF ? (bm | (1u << l)) : 0u;
         }
-        for (int l = 0; l < kAlpha; ++l) f[0][l] = INF;
+        cur = nx;
     }
-    return best;
+    return best_mask;  // valid in thread 0
 }
 
-// Entropy (bits per entry) of the subset given by mask.
-__device__ double subset_entropy(const double* Mlr, int m, uint32_t mask, double inv_n) {
-    int prev = -1;
-    double Hs = 0.0;
+// Entropy (bits per entry) of the subset given by mask: each point's mass
+// is what the interval on its left sends right plus what the interval on
+// its right sends left.
+__device__ double subset_entropy(const DpShared& sh, int M, uint32_t mask, int n) {
+    const int m = sh.m;
     int pts[kAlpha];
     int k = 0;
     for (int i = 0; i < m; ++i)
         if (mask & (1u << i)) pts[k++] = i;
     if (k <= 1) return 0.0;
+    double Hs = 0.0;
     for (int t = 0; t < k; ++t) {
         double mass = 0.0;
-        if (t > 0) mass += Mlr[2 * pair_index(pts[t - 1], pts[t]) + 1];
-        if (t + 1 < k) mass += Mlr[2 * pair_index(pts[t], pts[t + 1])];
-        Hs += hbits(mass * inv_n);
+        if (t > 0) mass += sh.MR[pair_index(pts[t - 1], pts[t], M)];
+        if (t + 1 < k) mass += sh.ML[pair_index(pts[t], pts[t + 1], M)];
+        Hs += hbits(mass / (double)n);
     }
-    (void)prev;
     return Hs;
 }
 
-__device__ int distinct_alphabet(const float* st, int alpha_m, float* A) {
-    int m = 0;
-    for (int j = 0; j < alpha_m; ++j)
-        if (m == 0 || st[j] != A[m - 1]) A[m++] = st[j];
-    return m;
-}
-
-__global__ void __launch_bounds__(64)
+// Rate of every multiplier of the pass: workgroup (block r, multiplier j).
+__global__ void __launch_bounds__(kDpThreads)
 rates_dp_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr,
                 const float* __restrict__ stats, int64_t R, int alpha_m, int smax, int n,
                 int shift, WsHeader* h) {
-    const int nlam = h->nlam;
-    if (h->done || nlam == 0) return;
+    __shared__ DpShared sh;
+    const int j = blockIdx.y;
+    if (h->done || j >= h->nlam) return;
     const int64_t r = blockIdx.x;
-    const int j = threadIdx.x;
-    if (j >= nlam) return;
-    float A[kAlpha];
-    const int m = distinct_alphabet(stats + r * alpha_m, alpha_m, A);
-    const double inv_n = 1.0 / (double)n;
+    const int P = n_pairs(alpha_m);
     const double w = h->lam[j] * (double)n;
-    uint32_t mask;
-    dp_min(Dp + r * kPairs, Mlr + r * kPairs * 2, m, smax, inv_n, w, mask);
-    const double Hs = subset_entropy(Mlr + r * kPairs * 2, m, mask, inv_n);
-    atomicAdd(&h->sums[j], rate_fx((double)n, Hs, shift));
+    const uint32_t mask = dp_block(sh, Dp + r * P, Mlr + r * P * 2, stats + r * alpha_m, alpha_m,
+                                   smax, n, w);
+    if (threadIdx.x == 0) {
+        const double Hs = subset_entropy(sh, alpha_m, mask, n);
+        atomicAdd(&h->sums[j], rate_fx((double)n, Hs, shift));
+    }
 }
 
-__global__ void __launch_bounds__(kSolveThreads)
+// The blocks' choice at the final multiplier: workgroup = block.
+__global__ void __launch_bounds__(kDpThreads)
 final_dp_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr,
                 const float* __restrict__ stats, int64_t R, int alpha_m, int smax, int s, int n,
                 int shift, WsHeader* h, int32_t* __restrict__ choice, float* __restrict__ codebook,
                 uint8_t* __restrict__ m_out, uint64_t* __restrict__ off) {
-    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (r == 0) off[0] = 0;
-    if (r >= R) return;
+    __shared__ DpShared sh;
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (r == 0 && tid == 0) off[0] = 0;
     if (h->err) {
-        choice[r] = -1;
-        m_out[r] = 1;
-        for (int j = 0; j < s; ++j) codebook[r * s + j] = 0.0f;
-        off[r + 1] = 0;
+        if (tid == 0) {
+            choice[r] = -1;
+            m_out[r] = 1;
+            off[r + 1] = 0;
+        }
+        for (int j = tid; j < s; j += blockDim.x) codebook[r * s + j] = 0.0f;
         return;
     }
-    float A[kAlpha];
-    const int m = distinct_alphabet(stats + r * alpha_m, alpha_m, A);
-    const double inv_n = 1.0 / (double)n;
+    const int P = n_pairs(alpha_m);
     const double w = h->lam_final * (double)n;
-    uint32_t mask;
-    dp_min(Dp + r * kPairs, Mlr + r * kPairs * 2, m, smax, inv_n, w, mask);
-    const double Hs = subset_entropy(Mlr + r * kPairs * 2, m, mask, inv_n);
-    atomicAdd(&h->rate_final, rate_fx((double)n, Hs, shift));
-    int k = 0;
-    for (int i = 0; i < m; ++i)
-        if (mask & (1u << i)) codebook[r * s + k++] = A[i];
-    for (int j = k; j < s; ++j) codebook[r * s + j] = 0.0f;
-    choice[r] = (int32_t)mask;
-    m_out[r] = (uint8_t)k;
-    off[r + 1] = ((uint64_t)n * (uint64_t)code_width(k) + 31u) / 32u;
+    const uint32_t mask = dp_block(sh, Dp + r * P, Mlr + r * P * 2, stats + r * alpha_m, alpha_m,
+                                   smax, n, w);
+    if (tid == 0) {
+        const double Hs = subset_entropy(sh, alpha_m, mask, n);
+        atomicAdd(&h->rate_final, rate_fx((double)n, Hs, shift));
+        int k = 0;
+        for (int i = 0; i < sh.m; ++i)
+            if (mask & (1u << i)) codebook[r * s + k++] = sh.A[i];
+        for (int j = k; j < s; ++j) codebook[r * s + j] = 0.0f;
+        choice[r] = (int32_t)mask;
+        m_out[r] = (uint8_t)k;
+        off[r + 1] = ((uint64_t)n * (uint64_t)code_width(k) + 31u) / 32u;
+    }
 }
 
 // --------------------------------------------------------- offsets scan ----
@@ -655,13 +692,18 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
         Bfx >= 18446744073709551615.0 ? ~0ull : (unsigned long long)floor(Bfx);
     hipLaunchKernelGGL(solve_init_kernel, dim3(1), dim3(64), 0, st, h, mode, lam_in, Btot_fx, iters);
     const unsigned grid = (unsigned)((R + kSolveThreads - 1) / kSolveThreads);
+    // exact DP: one thread per pair state, in whole waves
+    const int dp_pairs = p.search == KVQ_EXACT_DP ? n_pairs(p.alphabet_m) : 0;
+    const int dp_waves = (dp_pairs + 63) / 64;
+    const unsigned dp_threads = dp_waves < 1 ? 64u : (dp_waves > kDpThreads / 64 ? (unsigned)kDpThreads
+                                                                                : 64u * dp_waves);
     auto rates_pass = [&]() {
         if (p.search == KVQ_GRIDS) {
             hipLaunchKernelGGL(rates_grids_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, wgt,
                                R, p.n_cand, (double)n, shift, h);
         } else {
-            hipLaunchKernelGGL(rates_dp_kernel, dim3((unsigned)R), dim3(64), 0, st, D, H, stats, R,
-                               p.alphabet_m, p.s, n, shift, h);
+            hipLaunchKernelGGL(rates_dp_kernel, dim3((unsigned)R, kMaxLam - 1), dim3(dp_threads), 0, st,
+                               D, H, stats, R, p.alphabet_m, p.s, n, shift, h);
         }
         hipLaunchKernelGGL(solve_select_kernel, dim3(1), dim3(64), 0, st, h);
     };
@@ -683,7 +725,7 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
         hipLaunchKernelGGL(final_grids_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, wgt, stats,
                            R, p.n_cand, p.s, n, shift, rt, h, choice, codebook, m, off);
     } else {
-        hipLaunchKernelGGL(final_dp_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, stats, R,
+        hipLaunchKernelGGL(final_dp_kernel, dim3((unsigned)R), dim3(dp_threads), 0, st, D, H, stats, R,
                            p.alphabet_m, p.s, p.s, n, shift, h, choice, codebook, m, off);
     }
     if (mode == KVQ_BISECT_GREEDY && p.search == KVQ_GRIDS) {

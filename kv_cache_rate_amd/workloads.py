@@ -112,7 +112,17 @@ FEATURE_GROUP_EXACT_FP32 = Workload(
 
 WORKLOADS = (TINY_K_FP32, PREFILL_KV_FP16, DECODE_ADMIT_FP16,
              LONG_CONTEXT_KV_FP16, FEATURE_GROUP_EXACT_FP32)
-BY_NAME = {w.name: w for w in WORKLOADS}
+
+# The feature-group workload (same tensor) with the exact search widened to
+# a 32-quantile alphabet and codebooks of up to 16 points.
+FEATURE_GROUP_EXACT_M32 = Workload(
+    name="feature_group_exact_m32_fp32", index=5,
+    tensors=(("X", (1, 8, 8192, 128)),), dtype="f32",
+    tokens_per_block=256, dims_per_block=16, s=16, search="exact_dp",
+    B=2.5, mode="bisect", seed=0, alphabet_m=32,
+    note="feature-group tensor; exact search over a 32-quantile alphabet, |Q| <= 16")
+
+BY_NAME = {w.name: w for w in WORKLOADS + (FEATURE_GROUP_EXACT_M32,)}
 
 
 def _threads():

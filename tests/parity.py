@@ -17,6 +17,7 @@ import numpy as np
 
 from oracle import blocks as oblocks
 from oracle import codes as ocodes
+from oracle import exact_dp
 from oracle import pipeline
 
 D_RTOL = 1e-4
@@ -96,6 +97,7 @@ def compare_tables(g, o, search):
         assert np.array_equal(g["stats"].astype(np.float64), o["stats"]), "order statistics differ"
     else:
         R = g["D"].shape[0]
+        M = g["stats"].shape[1]  # alphabet size of the pair triangle
         eD = 0.0
         eM = 0.0
         for r in range(R):
@@ -103,7 +105,7 @@ def compare_tables(g, o, search):
             m = o["alphabets"][r].size
             for i in range(m):
                 for j in range(i + 1, m):
-                    p = i * (2 * 12 - i - 1) // 2 + (j - i - 1)
+                    p = i * (2 * M - i - 1) // 2 + (j - i - 1)
                     fl = 1e-9 * max(Dp.max(), 1e-300) / D_RTOL
                     eD = max(eD, abs(g["D"][r, p] - Dp[i, j]) / max(abs(Dp[i, j]), fl))
                     eM = max(eM, abs(g["H"][r, p, 0] - ML[i, j]) / max(abs(ML[i, j]), 1e-9 / D_RTOL))
@@ -122,6 +124,8 @@ def compare_choice(g, o, lam, d, weights=None):
     agree = np.zeros(R, dtype=bool)
     ties = 0
     max_gap = 0.0
+    if o.get("route") == "dp":
+        return compare_choice_dp(g, o, lam, d)
     Dw = o["D"] if weights is None else np.asarray(weights, dtype=np.float64)[:, None] * o["D"]
     obj = Dw + (lam * d) * o["H"]
     for r in range(R):
@@ -133,8 +137,8 @@ def compare_choice(g, o, lam, d, weights=None):
             continue
         oc = o["choice"][r]
         if "subsets" in o:
-            mask = int(g["choice"][r])
-            S = tuple(i for i in range(12) if mask >> i & 1)
+            mask = int(g["choice"][r]) & 0xFFFFFFFF
+            S = tuple(i for i in range(32) if mask >> i & 1)
             cand = o["subsets"][r].index(S)
             Qc = o["alphabets"][r][list(S)]
         else:
@@ -142,6 +146,44 @@ def compare_choice(g, o, lam, d, weights=None):
             Qc = o["books"][r][cand]
         assert np.array_equal(Qc, Qg), f"block {r}: GPU codebook is not candidate {cand}"
         gap = (obj[r, cand] - obj[r, oc]) / max(abs(obj[r, oc]), 1e-300)
+        assert gap < TIE_RTOL, f"block {r}: objective gap {gap} is not a tie"
+        ties += 1
+        max_gap = max(max_gap, gap)
+    return agree, ties, max_gap
+
+
+def subset_of_mask(mask):
+    mask = int(mask) & 0xFFFFFFFF
+    return tuple(i for i in range(32) if mask >> i & 1)
+
+
+def compare_choice_dp(g, o, lam, d, blocks=None):
+    """Exact search solved by the oracle's DP route: the GPU's subset (its
+    bitmask) equals the oracle's, except documented ties whose objectives
+    D + lam d H (scored from the oracle's pair statistics) differ by <
+    TIE_RTOL relative.  ``blocks`` restricts the check to those block
+    indices (the oracle's lists then hold those blocks in that order)."""
+    rows = range(g["m"].shape[0]) if blocks is None else blocks
+    agree = np.zeros(g["m"].shape[0], dtype=bool)
+    ties = 0
+    max_gap = 0.0
+    n = int(o["n"])
+    for k, r in enumerate(rows):
+        kk = r if blocks is None else k
+        Sg = subset_of_mask(g["choice"][r])
+        So = tuple(o["subsets_chosen"][kk])
+        A = o["alphabets"][kk]
+        mg = int(g["m"][r])
+        assert mg == len(Sg) and np.array_equal(g["codebook"][r, :mg].astype(np.float64), A[list(Sg)]), \
+            f"block {r}: codebook is not the masked alphabet points"
+        if Sg == So:
+            agree[r] = True
+            continue
+        Dp, ML, MR = o["pairs"][kk]
+        Dg_, Hg_ = exact_dp.subset_score(Dp, ML, MR, n, Sg)
+        Do_, Ho_ = exact_dp.subset_score(Dp, ML, MR, n, So)
+        og, oo = Dg_ + (lam * d) * Hg_, Do_ + (lam * d) * Ho_
+        gap = (og - oo) / max(abs(oo), 1e-300)
         assert gap < TIE_RTOL, f"block {r}: objective gap {gap} is not a tie"
         ties += 1
         max_gap = max(max_gap, gap)

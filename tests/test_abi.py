@@ -72,6 +72,7 @@ def test_plan_sizes(L, w):
         assert p.D_bytes == w.n_blocks * p.n_cand * 8
     else:
         assert p.n_cand == 66 and p.n_stats == 12
+        assert p.D_bytes == w.n_blocks * 66 * 8 and p.H_bytes == 2 * p.D_bytes
     assert p.max_code_words == w.n_blocks * (4096 * (w.s - 1).bit_length() // 32)
     assert p.codebook_bytes == w.n_blocks * w.s * 4
     assert p.offsets_bytes == (w.n_blocks + 1) * 8
@@ -92,9 +93,21 @@ def test_plan_rejects_bad_arguments(L):
     with pytest.raises(kvq.KvqError):
         kvq.kvq_plan_blocks([t, t.astype(np.float32)], 32, 128, 16)  # dtype mismatch
     with pytest.raises(kvq.KvqError):
-        kvq.kvq_plan_blocks([t], 32, 128, 8, kvq.KVQ_EXACT_DP, 13)  # alphabet > 12
+        kvq.kvq_plan_blocks([t], 32, 128, 8, kvq.KVQ_EXACT_DP, 33)  # alphabet > 32
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_plan_blocks([t], 32, 128, 8, kvq.KVQ_EXACT_DP, 1)  # alphabet < 2
     with pytest.raises(ValueError):
         kvq.kvq_plan_blocks([t.astype(np.float64)], 32, 128, 16)
+
+
+def test_plan_larger_alphabet(L):
+    """A 32-point alphabet has 496 pairs; the tables scale with it."""
+    t = np.zeros((1, 8, 8192, 128), dtype=np.float32)
+    p = kvq.kvq_plan_blocks([t], 256, 16, 16, kvq.KVQ_EXACT_DP, 32)
+    assert p.n_cand == 32 * 31 // 2 == 496 and p.n_stats == 32
+    assert p.D_bytes == 2048 * 496 * 8 and p.H_bytes == 2 * p.D_bytes
+    assert p.stats_bytes == 2048 * 32 * 4
+    assert p.max_code_words == 2048 * (4096 * 4 // 32)
 
 
 def test_calls_validate_before_launch(L):
