@@ -194,17 +194,22 @@ def _chain(parents, i, j):
 
 
 def _dp_rate_chunk(args):
-    pairs, n, lam, smax = args
+    pairs, n, lam, smax, width = args
     out = []
     for Dp, ML, MR in pairs:
-        _, S = dp_minimise(Dp, ML, MR, n, float(n), lam, smax)
+        if width is None:
+            _, S = dp_minimise(Dp, ML, MR, n, float(n), lam, smax)
+        else:
+            _, S = beam_minimise(Dp, ML, MR, n, float(n), lam, smax, width)
         out.append((S, float(n) * subset_score(Dp, ML, MR, n, S)[1]))
     return out
 
 
-def solve_bisect_dp(pairs, n, B, smax, iters=40, processes=None):
+def solve_bisect_dp(pairs, n, B, smax, iters=40, processes=None, width=None):
     """The bisection of :func:`ecasq.bisect_multiplier` with every block's
-    exact minimiser (:func:`dp_minimise`) at each probed multiplier.
+    minimiser at each probed multiplier: the exact pair-state DP
+    (:func:`dp_minimise`), or the beam search (:func:`beam_minimise`) of
+    the given ``width``.
 
     ``pairs`` lists (Dp, ML, MR) per block.  Returns ``(lam, subsets,
     rate_bits_total, B_total, probes)``; the rate of a choice is
@@ -223,7 +228,7 @@ def solve_bisect_dp(pairs, n, B, smax, iters=40, processes=None):
     pool = get_context("fork").Pool(processes) if processes and processes > 1 and R > 1 else None
     try:
         def rate(lam):
-            args = [(c, n, lam, smax) for c in chunks]
+            args = [(c, n, lam, smax, width) for c in chunks]
             res = pool.map(_dp_rate_chunk, args) if pool else [_dp_rate_chunk(a) for a in args]
             flat = [e for part in res for e in part]
             rt = math.fsum([t for _, t in flat])
@@ -236,3 +241,57 @@ def solve_bisect_dp(pairs, n, B, smax, iters=40, processes=None):
             pool.close()
             pool.join()
     return lam, subs, rt, Btot, probes
+
+
+def _lex_key(chain):
+    return (len(chain), chain)
+
+
+def beam_minimise(Dp, ML, MR, n, d, lam, smax, width):
+    """Beam search over ordered codepoints for min_S D(S) + lam d H(S).
+
+    Codebooks grow left to right over the ordered alphabet.  A partial
+    chain (0, ..., j, l) is scored with the cost the DP carries: the
+    distortion of its closed intervals and the entropy terms of every point
+    before its last (w = lam d, h(p) = -p log2 p):
+
+        cost(0, l)          = Dp[0, l] + w h(ML[0, l] / n)
+        cost(..., i, j, l)  = (cost(..., i, j) + Dp[j, l]) + w h((MR[i, j] + ML[j, l]) / n)
+        total(..., j, m-1)  = cost(..., j, m-1) + w h(MR[j, m-1] / n)
+
+    The beam: chains with the same number of points that end at the same
+    codepoint compete, and only the ``width`` cheapest of each such group
+    (ties to the lexicographically smaller chain) are extended, by every
+    later codepoint, up to ``smax`` points.  Every chain that reaches the
+    last point is complete and scored.  Returns ``(best_total,
+    best_chain)``, ties to the shorter, then the lexicographically smaller
+    chain.  With an unbounded width every chain is enumerated (brute force);
+    with the DP's state (the last two points) in place of the beam it would
+    be :func:`dp_minimise`.
+    """
+    m = Dp.shape[0]
+    if m == 1:
+        return 0.0, (0,)
+    w = lam * d
+    best = (math.inf, None)
+    arrivals = {}  # end point -> [(cost, chain)] of the current chain length
+    for l in range(1, m):
+        arrivals.setdefault(l, []).append((Dp[0, l] + w * _h(ML[0, l] / n), (0, l)))
+    length = 2
+    while True:
+        for cost, chain in arrivals.get(m - 1, []):
+            tot = cost + w * _h(MR[chain[-2], m - 1] / n)
+            if best[1] is None or (tot, _lex_key(chain)) < (best[0], _lex_key(best[1])):
+                best = (tot, chain)
+        if length >= min(smax, m):
+            break
+        nxt = {}
+        for j in range(1, m - 1):
+            for cost, chain in sorted(arrivals.get(j, []))[:width]:
+                i = chain[-2]
+                for l in range(j + 1, m):
+                    c2 = (cost + Dp[j, l]) + w * _h((MR[i, j] + ML[j, l]) / n)
+                    nxt.setdefault(l, []).append((c2, chain + (l,)))
+        arrivals = nxt
+        length += 1
+    return best

@@ -115,12 +115,17 @@ def eval_pairs(blocks, m_alpha, processes=None):
 
 
 def run(blocks, *, search="grids", s=16, alphabet_m=12, B=2.0, mode="bisect",
-        iters=40, lam_prev=0.0, eta=1e-3, seed=0, quantize=True, processes=None, weights=None):
+        iters=40, lam_prev=0.0, eta=1e-3, seed=0, quantize=True, processes=None, weights=None,
+        beam_width=None):
     """Admission of ``blocks`` ([R, n] fp64).  Returns a dict of every
     intermediate and final result (see the keys below).  ``weights`` ([R])
-    weights each block's distortion in the dual choice (grid search only)."""
+    weights each block's distortion in the dual choice (grid search only).
+    ``search``: "grids", "exact_dp" (brute force or the DP, same minimiser)
+    or "beam" (beam search of ``beam_width`` over the same alphabet)."""
     if weights is not None and search != "grids":
         raise ValueError("distortion weights apply to the grid search")
+    if search == "beam" and not (beam_width and beam_width >= 1):
+        raise ValueError("the beam search needs beam_width >= 1")
     R, n = blocks.shape
     d = float(n)
     out = {"n": n, "R": R}
@@ -128,10 +133,10 @@ def run(blocks, *, search="grids", s=16, alphabet_m=12, B=2.0, mode="bisect",
         D, H, stats, books = eval_grids(blocks, s, processes)
         out.update(D=D, H=H, stats=stats, books=books)
         Dt, Ht = D, H
-    elif search == "exact_dp" and n_subsets(alphabet_m, s) > EXACT_BRUTE_MAX:
+    elif search == "beam" or (search == "exact_dp" and n_subsets(alphabet_m, s) > EXACT_BRUTE_MAX):
         ev = eval_pairs(blocks, alphabet_m, processes)
         out.update(alphabet_raw=np.stack([e[0] for e in ev]), alphabets=[e[1] for e in ev],
-                   pairs=[(e[2], e[3], e[4]) for e in ev], route="dp")
+                   pairs=[(e[2], e[3], e[4]) for e in ev], route="dp" if search == "exact_dp" else "beam")
         Dt = Ht = None
     elif search == "exact_dp":
         ev = eval_exact(blocks, alphabet_m, s, processes)
@@ -149,11 +154,12 @@ def run(blocks, *, search="grids", s=16, alphabet_m=12, B=2.0, mode="bisect",
     else:
         raise ValueError(search)
 
-    if out.get("route") == "dp":
+    if out.get("route") in ("dp", "beam"):
         if mode != "bisect":
-            raise ValueError("the DP route runs the bisection")
-        lam, subs, rate, Btot, probes = exact_dp.solve_bisect_dp(out["pairs"], n, B, s, iters,
-                                                                 processes)
+            raise ValueError("the DP and beam routes run the bisection")
+        lam, subs, rate, Btot, probes = exact_dp.solve_bisect_dp(
+            out["pairs"], n, B, s, iters, processes,
+            beam_width if out["route"] == "beam" else None)
         out.update(lam=lam, subsets_chosen=subs, rate_bits=rate, B_total=Btot, probes=probes,
                    rate_per_entry=rate / (d * R))
     elif mode in ("bisect", "bisect_greedy"):
@@ -180,7 +186,7 @@ def run(blocks, *, search="grids", s=16, alphabet_m=12, B=2.0, mode="bisect",
     for r in range(R):
         if search == "grids":
             Q = books[r][choice[r]]
-        elif out.get("route") == "dp":
+        elif out.get("route") in ("dp", "beam"):
             Q = out["alphabets"][r][list(out["subsets_chosen"][r])]
         else:
             A = out["alphabets"][r]
@@ -191,10 +197,10 @@ def run(blocks, *, search="grids", s=16, alphabet_m=12, B=2.0, mode="bisect",
     widths = np.array([_codes.code_width(k) for k in m], dtype=np.int64)
     out.update(codebook=book, m=m, width=widths, chosen=chosen,
                offsets=_codes.offsets(n, widths))
-    if search == "exact_dp":
+    if search in ("exact_dp", "beam"):
         masks = np.zeros(R, dtype=np.int64)
         for r in range(R):
-            S = (out["subsets_chosen"][r] if out.get("route") == "dp"
+            S = (out["subsets_chosen"][r] if out.get("route") in ("dp", "beam")
                  else out["subsets"][r][choice[r]])
             for idx in S:
                 masks[r] |= 1 << idx

@@ -149,3 +149,107 @@ def test_bisection_over_dp_equals_bisection_over_brute_force():
         assert lam2 == lam and Btot2 == Btot
         assert rate2 == pytest.approx(rate, rel=1e-13) and rate2 <= Btot
         assert subs == [subsets[r][choice[r]] for r in range(len(blocks))]
+
+
+# ---- beam search over ordered codepoints ---------------------------------
+
+def _h(p):
+    return -p * math.log2(p) if p > 0 else 0.0
+
+
+def test_beam_hand_example():
+    """Five points, |S| <= 4, n = d = 1, lambda = 1 (w = 1).  Distortions are
+    10 on every pair except Dp(0,1) = Dp(0,2) = Dp(1,3) = Dp(3,4) = 0 and
+    Dp(2,3) = 0.6, so only the chains (0,1,3,4) and (0,2,3,4) stay below 10.
+    Masses: ML(0,1) = ML(0,2) = 0.1, ML(1,3) = 0.2, MR(1,3) = 0.07,
+    MR(2,3) = 0.6, ML(3,4) = 0.3, MR(3,4) = 0.2, all others 0.
+
+    Both chains reach the group (3 points, ending at point 3):
+      cost(0,1,3) = h(0.1) + 0 + h(0 + 0.2)   = 0.3322 + 0.4644 = 0.7966
+      cost(0,2,3) = h(0.1) + 0.6 + h(0 + 0)   = 0.3322 + 0.6    = 0.9322
+    width 1 keeps (0,1,3) and completes it:
+      total(0,1,3,4) = 0.7966 + h(0.07 + 0.3) + h(0.2) = 0.7966 + 0.5307 + 0.4644
+    width 2 also completes (0,2,3,4), which wins:
+      total(0,2,3,4) = 0.9322 + h(0.6 + 0.3) + h(0.2)  = 0.9322 + 0.1368 + 0.4644
+    and the exact DP agrees with width 2."""
+    m = 5
+    Dp = np.full((m, m), 10.0)
+    ML = np.zeros((m, m))
+    MR = np.zeros((m, m))
+    Dp[0, 1] = Dp[0, 2] = Dp[1, 3] = Dp[3, 4] = 0.0
+    Dp[2, 3] = 0.6
+    ML[0, 1] = ML[0, 2] = 0.1
+    ML[1, 3], MR[1, 3] = 0.2, 0.07
+    MR[2, 3] = 0.6
+    ML[3, 4], MR[3, 4] = 0.3, 0.2
+    t1 = (_h(0.1) + 0.0 + _h(0.2)) + 0.0 + _h(0.37) + _h(0.2)
+    t2 = (_h(0.1) + 0.6 + 0.0) + 0.0 + _h(0.9) + _h(0.2)
+    assert t2 < t1 < 10.0
+    v1, S1 = exact_dp.beam_minimise(Dp, ML, MR, 1, 1.0, 1.0, 4, 1)
+    v2, S2 = exact_dp.beam_minimise(Dp, ML, MR, 1, 1.0, 1.0, 4, 2)
+    vd, Sd = exact_dp.dp_minimise(Dp, ML, MR, 1, 1.0, 1.0, 4)
+    assert S1 == (0, 1, 3, 4) and v1 == pytest.approx(t1, rel=1e-12)
+    assert S2 == (0, 2, 3, 4) and v2 == pytest.approx(t2, rel=1e-12)
+    assert Sd == S2 and vd == pytest.approx(t2, rel=1e-12)
+
+
+@pytest.mark.parametrize("M,smax", [(12, 8), (20, 5), (9, 9)])
+def test_beam_unbounded_is_brute_force(M, smax):
+    """With no pruning the beam enumerates every chain: it returns brute
+    force's minimum and, on exact ties, its subset."""
+    d = 4096.0
+    for x in _blocks(3):
+        A, (Dp, ML, MR) = _pairs(x, M)
+        Dt, Ht, S_list = exact_dp.brute_force_tables(Dp, ML, MR, x.size, smax)
+        for lam in (0.0, 1e-3, 0.05, 10.0):
+            obj = Dt + (lam * d) * Ht
+            bf = int(np.argmin(obj))
+            val, S = exact_dp.beam_minimise(Dp, ML, MR, x.size, d, lam, smax, 10 ** 9)
+            assert val == pytest.approx(obj[bf], rel=1e-12, abs=1e-12)
+            assert S == S_list[bf] or obj[S_list.index(S)] == pytest.approx(obj[bf], rel=1e-12)
+
+
+@pytest.mark.parametrize("width", [1, 2, 4])
+def test_beam_value_is_its_codebook_score(width):
+    """The beam's value is the directly scored objective of the codebook it
+    returns (per-entry evaluation), never below the exact optimum, and the
+    codebook is an endpoint-containing subset within the size limit."""
+    x = _blocks(2)[1]
+    A, (Dp, ML, MR) = _pairs(x, 32)
+    for lam, smax in ((0.0, 16), (2e-3, 12), (0.1, 6)):
+        val, S = exact_dp.beam_minimise(Dp, ML, MR, x.size, 4096.0, lam, smax, width)
+        assert S[0] == 0 and S[-1] == A.size - 1 and list(S) == sorted(set(S)) and len(S) <= smax
+        D, H, _ = ecasq.score_codebook(x, A[list(S)])
+        assert val == pytest.approx(D + lam * 4096.0 * H, rel=1e-10)
+        opt, _ = exact_dp.dp_minimise(Dp, ML, MR, x.size, 4096.0, lam, smax)
+        assert val >= opt * (1 - 1e-12)
+
+
+def test_beam_width_two_is_exact_on_feature_groups():
+    """On the feature-group blocks with the 12-quantile alphabet and
+    |Q| <= 8, a beam of width 2 finds the exact minimiser at every tested
+    multiplier (width 1 already misses some)."""
+    misses1 = 0
+    for x in _blocks(6):
+        A, (Dp, ML, MR) = _pairs(x, 12)
+        for lam in (0.0, 1e-3, 0.05, 1.0):
+            _, Sd = exact_dp.dp_minimise(Dp, ML, MR, x.size, 4096.0, lam, 8)
+            _, S2 = exact_dp.beam_minimise(Dp, ML, MR, x.size, 4096.0, lam, 8, 2)
+            _, S1 = exact_dp.beam_minimise(Dp, ML, MR, x.size, 4096.0, lam, 8, 1)
+            assert S2 == Sd
+            misses1 += S1 != Sd
+    assert misses1 > 0
+
+
+def test_beam_bisection_route():
+    """The pipeline's beam route: budget met, masks name the codebooks, and
+    an unbounded width reproduces the exact route's multiplier and subsets."""
+    w = W.FEATURE_GROUP_EXACT_FP32
+    b = oblocks.partition(W.generate(w), w.tokens_per_block, w.dims_per_block)[:6]
+    from oracle import pipeline
+    ob = pipeline.run(b, search="beam", s=8, alphabet_m=12, B=2.0, beam_width=10 ** 9, seed=0)
+    oe = pipeline.run(b, search="exact_dp", s=8, alphabet_m=12, B=2.0, seed=0)
+    assert ob["route"] == "beam" and ob["lam"] == oe["lam"] > 0.0
+    assert np.array_equal(ob["mask"], oe["mask"])
+    o1 = pipeline.run(b, search="beam", s=8, alphabet_m=12, B=2.0, beam_width=1, seed=0)
+    assert o1["rate_bits"] <= 2.0 * b.size
