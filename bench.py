@@ -219,16 +219,19 @@ def decode_stream(torch, kvq, W, steps=200, batches=16):
 
 
 def exact_search(torch, kvq, W, reps=5):
-    """Exact codebook search on the feature-group tensor: the 12-quantile
-    alphabet with |Q| <= 8 and the 32-quantile alphabet with |Q| <= 16.
+    """Searches over a quantile alphabet on the feature-group tensor: the
+    exact DP (12 quantiles with |Q| <= 8, 32 quantiles with |Q| <= 16) and
+    the beam over ordered codepoints (widths 2 and 4 on the same two).
     Medians of eval (HIP events) and of the solve call (host clock: it
     synchronises), with the multiplier and modelled rate."""
     out = {}
     t = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in W.generate(W.FEATURE_GROUP_EXACT_FP32)]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    for w in (W.FEATURE_GROUP_EXACT_FP32, W.FEATURE_GROUP_EXACT_M32):
-        plan = kvq.kvq_plan_blocks(t, w.tokens_per_block, w.dims_per_block, w.s, kvq.KVQ_EXACT_DP,
-                                   w.alphabet_m)
+    cases = [("exact_dp", W.FEATURE_GROUP_EXACT_FP32, 0), ("exact_dp", W.FEATURE_GROUP_EXACT_M32, 0),
+             ("beam", W.FEATURE_GROUP_EXACT_FP32, 2), ("beam", W.FEATURE_GROUP_EXACT_M32, 4)]
+    for search, w, width in cases:
+        sm = kvq.KVQ_EXACT_DP if search == "exact_dp" else kvq.KVQ_BEAM
+        plan = kvq.kvq_plan_blocks(t, w.tokens_per_block, w.dims_per_block, w.s, sm, w.alphabet_m, width)
         buf = kvq.allocate(plan)
         te, ts = [], []
         for _ in range(reps + 1):
@@ -242,9 +245,11 @@ def exact_search(torch, kvq, W, reps=5):
                                              w.iters, w.eta, 0.0, buf["choice"], buf["codebook"], buf["m"],
                                              buf["off"], buf["workspace"])
             ts.append(1e3 * (time.perf_counter() - t0))
-        out[w.name] = {"alphabet": w.alphabet_m, "max_levels": w.s, "blocks": plan.n_blocks,
-                       "pairs_per_block": plan.n_cand, "eval_ms": float(np.median(te[1:])),
-                       "solve_ms": float(np.median(ts[1:])), "lambda": lam, "rate_bits_per_entry": rate}
+        key = f"{search}_m{w.alphabet_m}_s{w.s}" + (f"_w{width}" if width else "")
+        out[key] = {"alphabet": w.alphabet_m, "max_levels": w.s, "beam_width": width or None,
+                    "blocks": plan.n_blocks, "pairs_per_block": plan.n_cand,
+                    "eval_ms": float(np.median(te[1:])), "solve_ms": float(np.median(ts[1:])),
+                    "lambda": lam, "rate_bits_per_entry": rate}
         del buf
     return out
 

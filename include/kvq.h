@@ -64,6 +64,14 @@ typedef int32_t kvq_status;
 #define KVQ_GRIDS 0    /* {min,max} + uniform and quantile grids, k = 3..s */
 #define KVQ_EXACT_DP 1 /* every endpoint-containing subset (2..s points) of a
                           quantile alphabet of alphabet_m points, exact DP */
+#define KVQ_BEAM 2     /* the same alphabet and subsets, searched by a beam
+                          over ordered codepoints (Implementation notes):
+                          codebooks grow left to right with the DP's partial
+                          cost; chains of equal length ending at the same
+                          codepoint compete and the beam_width cheapest of
+                          each group (ties: lexicographically smaller chain)
+                          are extended; the best completed chain wins (ties:
+                          shorter, then lexicographically smaller) */
 
 /* multiplier update (kvq_solve_lambda.mode) */
 #define KVQ_BISECT 0  /* bracket doubling then `iters` halvings; feasible end */
@@ -74,6 +82,7 @@ typedef int32_t kvq_status;
 #define KVQ_MAX_S 16
 #define KVQ_MAX_BLOCK 4096
 #define KVQ_MAX_ALPHABET 32
+#define KVQ_MAX_BEAM 8
 
 /* A KV tensor [outer, heads, tokens, dim] in device memory (caller-owned).
    Strides are in elements; every stride must be positive. */
@@ -91,8 +100,9 @@ typedef struct {
     int32_t tokens_per_block; /* 32 for head x 32-token blocks */
     int32_t dims_per_block;   /* head_dim, or the feature-group width */
     int32_t s;                /* codebook size limit |Q| <= s, 2..16 */
-    int32_t search;           /* KVQ_GRIDS | KVQ_EXACT_DP */
-    int32_t alphabet_m;       /* KVQ_EXACT_DP alphabet size (2..32); else 0 */
+    int32_t search;           /* KVQ_GRIDS | KVQ_EXACT_DP | KVQ_BEAM */
+    int32_t alphabet_m;       /* KVQ_EXACT_DP / KVQ_BEAM alphabet size (2..32); else 0 */
+    int32_t beam_width;       /* KVQ_BEAM: chains kept per group (1..8); else 0 */
 } kvq_block_spec;
 
 /* Result of kvq_plan_blocks: block geometry and the byte size of every buffer
@@ -103,7 +113,7 @@ typedef struct {
     int64_t n_blocks;      /* R */
     int64_t n_entries;     /* R * d_block */
     int32_t d_block;       /* d_r, entries per block (<= 4096) */
-    int32_t n_cand;        /* GRIDS: candidates C = 1 + 2 (s - 2); EXACT_DP: pairs */
+    int32_t n_cand;        /* GRIDS: candidates C = 1 + 2 (s - 2); EXACT_DP, BEAM: pairs */
     int32_t n_stats;       /* order statistics kept per block */
     int32_t s;
     int32_t search;
@@ -116,7 +126,7 @@ typedef struct {
     int64_t shape[KVQ_MAX_TENSORS][4];      /* tensor shapes the plan was made for */
     size_t D_bytes;        /* kvq_eval_candidates D */
     size_t H_bytes;        /* kvq_eval_candidates H */
-    size_t stats_bytes;    /* order statistics, fp32 [n_stats][R] (GRIDS) or [R][m] (EXACT_DP) */
+    size_t stats_bytes;    /* order statistics, fp32 [n_stats][R] (GRIDS) or [R][m] (EXACT_DP, BEAM) */
     size_t choice_bytes;   /* int32 [R] */
     size_t codebook_bytes; /* fp32 [R][s] */
     size_t m_bytes;        /* uint8 [R] */
@@ -124,7 +134,7 @@ typedef struct {
     size_t workspace_bytes;
     uint64_t max_code_words; /* code-stream words when every block uses s levels */
     int32_t rate_shift;    /* fixed-point scale 2^rate_shift of the rate sums */
-    int32_t pad_;
+    int32_t beam_width;    /* KVQ_BEAM: chains kept per group; else 0 */
 } kvq_plan;
 
 /* Human-readable name of a status code (static string). */
@@ -153,7 +163,7 @@ kvq_status kvq_plan_blocks(const kvq_tensor* t, int32_t n_tensors,
                stats[n_stats][R] (fp32) order statistics at the sorted
                         distinct quantile ranks j (n-1)/(k-1) rounded half up
                         (first = minimum, last = maximum).
-   KVQ_EXACT_DP: stats[R][alphabet_m] the alphabet order statistics (with
+   KVQ_EXACT_DP and KVQ_BEAM: stats[R][alphabet_m] the alphabet order statistics (with
                repeats); with A the sorted distinct alphabet (m points) and
                pair p = index of (i < j) in row-major upper-triangle order of
                an alphabet_m-point alphabet, P = plan.n_cand =
@@ -186,7 +196,7 @@ kvq_status kvq_eval_candidates(const kvq_plan* p, const kvq_tensor* t, int32_t n
    KVQ_SUBGRAD: blocks are chosen at *lambda_io (host, input); then
      *lambda_io <- max(0, lambda + eta (Rbar - B)) with Rbar the modelled
      bits per entry.
-   Outputs (device): choice[R] (GRIDS: candidate index; EXACT_DP: bitmask of
+   Outputs (device): choice[R] (GRIDS: candidate index; EXACT_DP, BEAM: bitmask of
    the chosen distinct-alphabet points), codebook[R][s] (fp32, unused slots
    0), m[R] (levels), word_off[R+1] (exclusive scan of ceil(d_r w_r / 32),
    w_r = ceil(log2 m_r)); *rate_bits_per_entry_out (host) is the modelled

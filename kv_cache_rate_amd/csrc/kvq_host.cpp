@@ -68,7 +68,9 @@ void rank_table(const kvq_plan& p, kvq::RankTable& rt) {
 
 bool valid_plan(const kvq_plan* p) {
     return p && p->n_blocks >= 0 && p->d_block >= 2 && p->d_block <= KVQ_MAX_BLOCK && p->s >= 2 &&
-           p->s <= KVQ_MAX_S && (p->search == KVQ_GRIDS || p->search == KVQ_EXACT_DP) &&
+           p->s <= KVQ_MAX_S &&
+           (p->search == KVQ_GRIDS || p->search == KVQ_EXACT_DP || p->search == KVQ_BEAM) &&
+           (p->search != KVQ_BEAM || (p->beam_width >= 1 && p->beam_width <= KVQ_MAX_BEAM)) &&
            p->n_tensors >= 1 && p->n_tensors <= KVQ_MAX_TENSORS;
 }
 
@@ -144,9 +146,11 @@ kvq_status kvq_plan_blocks(const kvq_tensor* t, int32_t nt, const kvq_block_spec
     const int64_t n = (int64_t)Tb * Db;
     if (n < 2 || n > KVQ_MAX_BLOCK) return fail(KVQ_EINVAL, "block of %lld entries (need 2..4096)", (long long)n);
     if (spec->s < 2 || spec->s > KVQ_MAX_S) return fail(KVQ_EINVAL, "s=%d outside 2..16", spec->s);
-    if (spec->search != KVQ_GRIDS && spec->search != KVQ_EXACT_DP)
+    if (spec->search != KVQ_GRIDS && spec->search != KVQ_EXACT_DP && spec->search != KVQ_BEAM)
         return fail(KVQ_EINVAL, "unknown search mode %d", spec->search);
-    if (spec->search == KVQ_EXACT_DP && (spec->alphabet_m < 2 || spec->alphabet_m > KVQ_MAX_ALPHABET))
+    if (spec->search == KVQ_BEAM && (spec->beam_width < 1 || spec->beam_width > KVQ_MAX_BEAM))
+        return fail(KVQ_EINVAL, "beam_width=%d outside 1..%d", spec->beam_width, KVQ_MAX_BEAM);
+    if (spec->search != KVQ_GRIDS && (spec->alphabet_m < 2 || spec->alphabet_m > KVQ_MAX_ALPHABET))
         return fail(KVQ_EINVAL, "alphabet_m=%d outside 2..%d", spec->alphabet_m, KVQ_MAX_ALPHABET);
     kvq_plan p;
     memset(&p, 0, sizeof p);
@@ -175,7 +179,8 @@ kvq_status kvq_plan_blocks(const kvq_tensor* t, int32_t nt, const kvq_block_spec
     p.d_block = (int32_t)n;
     p.s = spec->s;
     p.search = spec->search;
-    p.alphabet_m = spec->search == KVQ_EXACT_DP ? spec->alphabet_m : 0;
+    p.alphabet_m = spec->search != KVQ_GRIDS ? spec->alphabet_m : 0;
+    p.beam_width = spec->search == KVQ_BEAM ? spec->beam_width : 0;
     p.n_tensors = nt;
     p.tokens_per_block = Tb;
     p.dims_per_block = Db;

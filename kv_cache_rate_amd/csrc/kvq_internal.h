@@ -17,6 +17,7 @@ constexpr int kMaxCand = 1 + 2 * (kMaxS - 2);     // 29 grid candidates
 constexpr int kMaxStats = 80;                     // >= 73 distinct quantile ranks
 constexpr int kAlpha = KVQ_MAX_ALPHABET;             // 32
 constexpr int kMaxPairs = kAlpha * (kAlpha - 1) / 2; // 496
+constexpr int kMaxBeam = KVQ_MAX_BEAM;                // 8
 constexpr int kMaxLam = 64;                       // multipliers per solve pass
 
 // Device status bits (workspace header).
@@ -34,7 +35,9 @@ struct WsHeader {
     int32_t nlam;        // multipliers probed by the next rates pass
     int32_t bits_left;   // halvings still to emulate
     int32_t bits_now;    // halvings covered by the current pass
-    int32_t pad0;
+    int32_t bits_max;    // halvings per multisection pass (2^b - 1 multipliers)
+    int32_t dbl_n;       // powers of two probed per doubling pass
+    int32_t dbl_base;    // exponent of the current doubling pass's first probe
     double lo, hi;       // bracket
     double lam_final;    // multiplier the blocks are chosen at
     uint64_t rate_final; // fixed-point rate of the final choice

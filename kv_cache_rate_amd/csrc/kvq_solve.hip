@@ -21,6 +21,9 @@
 //           and give the same final bracket bit for bit.
 // Rates are summed as unsigned fixed point (d_r H_r scaled by 2^shift and
 // rounded), so the sum is exact and independent of summation order.
+#include <algorithm>
+#include <type_traits>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -51,12 +54,15 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
 }
 
 __global__ void solve_init_kernel(WsHeader* h, int mode, double lam_in, unsigned long long Btot_fx,
-                                  int iters) {
+                                  int iters, int bits_max, int dbl_n) {
     if (threadIdx.x != 0) return;
     h->done = 0;
     h->err = 0;
     h->Btot_fx = Btot_fx;
     h->bits_left = iters;
+    h->bits_max = bits_max;
+    h->dbl_n = dbl_n;
+    h->dbl_base = 0;
     h->rate_final = 0;
     for (int j = 0; j < kMaxLam + 8; ++j) h->sums[j] = 0ull;
     h->pool_n = 0;
@@ -81,7 +87,7 @@ __device__ void setup_multisection(WsHeader* h) {
         h->nlam = 0;
         return;
     }
-    const int b = h->bits_left < 6 ? h->bits_left : 6;
+    const int b = h->bits_left < h->bits_max ? h->bits_left : h->bits_max;
     const int pts = (1 << b) - 1;
     const double lo = h->lo, width = h->hi - h->lo;
     for (int i = 1; i <= pts; ++i) h->lam[i - 1] = lo + (width * (double)i) / (double)(1 << b);
@@ -98,23 +104,31 @@ __global__ void solve_select_kernel(WsHeader* h) {
         if (h->sums[0] <= B) {
             h->lam_final = 0.0;
             h->done = 1;
-        } else {  // bracket doubling: 2^0 .. 2^62 in one pass
+        } else {  // bracket doubling: 2^0, 2^1, ... dbl_n per pass, up to 2^62
             h->phase = kPhaseDouble;
-            h->nlam = kMaxLam - 1;
-            for (int j = 0; j < kMaxLam - 1; ++j) h->lam[j] = ldexp(1.0, j);
+            h->dbl_base = 0;
+            h->nlam = h->dbl_n;
+            for (int j = 0; j < h->nlam; ++j) h->lam[j] = ldexp(1.0, j);
         }
         break;
     case kPhaseDouble: {
         int first = -1;
-        for (int j = 0; j < kMaxLam - 1; ++j)
+        for (int j = 0; j < h->nlam; ++j)
             if (h->sums[j] <= B) {
                 first = j;
                 break;
             }
+        const int e0 = h->dbl_base;
         if (first >= 0) {
-            h->hi = h->lam[first];
-            h->lo = first == 0 ? 0.0 : h->lam[first - 1];
+            h->hi = ldexp(1.0, e0 + first);
+            h->lo = e0 + first == 0 ? 0.0 : ldexp(1.0, e0 + first - 1);
             setup_multisection(h);
+        } else if (e0 + h->nlam < kMaxLam - 1) {  // next powers of two
+            const int base = e0 + h->nlam;
+            const int cnt = min(h->dbl_n, kMaxLam - 1 - base);
+            h->dbl_base = base;
+            h->nlam = cnt;
+            for (int j = 0; j < cnt; ++j) h->lam[j] = ldexp(1.0, base + j);
         } else {
             h->phase = kPhaseDouble2;
             h->nlam = 2;
@@ -295,6 +309,8 @@ final_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
 __device__ __forceinline__ double hbits(double p) { return p > 0.0 ? -p * log2(p) : 0.0; }
 
 constexpr int kDpThreads = 256;
+// beam arrivals at one destination, (l - 1) width <= 30 x 8, over 64 lanes
+constexpr int kArrivalsPerLane = ((kAlpha - 2) * kMaxBeam + 63) / 64;
 
 // Pair-state dynamic program over the distinct alphabet A (m points, pairs
 // indexed in the M-point triangle), one workgroup per (block, multiplier):
@@ -308,141 +324,379 @@ constexpr int kDpThreads = 256;
 // point are complete.  Ties: lowest i, and across completions the smallest
 // c, then the lowest i.  One thread per state (j, l) per layer, layers
 // double-buffered in LDS; the chain's points ride along as a bitmask.
-struct DpShared {
-    double Dp[kMaxPairs], ML[kMaxPairs], MR[kMaxPairs];
-    double f[2][kMaxPairs];
-    uint32_t mk[2][kMaxPairs];
-    float A[kAlpha];
-    int m;
+// LDS of one alphabet-search workgroup, carved from dynamic shared memory
+// and sized by the alphabet (P pairs) and the beam width W (0: the DP):
+//   Dp, ML, MR [P] (fp64)  pair statistics
+//   DP:   f[2][P] (fp64), mk[2][P] (u32)       two layers of chain costs / masks
+//   beam: cand[P][W] (fp64), g[2][M][W], cnt[2][M]  arrivals and kept groups
+//   A[M] (fp32) distinct alphabet, m (its size)
+struct BeamEntry {
+    double cost;
+    uint32_t mask;   // the chain's points
+    uint32_t prev;   // the point before the last
 };
 
-__device__ uint32_t dp_block(DpShared& sh, const double* __restrict__ Dg, const double* __restrict__ Mg,
+struct AlphaLds {
+    double *Dp, *ML, *MR, *f, *cand;
+    uint32_t* mk;
+    BeamEntry* g;
+    int* cnt;
+    float* A;
+    int* m;
+};
+
+__host__ __device__ inline size_t alpha_lds_bytes(int M, int W, AlphaLds* v, unsigned char* base) {
+    const size_t P = (size_t)n_pairs(M);
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = (o + bytes + 15) & ~(size_t)15;
+        return base ? base + at : nullptr;
+    };
+    AlphaLds t{};
+    t.Dp = (double*)take(P * 8);
+    t.ML = (double*)take(P * 8);
+    t.MR = (double*)take(P * 8);
+    if (W == 0) {
+        t.f = (double*)take(2 * P * 8);
+        t.mk = (uint32_t*)take(2 * P * 4);
+    } else {
+        t.cand = (double*)take(P * (size_t)W * 8);
+        t.g = (BeamEntry*)take(2 * (size_t)M * W * sizeof(BeamEntry));
+        t.cnt = (int*)take(2 * (size_t)M * 4);
+    }
+    t.A = (float*)take((size_t)M * 4);
+    t.m = (int*)take(4);
+    if (v) *v = t;
+    return o;
+}
+
+// Load one block's pair statistics and distinct alphabet into LDS.
+__device__ void load_pairs(const AlphaLds& t, const double* __restrict__ Dg, const double* __restrict__ Mg,
+                           const float* __restrict__ st, int M) {
+    const int P = n_pairs(M);
+    for (int p = threadIdx.x; p < P; p += blockDim.x) {
+        t.Dp[p] = Dg[p];
+        t.ML[p] = Mg[2 * p];
+        t.MR[p] = Mg[2 * p + 1];
+    }
+    if (threadIdx.x == 0) {
+        int m = 0;
+        for (int j = 0; j < M; ++j)
+            if (m == 0 || st[j] != t.A[m - 1]) t.A[m++] = st[j];
+        *t.m = m;
+    }
+}
+
+// Pair index -> (j, l) of the M-point triangle.
+__device__ __forceinline__ void pair_of(int p, int M, int& j, int& l) {
+    j = 0;
+    int rem = p;
+    while (rem >= M - 1 - j) {
+        rem -= M - 1 - j;
+        ++j;
+    }
+    l = j + 1 + rem;
+}
+
+__device__ uint32_t dp_block(const AlphaLds& t, const double* __restrict__ Dg, const double* __restrict__ Mg,
                              const float* __restrict__ st, int M, int smax, int n, double w) {
     const int tid = threadIdx.x;
     const int P = n_pairs(M);
     const double dn = (double)n;
     const double INF = __builtin_huge_val();
+    load_pairs(t, Dg, Mg, st, M);
     for (int p = tid; p < P; p += blockDim.x) {
-        sh.Dp[p] = Dg[p];
-        sh.ML[p] = Mg[2 * p];
-        sh.MR[p] = Mg[2 * p + 1];
-        sh.f[0][p] = INF;
-        sh.mk[0][p] = 0u;
-    }
-    if (tid == 0) {
-        int m = 0;
-        for (int j = 0; j < M; ++j)
-            if (m == 0 || st[j] != sh.A[m - 1]) sh.A[m++] = st[j];
-        sh.m = m;
+        t.f[p] = INF;
+        t.mk[p] = 0u;
     }
     __syncthreads();
-    const int m = sh.m;
+    const int m = *t.m;
     if (m <= 1) return 1u;
     for (int l = 1 + tid; l < m; l += blockDim.x) {
         const int p = pair_index(0, l, M);
-        sh.f[0][p] = sh.Dp[p] + w * hbits(sh.ML[p] / dn);
-        sh.mk[0][p] = 1u | (1u << l);
+        t.f[p] = t.Dp[p] + w * hbits(t.ML[p] / dn);
+        t.mk[p] = 1u | (1u << l);
     }
-    double best = INF;  // thread 0's running completion
+    double best = INF;  // wave 0's running completion
     uint32_t best_mask = 0u;
     const int cmax = smax < m ? smax : m;
     int cur = 0;
     for (int c = 2;; ++c) {
         __syncthreads();
-        if (tid == 0) {
-            for (int i = 0; i < m - 1; ++i) {
-                const int p = pair_index(i, m - 1, M);
-                const double fv = sh.f[cur][p];
-                if (fv < INF) {
-                    const double tot = fv + w * hbits(sh.MR[p] / dn);
-                    if (tot < best) {
-                        best = tot;
-                        best_mask = sh.mk[cur][p];
-                    }
-                }
+        const double* fc = t.f + cur * P;
+        const uint32_t* mc = t.mk + cur * P;
+        if (tid < 64) {
+            // completions (i, m - 1): lane i scores its chain; the minimum
+            // wins, ties to the lowest i
+            double tot = INF;
+            if (tid < m - 1) {
+                const int p = pair_index(tid, m - 1, M);
+                const double fv = fc[p];
+                if (fv < INF) tot = fv + w * hbits(t.MR[p] / dn);
+            }
+            double mn = tot;
+            for (int o = 32; o > 0; o >>= 1) mn = fmin(mn, __shfl_xor(mn, o, 64));
+            const unsigned long long hit = __ballot(tot == mn && mn < INF);
+            if (mn < best && hit) {
+                const int i = __ffsll((long long)hit) - 1;
+                best = mn;
+                best_mask = mc[pair_index(i, m - 1, M)];
             }
         }
         if (c >= cmax) break;
         const int nx = cur ^ 1;
+        double* fn = t.f + nx * P;
+        uint32_t* mn_ = t.mk + nx * P;
         // states (j, l): 1 <= j <= m - 2, j < l <= m - 1; every other entry
         // of the next layer is unreachable
         for (int p = tid; p < P; p += blockDim.x) {
-            int j = 0, rem = p;
-            while (rem >= M - 1 - j) {
-                rem -= M - 1 - j;
-                ++j;
-            }
-            const int l = j + 1 + rem;
+            int j, l;
+            pair_of(p, M, j, l);
             double bv = INF;
             uint32_t bm = 0u;
             if (j >= 1 && l < m) {
-                const double Djl = sh.Dp[p], MLjl = sh.ML[p];
+                const double Djl = t.Dp[p], MLjl = t.ML[p];
                 for (int i = 0; i < j; ++i) {
                     const int q = pair_index(i, j, M);
-                    const double fv = sh.f[cur][q];
+                    const double fv = fc[q];
                     if (fv < INF) {
-                        const double v = (fv + Djl) + w * hbits((sh.MR[q] + MLjl) / dn);
+                        const double v = (fv + Djl) + w * hbits((t.MR[q] + MLjl) / dn);
                         if (v < bv) {
                             bv = v;
-                            bm = sh.mk[cur][q];
+                            bm = mc[q];
                         }
                     }
                 }
             }
-            sh.f[nx][p] = bv;
-            sh.mk[nx][p] = bv < INF ? (bm | (1u << l)) : 0u;
+            fn[p] = bv;
+            mn_[p] = bv < INF ? (bm | (1u << l)) : 0u;
         }
         cur = nx;
     }
-    return best_mask;  // valid in thread 0
+    return best_mask;  // valid in wave 0
+}
+
+// a precedes b among chains of equal length: the lowest point where they
+// differ belongs to a
+__device__ __forceinline__ bool lex_before(uint32_t a, uint32_t b) {
+    const uint32_t d = a ^ b;
+    return (d & (0u - d) & a) != 0u;
+}
+
+// Beam search over ordered codepoints (the same partial cost as the DP):
+// chains with the same number of points ending at the same codepoint
+// compete, and only the `width` cheapest of each such group are extended,
+// ties to the lexicographically smaller chain.  Chains reaching the last
+// point are complete; the best completion wins, ties to the shorter, then
+// the lexicographically smaller chain.
+//   layer step: thread per (source group j, destination l > j) scores the
+//   j-group's chains extended by l into cand; then every arrival counts
+//   the arrivals at its destination that precede it and the `width` first
+//   take the next layer's group; wave 0 picks the best completion
+//   (destination m - 1).
+__device__ uint32_t beam_block(const AlphaLds& t, const double* __restrict__ Dg, const double* __restrict__ Mg,
+                               const float* __restrict__ st, int M, int smax, int width, int n, double w) {
+    const int tid = threadIdx.x;
+    const int P = n_pairs(M);
+    const double dn = (double)n;
+    const double INF = __builtin_huge_val();
+    load_pairs(t, Dg, Mg, st, M);
+    __syncthreads();
+    const int m = *t.m;
+    if (m <= 1) return 1u;
+    auto grp = [&](int layer, int l) { return t.g + ((size_t)layer * M + l) * width; };
+    auto cnt = [&](int layer, int l) -> int& { return t.cnt[layer * M + l]; };
+    // length 2: group l holds the chain (0, l); (0, m - 1) is complete
+    for (int l = tid; l < m; l += blockDim.x) {
+        cnt(0, l) = 0;
+        if (l >= 1 && l < m - 1) {
+            const int p = pair_index(0, l, M);
+            grp(0, l)[0] = BeamEntry{t.Dp[p] + w * hbits(t.ML[p] / dn), 1u | (1u << l), 0u};
+            cnt(0, l) = 1;
+        }
+    }
+    // wave 0's running completion, starting from the chain (0, m - 1)
+    double best;
+    uint32_t best_mask;
+    {
+        const int p = pair_index(0, m - 1, M);
+        best = (t.Dp[p] + w * hbits(t.ML[p] / dn)) + w * hbits(t.MR[p] / dn);
+        best_mask = 1u | (1u << (m - 1));
+    }
+    const int cmax = smax < m ? smax : m;
+    int cur = 0;
+    for (int c = 2; c < cmax; ++c) {
+        __syncthreads();
+        // arrivals: chain b of group j extended by l
+        for (int p = tid; p < P; p += blockDim.x) {
+            int j, l;
+            pair_of(p, M, j, l);
+            if (j >= 1 && l < m) {
+                const int nb = cnt(cur, j);
+                const BeamEntry* gj = grp(cur, j);
+                const double Djl = t.Dp[p], MLjl = t.ML[p];
+                const double fin = l == m - 1 ? w * hbits(t.MR[p] / dn) : 0.0;
+                for (int b = 0; b < nb; ++b) {
+                    const BeamEntry e = gj[b];
+                    const int q = pair_index((int)e.prev, j, M);
+                    const double v = (e.cost + Djl) + w * hbits((t.MR[q] + MLjl) / dn);
+                    t.cand[(size_t)p * width + b] = l == m - 1 ? v + fin : v;
+                }
+            }
+        }
+        __syncthreads();
+        const int nx = cur ^ 1;
+        // destinations l = 2 .. m - 2 keep their `width` cheapest arrivals
+        // (ties: lexicographically smaller), one wave per destination: lane
+        // q holds arrivals q, q + 64, ... (arrival x = chain x % width of
+        // group 1 + x / width), and `width` rounds extract the wave minimum
+        {
+            const int lane = tid & 63, nw = (int)blockDim.x >> 6;
+            for (int l = 2 + (tid >> 6); l < m - 1; l += nw) {
+                double v[kArrivalsPerLane];
+                uint32_t pm[kArrivalsPerLane], src[kArrivalsPerLane];
+#pragma unroll
+                for (int k = 0; k < kArrivalsPerLane; ++k) {
+                    const int x = lane + 64 * k;
+                    const int j = 1 + x / width, b = x - (j - 1) * width;
+                    v[k] = INF;
+                    pm[k] = 0u;
+                    src[k] = 0u;
+                    if (j < l && b < cnt(cur, j)) {
+                        v[k] = t.cand[(size_t)pair_index(j, l, M) * width + b];
+                        pm[k] = grp(cur, j)[b].mask;
+                        src[k] = (uint32_t)j;
+                    }
+                }
+                int kept = 0;
+                for (int r = 0; r < width; ++r) {
+                    // this lane's first remaining arrival in the order
+                    double bv = INF;
+                    uint32_t bm = 0u;
+#pragma unroll
+                    for (int k = 0; k < kArrivalsPerLane; ++k)
+                        if (pm[k] != 0u && (v[k] < bv || (v[k] == bv && (bm == 0u || lex_before(pm[k], bm))))) {
+                            bv = v[k];
+                            bm = pm[k];
+                        }
+                    // the wave's first: the (cost, chain) order is strict
+                    double wv = bv;
+                    uint32_t wm = bm;
+                    for (int o = 32; o > 0; o >>= 1) {
+                        const double ov = __shfl_xor(wv, o, 64);
+                        const uint32_t om = __shfl_xor(wm, o, 64);
+                        if (om != 0u && (wm == 0u || ov < wv || (ov == wv && lex_before(om, wm)))) {
+                            wv = ov;
+                            wm = om;
+                        }
+                    }
+                    if (wm == 0u) break;  // no arrival left
+#pragma unroll
+                    for (int k = 0; k < kArrivalsPerLane; ++k)
+                        if (pm[k] == wm && v[k] == wv) {  // the holder records and drops it
+                            grp(nx, l)[r] = BeamEntry{wv, wm | (1u << l), src[k]};
+                            pm[k] = 0u;
+                        }
+                    ++kept;
+                }
+                if (lane == 0) cnt(nx, l) = kept;
+            }
+        }
+        for (int l = tid; l < m; l += blockDim.x)
+            if (l < 2 || l == m - 1) cnt(nx, l) = 0;
+        // completions at the last point: lane j scores group j's chains,
+        // then the wave keeps the cheapest (ties: lexicographically smaller)
+        if (tid < 64) {
+            double tot = INF;
+            uint32_t tm = 0u;
+            if (tid >= 1 && tid < m - 1) {
+                const int nb = cnt(cur, tid);
+                const BeamEntry* gj = grp(cur, tid);
+                const double* cp = t.cand + (size_t)pair_index(tid, m - 1, M) * width;
+                for (int b2 = 0; b2 < nb; ++b2) {
+                    const double v = cp[b2];
+                    const uint32_t mk = gj[b2].mask | (1u << (m - 1));
+                    if (v < tot || (v == tot && lex_before(mk, tm))) {
+                        tot = v;
+                        tm = mk;
+                    }
+                }
+            }
+            for (int o = 32; o > 0; o >>= 1) {
+                const double ot = __shfl_xor(tot, o, 64);
+                const uint32_t om = __shfl_xor(tm, o, 64);
+                if (ot < tot || (ot == tot && om != 0u && (tm == 0u || lex_before(om, tm)))) {
+                    tot = ot;
+                    tm = om;
+                }
+            }
+            if (tm != 0u && (tot < best || (tot == best && __popc(tm) == __popc(best_mask) &&
+                                            lex_before(tm, best_mask)))) {
+                best = tot;
+                best_mask = tm;
+            }
+        }
+        cur = nx;
+    }
+    return best_mask;  // valid in wave 0
 }
 
 // Entropy (bits per entry) of the subset given by mask: each point's mass
 // is what the interval on its left sends right plus what the interval on
 // its right sends left.
-__device__ double subset_entropy(const DpShared& sh, int M, uint32_t mask, int n) {
-    const int m = sh.m;
+__device__ double subset_entropy(const AlphaLds& t, int M, uint32_t mask, int n) {
+    const int m = *t.m;
     int pts[kAlpha];
     int k = 0;
     for (int i = 0; i < m; ++i)
         if (mask & (1u << i)) pts[k++] = i;
     if (k <= 1) return 0.0;
     double Hs = 0.0;
-    for (int t = 0; t < k; ++t) {
+    for (int q = 0; q < k; ++q) {
         double mass = 0.0;
-        if (t > 0) mass += sh.MR[pair_index(pts[t - 1], pts[t], M)];
-        if (t + 1 < k) mass += sh.ML[pair_index(pts[t], pts[t + 1], M)];
+        if (q > 0) mass += t.MR[pair_index(pts[q - 1], pts[q], M)];
+        if (q + 1 < k) mass += t.ML[pair_index(pts[q], pts[q + 1], M)];
         Hs += hbits(mass / (double)n);
     }
     return Hs;
 }
 
-// Rate of every multiplier of the pass: workgroup (block r, multiplier j).
+__device__ __forceinline__ uint32_t alpha_search(const AlphaLds& t, const double* Dg, const double* Mg,
+                                                 const float* st, int M, int smax, int width, int n,
+                                                 double w) {
+    return width ? beam_block(t, Dg, Mg, st, M, smax, width, n, w) : dp_block(t, Dg, Mg, st, M, smax, n, w);
+}
+
+// Rate of every multiplier of the pass: workgroup (block r, multiplier j);
+// width 0 runs the exact DP, else the beam.
 __global__ void __launch_bounds__(kDpThreads)
-rates_dp_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr,
-                const float* __restrict__ stats, int64_t R, int alpha_m, int smax, int n,
-                int shift, WsHeader* h) {
-    __shared__ DpShared sh;
+rates_alpha_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr,
+                   const float* __restrict__ stats, int64_t R, int alpha_m, int smax, int width, int n,
+                   int shift, WsHeader* h) {
+    extern __shared__ __align__(16) unsigned char lds[];
     const int j = blockIdx.y;
     if (h->done || j >= h->nlam) return;
+    AlphaLds t;
+    alpha_lds_bytes(alpha_m, width, &t, lds);
     const int64_t r = blockIdx.x;
     const int P = n_pairs(alpha_m);
     const double w = h->lam[j] * (double)n;
-    const uint32_t mask = dp_block(sh, Dp + r * P, Mlr + r * P * 2, stats + r * alpha_m, alpha_m,
-                                   smax, n, w);
+    const uint32_t mask = alpha_search(t, Dp + r * P, Mlr + r * P * 2, stats + r * alpha_m, alpha_m, smax,
+                                       width, n, w);
     if (threadIdx.x == 0) {
-        const double Hs = subset_entropy(sh, alpha_m, mask, n);
+        const double Hs = subset_entropy(t, alpha_m, mask, n);
         atomicAdd(&h->sums[j], rate_fx((double)n, Hs, shift));
     }
 }
 
 // The blocks' choice at the final multiplier: workgroup = block.
 __global__ void __launch_bounds__(kDpThreads)
-final_dp_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr,
-                const float* __restrict__ stats, int64_t R, int alpha_m, int smax, int s, int n,
-                int shift, WsHeader* h, int32_t* __restrict__ choice, float* __restrict__ codebook,
-                uint8_t* __restrict__ m_out, uint64_t* __restrict__ off) {
-    __shared__ DpShared sh;
+final_alpha_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr,
+                   const float* __restrict__ stats, int64_t R, int alpha_m, int smax, int width, int s,
+                   int n, int shift, WsHeader* h, int32_t* __restrict__ choice, float* __restrict__ codebook,
+                   uint8_t* __restrict__ m_out, uint64_t* __restrict__ off) {
+    extern __shared__ __align__(16) unsigned char lds[];
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x;
     if (r == 0 && tid == 0) off[0] = 0;
@@ -455,16 +709,19 @@ final_dp_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr,
         for (int j = tid; j < s; j += blockDim.x) codebook[r * s + j] = 0.0f;
         return;
     }
+    AlphaLds t;
+    alpha_lds_bytes(alpha_m, width, &t, lds);
     const int P = n_pairs(alpha_m);
     const double w = h->lam_final * (double)n;
-    const uint32_t mask = dp_block(sh, Dp + r * P, Mlr + r * P * 2, stats + r * alpha_m, alpha_m,
-                                   smax, n, w);
+    const uint32_t mask = alpha_search(t, Dp + r * P, Mlr + r * P * 2, stats + r * alpha_m, alpha_m, smax,
+                                       width, n, w);
     if (tid == 0) {
-        const double Hs = subset_entropy(sh, alpha_m, mask, n);
+        const double Hs = subset_entropy(t, alpha_m, mask, n);
         atomicAdd(&h->rate_final, rate_fx((double)n, Hs, shift));
+        const int m = *t.m;
         int k = 0;
-        for (int i = 0; i < sh.m; ++i)
-            if (mask & (1u << i)) codebook[r * s + k++] = sh.A[i];
+        for (int i = 0; i < m; ++i)
+            if (mask & (1u << i)) codebook[r * s + k++] = t.A[i];
         for (int j = k; j < s; ++j) codebook[r * s + j] = 0.0f;
         choice[r] = (int32_t)mask;
         m_out[r] = (uint8_t)k;
@@ -690,10 +947,24 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
     const double Bfx = ldexp(Btot, shift);
     const unsigned long long Btot_fx =
         Bfx >= 18446744073709551615.0 ? ~0ull : (unsigned long long)floor(Bfx);
-    hipLaunchKernelGGL(solve_init_kernel, dim3(1), dim3(64), 0, st, h, mode, lam_in, Btot_fx, iters);
+    // Multipliers per pass: the grid search scores a block at 63 multipliers
+    // for little more than the cost of one, so it takes 6 halvings (and all
+    // 63 doubling probes) per pass; the alphabet searches cost a dynamic
+    // program per multiplier, so they take one halving (and 8 doubling
+    // probes) per pass: fewer evaluations, more passes.
+    const bool grids = p.search == KVQ_GRIDS;
+    const int bits_max = grids ? 6 : 1;
+    const int dbl_n = grids ? kMaxLam - 1 : 8;
+    hipLaunchKernelGGL(solve_init_kernel, dim3(1), dim3(64), 0, st, h, mode, lam_in, Btot_fx, iters,
+                       bits_max, dbl_n);
+    // workgroups per block in an alphabet-search pass: the most multipliers
+    // any pass probes
+    const unsigned lam_slots = (unsigned)std::max(std::max(dbl_n, (1 << bits_max) - 1), 2);
+    const int width = p.search == KVQ_BEAM ? p.beam_width : 0;
+    const size_t alpha_lds = grids ? 0 : alpha_lds_bytes(p.alphabet_m, width, nullptr, nullptr);
     const unsigned grid = (unsigned)((R + kSolveThreads - 1) / kSolveThreads);
     // exact DP: one thread per pair state, in whole waves
-    const int dp_pairs = p.search == KVQ_EXACT_DP ? n_pairs(p.alphabet_m) : 0;
+    const int dp_pairs = p.search != KVQ_GRIDS ? n_pairs(p.alphabet_m) : 0;
     const int dp_waves = (dp_pairs + 63) / 64;
     const unsigned dp_threads = dp_waves < 1 ? 64u : (dp_waves > kDpThreads / 64 ? (unsigned)kDpThreads
                                                                                 : 64u * dp_waves);
@@ -702,8 +973,8 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
             hipLaunchKernelGGL(rates_grids_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, wgt,
                                R, p.n_cand, (double)n, shift, h);
         } else {
-            hipLaunchKernelGGL(rates_dp_kernel, dim3((unsigned)R, kMaxLam - 1), dim3(dp_threads), 0, st,
-                               D, H, stats, R, p.alphabet_m, p.s, n, shift, h);
+            hipLaunchKernelGGL(rates_alpha_kernel, dim3((unsigned)R, lam_slots), dim3(dp_threads), alpha_lds,
+                               st, D, H, stats, R, p.alphabet_m, p.s, width, n, shift, h);
         }
         hipLaunchKernelGGL(solve_select_kernel, dim3(1), dim3(64), 0, st, h);
     };
@@ -715,9 +986,10 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
         if (e == hipSuccess) e = hipStreamSynchronize(st);
         if (e != hipSuccess) return e;
         if (!done) {
-            // doubling (2^0..2^62), the 2^63 / 2^64 pass if needed, then
-            // multisection passes of up to 6 halvings each
-            const int passes = 2 + (iters + 5) / 6;
+            // doubling passes up to 2^62, the 2^63 / 2^64 pass if needed,
+            // then multisection passes of up to bits_max halvings each;
+            // passes after the bracket is closed return at once
+            const int passes = (kMaxLam - 1 + dbl_n - 1) / dbl_n + 1 + (iters + bits_max - 1) / bits_max;
             for (int ps = 0; ps < passes; ++ps) rates_pass();
         }
     }
@@ -725,8 +997,8 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
         hipLaunchKernelGGL(final_grids_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, wgt, stats,
                            R, p.n_cand, p.s, n, shift, rt, h, choice, codebook, m, off);
     } else {
-        hipLaunchKernelGGL(final_dp_kernel, dim3((unsigned)R), dim3(dp_threads), 0, st, D, H, stats, R,
-                           p.alphabet_m, p.s, p.s, n, shift, h, choice, codebook, m, off);
+        hipLaunchKernelGGL(final_alpha_kernel, dim3((unsigned)R), dim3(dp_threads), alpha_lds, st, D, H,
+                           stats, R, p.alphabet_m, p.s, width, p.s, n, shift, h, choice, codebook, m, off);
     }
     if (mode == KVQ_BISECT_GREEDY && p.search == KVQ_GRIDS) {
         uint2* pool = (uint2*)((char*)ws + ws_pool_offset(R));

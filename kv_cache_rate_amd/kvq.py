@@ -25,6 +25,7 @@ KVQ_F16 = 1
 KVQ_F32 = 2
 KVQ_GRIDS = 0
 KVQ_EXACT_DP = 1
+KVQ_BEAM = 2
 KVQ_BISECT = 0
 KVQ_SUBGRAD = 1
 KVQ_BISECT_GREEDY = 2
@@ -43,7 +44,8 @@ class KvqTensor(ctypes.Structure):
 
 class KvqBlockSpec(ctypes.Structure):
     _fields_ = [("tokens_per_block", ctypes.c_int32), ("dims_per_block", ctypes.c_int32),
-                ("s", ctypes.c_int32), ("search", ctypes.c_int32), ("alphabet_m", ctypes.c_int32)]
+                ("s", ctypes.c_int32), ("search", ctypes.c_int32), ("alphabet_m", ctypes.c_int32),
+                ("beam_width", ctypes.c_int32)]
 
 
 class KvqPlan(ctypes.Structure):
@@ -59,7 +61,7 @@ class KvqPlan(ctypes.Structure):
                 ("codebook_bytes", ctypes.c_size_t), ("m_bytes", ctypes.c_size_t),
                 ("offsets_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t),
                 ("max_code_words", ctypes.c_uint64), ("rate_shift", ctypes.c_int32),
-                ("pad_", ctypes.c_int32)]
+                ("beam_width", ctypes.c_int32)]
 
 
 class KvqError(RuntimeError):
@@ -181,8 +183,9 @@ def _stream(stream):
     return getattr(stream, "cuda_stream", stream)
 
 
-def kvq_plan_blocks(tensors, tokens_per_block, dims_per_block, s, search=KVQ_GRIDS, alphabet_m=0):
-    spec = KvqBlockSpec(tokens_per_block, dims_per_block, s, search, alphabet_m)
+def kvq_plan_blocks(tensors, tokens_per_block, dims_per_block, s, search=KVQ_GRIDS, alphabet_m=0,
+                    beam_width=0):
+    spec = KvqBlockSpec(tokens_per_block, dims_per_block, s, search, alphabet_m, beam_width)
     plan = KvqPlan()
     arr = _tensor_array(tensors)
     _check(lib().kvq_plan_blocks(arr, len(tensors), ctypes.byref(spec), ctypes.byref(plan)))

@@ -30,16 +30,17 @@ def to_cuda(arrays):
 
 
 def run_gpu(tensors, *, tokens_per_block, dims_per_block, s, search, alphabet_m=12, B, mode,
-            iters=40, eta=1e-3, lam=0.0, seed=0, dequant=True, tensors_dev=None, weights=None):
+            iters=40, eta=1e-3, lam=0.0, seed=0, dequant=True, tensors_dev=None, weights=None,
+            beam_width=0):
     """Run plan -> eval -> solve -> quantize -> dequantize through the C ABI
     and return every output as numpy (``weights``: per-block distortion
     weights, solved with kvq_solve_lambda_weighted)."""
     import torch
     from kv_cache_rate_amd import kvq
     dev = tensors_dev if tensors_dev is not None else to_cuda(tensors)
-    sm = kvq.KVQ_GRIDS if search == "grids" else kvq.KVQ_EXACT_DP
+    sm = {"grids": kvq.KVQ_GRIDS, "exact_dp": kvq.KVQ_EXACT_DP, "beam": kvq.KVQ_BEAM}[search]
     plan = kvq.kvq_plan_blocks(dev, tokens_per_block, dims_per_block, s, sm,
-                               alphabet_m if sm else 0)
+                               alphabet_m if sm else 0, beam_width if search == "beam" else 0)
     buf = kvq.allocate(plan, dequant=dequant)
     md = {"bisect": kvq.KVQ_BISECT, "subgrad": kvq.KVQ_SUBGRAD,
           "bisect_greedy": kvq.KVQ_BISECT_GREEDY}[mode]
@@ -69,11 +70,12 @@ def run_gpu(tensors, *, tokens_per_block, dims_per_block, s, search, alphabet_m=
 
 
 def run_oracle(tensors, *, tokens_per_block, dims_per_block, s, search, alphabet_m=12, B, mode,
-               iters=40, eta=1e-3, lam=0.0, seed=0, processes=None, weights=None):
+               iters=40, eta=1e-3, lam=0.0, seed=0, processes=None, weights=None, beam_width=0):
     b = oblocks.partition(tensors, tokens_per_block, dims_per_block)
     out = pipeline.run(b, search=search, s=s, alphabet_m=alphabet_m, B=B, mode=mode, iters=iters,
                        lam_prev=lam, eta=eta, seed=seed,
-                       processes=processes or pipeline.default_processes(), weights=weights)
+                       processes=processes or pipeline.default_processes(), weights=weights,
+                       beam_width=beam_width or None)
     out["blocks"] = b
     return out
 
@@ -124,7 +126,7 @@ def compare_choice(g, o, lam, d, weights=None):
     agree = np.zeros(R, dtype=bool)
     ties = 0
     max_gap = 0.0
-    if o.get("route") == "dp":
+    if o.get("route") in ("dp", "beam"):
         return compare_choice_dp(g, o, lam, d)
     Dw = o["D"] if weights is None else np.asarray(weights, dtype=np.float64)[:, None] * o["D"]
     obj = Dw + (lam * d) * o["H"]

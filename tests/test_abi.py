@@ -110,6 +110,25 @@ def test_plan_larger_alphabet(L):
     assert p.max_code_words == 2048 * (4096 * 4 // 32)
 
 
+def test_plan_beam(L):
+    """KVQ_BEAM plans like KVQ_EXACT_DP (same alphabet tables) and carries
+    its width; widths outside 1..8 and missing alphabets are rejected."""
+    t = np.zeros((1, 8, 8192, 128), dtype=np.float32)
+    p = kvq.kvq_plan_blocks([t], 256, 16, 16, kvq.KVQ_BEAM, 32, 4)
+    assert p.search == kvq.KVQ_BEAM and p.beam_width == 4
+    assert p.n_cand == 496 and p.n_stats == 32 and p.H_bytes == 2 * p.D_bytes
+    q = kvq.kvq_plan_blocks([t], 256, 16, 16, kvq.KVQ_EXACT_DP, 32)
+    assert q.beam_width == 0 and q.D_bytes == p.D_bytes
+    for width in (0, 9):
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kvq_plan_blocks([t], 256, 16, 16, kvq.KVQ_BEAM, 32, width)
+        assert e.value.status == kvq.KVQ_EINVAL and "beam_width" in e.value.detail
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_plan_blocks([t], 256, 16, 16, kvq.KVQ_BEAM, 0, 2)  # no alphabet
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_plan_blocks([t], 256, 16, 16, 3, 12)  # unknown search
+
+
 def test_calls_validate_before_launch(L):
     """Null pointers, mismatched tensors and short code buffers are refused on
     the host; nothing is launched so no GPU is needed."""
