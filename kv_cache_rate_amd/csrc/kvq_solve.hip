@@ -253,6 +253,45 @@ __device__ int build_grid_codebook(int c, const float* st, int64_t stride, const
     return m;
 }
 
+// One block's choice at multiplier lam (grid search): candidate, codebook,
+// levels and code words; returns the block's fixed-point rate.
+__device__ unsigned long long final_grid_block(int64_t r, const double* __restrict__ D,
+                                               const double* __restrict__ H, const double* __restrict__ wgt,
+                                               const float* __restrict__ stats, int64_t R, int C, int s,
+                                               int n, int shift, const RankTable& rt, bool err, double lam,
+                                               int32_t* __restrict__ choice, float* __restrict__ codebook,
+                                               uint8_t* __restrict__ m_out, uint64_t& words) {
+    if (err) {
+        // no feasible multiplier: leave a well-formed empty result
+        choice[r] = -1;
+        m_out[r] = 1;
+        for (int j = 0; j < s; ++j) codebook[r * s + j] = 0.0f;
+        words = 0;
+        return 0;
+    }
+    const double d = (double)n;
+    const double lamd = lam * d;
+    const double* Dr = D + r;
+    const double* Hr = H + r;
+    const double wr = wgt ? wgt[r] : 1.0;
+    double best = objective(wr * Dr[0], Hr[0], lamd);
+    int bc = 0;
+    for (int c = 1; c < C; ++c) {
+        const double o = objective(wr * Dr[c * R], Hr[c * R], lamd);
+        if (o < best) {
+            best = o;
+            bc = c;
+        }
+    }
+    float q[kMaxS];
+    const int m = build_grid_codebook(bc, stats + r, R, rt, n, q);
+    choice[r] = bc;
+    m_out[r] = (uint8_t)m;
+    for (int j = 0; j < s; ++j) codebook[r * s + j] = j < m ? q[j] : 0.0f;
+    words = ((uint64_t)n * (uint64_t)code_width(m) + 31u) / 32u;
+    return rate_fx(d, Hr[bc * R], shift);
+}
+
 __global__ void __launch_bounds__(kSolveThreads)
 final_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
                    const double* __restrict__ wgt, const float* __restrict__ stats, int64_t R,
@@ -264,35 +303,11 @@ final_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
     const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r == 0) off[0] = 0;
     unsigned long long v = 0;
-    if (r < R && h->err) {
-        // no feasible multiplier: leave a well-formed empty result
-        choice[r] = -1;
-        m_out[r] = 1;
-        for (int j = 0; j < s; ++j) codebook[r * s + j] = 0.0f;
-        off[r + 1] = 0;
-    } else if (r < R) {
-        const double d = (double)n;
-        const double lamd = h->lam_final * d;
-        const double* Dr = D + r;
-        const double* Hr = H + r;
-        const double wr = wgt ? wgt[r] : 1.0;
-        double best = objective(wr * Dr[0], Hr[0], lamd);
-        int bc = 0;
-        for (int c = 1; c < C; ++c) {
-            const double o = objective(wr * Dr[c * R], Hr[c * R], lamd);
-            if (o < best) {
-                best = o;
-                bc = c;
-            }
-        }
-        v = rate_fx(d, Hr[bc * R], shift);
-        float q[kMaxS];
-        const int m = build_grid_codebook(bc, stats + r, R, rt, n, q);
-        choice[r] = bc;
-        m_out[r] = (uint8_t)m;
-        for (int j = 0; j < s; ++j) codebook[r * s + j] = j < m ? q[j] : 0.0f;
-        const int w = code_width(m);
-        off[r + 1] = ((uint64_t)n * (uint64_t)w + 31u) / 32u;
+    if (r < R) {
+        uint64_t words;
+        v = final_grid_block(r, D, H, wgt, stats, R, C, s, n, shift, rt, h->err != 0, h->lam_final, choice,
+                             codebook, m_out, words);
+        off[r + 1] = words;
     }
     v = wave_sum_u64(v);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
@@ -934,6 +949,53 @@ greedy_apply_kernel(const double* __restrict__ D, const double* __restrict__ H,
 
 // ----------------------------------------------------------------- host ----
 
+// Up to kSmallR blocks (grid search) in one workgroup: the final choice,
+// the rate sum and the exclusive scan of the code words in one launch.  In
+// the subgradient mode it also does the header set-up of solve_init_kernel
+// (the blocks are chosen at lam_in), so the call is a single kernel.
+constexpr int kSmallR = 1024;
+
+__global__ void __launch_bounds__(kSmallR)
+final_grids_small_kernel(const double* __restrict__ D, const double* __restrict__ H,
+                         const double* __restrict__ wgt, const float* __restrict__ stats, int64_t R, int C,
+                         int s, int n, int shift, RankTable rt, WsHeader* h, int subgrad, double lam_in,
+                         int32_t* __restrict__ choice, float* __restrict__ codebook,
+                         uint8_t* __restrict__ m_out, uint64_t* __restrict__ off) {
+    __shared__ unsigned long long part[kSmallR / 64][2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool err = subgrad ? false : h->err != 0;
+    const double lam = subgrad ? lam_in : h->lam_final;
+    unsigned long long v = 0;
+    uint64_t words = 0;
+    if (tid < R)
+        v = final_grid_block(tid, D, H, wgt, stats, R, C, s, n, shift, rt, err, lam, choice, codebook, m_out,
+                             words);
+    const uint64_t inc = wave_incl_scan_u64(words);
+    v = wave_sum_u64(v);
+    if (lane == 63) part[wave][0] = inc;
+    if (lane == 0) part[wave][1] = v;
+    __syncthreads();
+    uint64_t pre = 0;
+    for (int w = 0; w < wave; ++w) pre += part[w][0];
+    if (tid < R) off[tid + 1] = pre + inc;
+    if (tid == 0) {
+        off[0] = 0;
+        unsigned long long t = 0;
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += part[w][1];
+        if (subgrad) {
+            h->phase = kPhaseSubgrad;
+            h->nlam = 0;
+            h->done = 1;
+            h->err = 0;
+            h->lam_final = lam_in;
+            h->pool_n = 0;
+            h->pool_overflow = 0;
+            h->swaps = 0;
+        }
+        h->rate_final = t;
+    }
+}
+
 hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D, const double* H,
                         const double* wgt, const float* stats, double B, int mode, int iters,
                         double lam_in,
@@ -955,6 +1017,14 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
     const bool grids = p.search == KVQ_GRIDS;
     const int bits_max = grids ? 6 : 1;
     const int dbl_n = grids ? kMaxLam - 1 : 8;
+    // few blocks (a decode step): choice, rate and offsets in one workgroup
+    const bool small = grids && R >= 1 && R <= kSmallR && mode != KVQ_BISECT_GREEDY;
+    const unsigned small_threads = (unsigned)((R + 63) / 64 * 64);
+    if (small && mode == KVQ_SUBGRAD) {
+        hipLaunchKernelGGL(final_grids_small_kernel, dim3(1), dim3(small_threads), 0, st, D, H, wgt, stats, R,
+                           p.n_cand, p.s, n, shift, rt, h, 1, lam_in, choice, codebook, m, off);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(solve_init_kernel, dim3(1), dim3(64), 0, st, h, mode, lam_in, Btot_fx, iters,
                        bits_max, dbl_n);
     // workgroups per block in an alphabet-search pass: the most multipliers
@@ -993,6 +1063,11 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
             for (int ps = 0; ps < passes; ++ps) rates_pass();
         }
     }
+    if (small) {
+        hipLaunchKernelGGL(final_grids_small_kernel, dim3(1), dim3(small_threads), 0, st, D, H, wgt, stats, R,
+                           p.n_cand, p.s, n, shift, rt, h, 0, 0.0, choice, codebook, m, off);
+        return hipGetLastError();
+    }
     if (p.search == KVQ_GRIDS) {
         hipLaunchKernelGGL(final_grids_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, wgt, stats,
                            R, p.n_cand, p.s, n, shift, rt, h, choice, codebook, m, off);
@@ -1018,6 +1093,7 @@ hipError_t launch_offsets_scan(uint64_t* off, int64_t R, void* ws, hipStream_t s
     uint64_t* tile_sums = (uint64_t*)((char*)ws + kWsHeaderBytes);
     hipLaunchKernelGGL(scan_tiles_kernel, dim3((unsigned)tiles), dim3(kSolveThreads), 0, st, off, R,
                        tile_sums);
+    if (tiles == 1) return hipGetLastError();  // one tile: its scan is the result
     hipLaunchKernelGGL(scan_sums_kernel, dim3(1), dim3(kSolveThreads), 0, st, tile_sums, tiles);
     hipLaunchKernelGGL(scan_add_kernel, dim3((unsigned)tiles), dim3(kSolveThreads), 0, st, off, R,
                        tile_sums);
