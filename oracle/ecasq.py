@@ -21,7 +21,7 @@ Everything is fp64 and follows the page "Rate-adaptive KV-cache quantizer"
 * Implementation notes: the candidate alphabet of a block is built from its
   minimum, maximum and quantiles, for codebook sizes k <= s.
 
-Readings taken where the pages are silent (listed again in the design doc):
+Readings taken where the pages are silent:
 
 * D_r is a sum over the block; H_r is bits per entry, so d_r H_r is bits per
   block and a per-entry budget B means a total of B * sum_r d_r.
