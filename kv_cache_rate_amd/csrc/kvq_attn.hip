@@ -15,7 +15,7 @@
 // Kernel 1: a workgroup takes (o, h, split of 16 chunks).  Thread (slot j,
 // feature group f) owns tokens j and j + 16 of every chunk and features
 // 8f..8f+7; it decodes its 8 K and 8 V entries per token, finishes the G dot
-// products with its 15 partners by xor shuffles, and keeps a running
+// products with its 15 partners by DPP row sums, and keeps a running
 // maximum, sum of weights and weighted V sum (online softmax) per query
 // head.  The 16 token slots are merged by log-sum-exp (shuffles inside a
 // wave, LDS across the 4 waves) into one partial per query head and split.
@@ -44,11 +44,25 @@ __device__ __forceinline__ uint32_t codes8(const uint32_t* cw, uint32_t nwords, 
     return (uint32_t)((((uint64_t)b << 32) | a) >> sh);
 }
 
+// Sum over a 16-lane row, the same bits in every lane: partner swaps inside
+// quads (lane ^ 1, lane ^ 2), then the half-row mirror (quad q <-> 1 - q)
+// and the row mirror (half h <-> 1 - h); each step adds a value to its
+// mirror image, so both partners round identically.  DPP moves, no LDS.
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float xor_sum16(float v) {
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    v += __shfl_xor(v, 8, 64);
+    v += dpp_f32<kDppQuadXor1>(v);
+    v += dpp_f32<kDppQuadXor2>(v);
+    v += dpp_f32<kDppRowHalfMirror>(v);
+    v += dpp_f32<kDppRowMirror>(v);
     return v;
 }
 
