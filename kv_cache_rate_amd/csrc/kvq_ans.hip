@@ -178,26 +178,88 @@ ans_compact_kernel(const uint16_t* __restrict__ scratch, const uint64_t* __restr
 }
 
 // Decode every block and write its codepoints (fp32, entries row-major).
-__global__ void __launch_bounds__(kAT)
+// A workgroup is one wave of 8 blocks.  The 8 blocks' coded bytes are
+// consecutive in the stream; when they fit kDecodeStage bytes the wave
+// first copies them into LDS with coalesced 4-byte loads, so the refills
+// that sit on every state update come from LDS; larger workgroups (over 2
+// coded bits per entry on average) refill from global memory.
+constexpr int kDB = 8;                    // blocks per decode workgroup
+constexpr int kDT = kDB * kAL;            // 64 threads
+constexpr uint32_t kDecodeStage = 8448;   // staged bytes per workgroup
+
+// The decode loop of one block's state i over a word stream wd (LDS or
+// global memory); false if the stream runs out or the state does not end
+// at its start value.
+template <typename WordPtr>
+__device__ __forceinline__ bool decode_steps(WordPtr wd, uint32_t nwd, const uint32_t* cum,
+                                             const uint32_t* frq, const float* q, int m, int n, int k,
+                                             int i, int lane, float* __restrict__ out) {
+    const uint32_t M = 1u << k;
+    uint32_t x = ((uint32_t)wd[m + 2 * i] << 16) | wd[m + 2 * i + 1];
+    uint32_t ptr = (uint32_t)m + 2 * kAL;
+    bool bad = false;
+    const int steps = (n + kAL - 1) / kAL;
+    for (int j = 0; j < steps; ++j) {
+        const int t = kAL * j + i;
+        const bool act = t < n;
+        const uint32_t slot = x & (M - 1u);
+        // last symbol with C_sym <= slot (C is padded with M past m)
+        uint32_t sym = 0;
+#pragma unroll
+        for (uint32_t h = kMaxS / 2; h; h >>= 1)
+            if (cum[sym + h] <= slot) sym += h;
+        if (act) x = frq[sym] * (x >> k) + slot - cum[sym];
+        const bool need = act && x < kStateLow;
+        const uint32_t bits = group_bits(__ballot(need), lane);
+        if (need) {
+            const uint32_t at = ptr + __popc(bits & ((1u << i) - 1u));
+            const uint32_t word = at < nwd ? wd[at] : 0u;
+            bad |= at >= nwd;
+            x = (x << 16) | word;
+        }
+        ptr += __popc(bits);
+        if (act) out[t] = q[sym];
+    }
+    return x == kStateLow && !bad;
+}
+
+__global__ void __launch_bounds__(kDT)
 ans_decode_kernel(const uint8_t* __restrict__ stream, const uint64_t* __restrict__ block_off,
                   const float* __restrict__ codebook, const uint8_t* __restrict__ m_in, int64_t R,
                   int n, int s, int k, float* __restrict__ xhat, WsHeader* ws) {
-    __shared__ uint32_t cum[kAB][kMaxS + 1];   // C_j, padded with 2^k
-    __shared__ uint32_t frq[kAB][kMaxS];
-    __shared__ float q[kAB][kMaxS];
+    __shared__ __align__(16) uint32_t lds_words[kDecodeStage / 4];
+    __shared__ uint32_t cum[kDB][kMaxS + 1];   // C_j, padded with 2^k
+    __shared__ uint32_t frq[kDB][kMaxS];
+    __shared__ float q[kDB][kMaxS];
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
     const int bl = tid >> 3;
     const int i = tid & 7;
-    const int64_t r = (int64_t)blockIdx.x * kAB + bl;
+    const int64_t r0 = (int64_t)blockIdx.x * kDB;
+    const int64_t r = r0 + bl;
     const bool valid = r < R;
+    const int64_t rl = min(r0 + kDB, R);          // one past the workgroup's last block
+    const uint64_t b0 = block_off[r0], b1 = block_off[rl];
+    // stage the workgroup's bytes (whole 4-byte words: block sizes are
+    // multiples of 4 and the stream is 4-byte aligned)
+    const bool staged = b1 - b0 <= kDecodeStage;
+    if (staged) {
+        const uint32_t nw = (uint32_t)((b1 - b0) / 4);
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(stream + b0);
+        for (uint32_t t = tid; t < nw; t += kDT) lds_words[t] = src[t];
+    }
     const int m = valid ? min(max((int)m_in[r], 1), s) : 1;
-    const uint16_t* wd = valid ? reinterpret_cast<const uint16_t*>(stream + block_off[r]) : nullptr;
     const uint32_t M = 1u << k;
+    __syncthreads();
+    const uint16_t* lw = staged ? reinterpret_cast<const uint16_t*>(lds_words)
+                                : reinterpret_cast<const uint16_t*>(stream + b0);
+    const uint64_t wbeg = valid ? (block_off[r] - b0) / 2 : 0;   // block start, in words
+    const uint64_t wend = valid ? (block_off[r + 1] - b0) / 2 : 0;
+    const uint16_t* wd = lw + wbeg;
+    const uint32_t nwd = (uint32_t)min(wend - wbeg, (uint64_t)0xffffffffu);
     if (valid && i == 0) {
         uint32_t c = 0;
         for (int j = 0; j < kMaxS; ++j) {
-            const uint32_t f = j < m ? wd[j] : 0u;
+            const uint32_t f = j < m && (uint32_t)j < nwd ? wd[j] : 0u;
             cum[bl][j] = j < m ? c : M;
             frq[bl][j] = f;
             q[bl][j] = j < m ? codebook[r * s + j] : 0.0f;
@@ -207,27 +269,16 @@ ans_decode_kernel(const uint8_t* __restrict__ stream, const uint64_t* __restrict
     }
     __syncthreads();
     if (!valid) return;
-    uint32_t x = ((uint32_t)wd[m + 2 * i] << 16) | wd[m + 2 * i + 1];
-    int64_t ptr = m + 2 * kAL;
-    const int steps = (n + kAL - 1) / kAL;
-    float* out = xhat + r * (int64_t)n;
-    for (int j = 0; j < steps; ++j) {
-        const int t = kAL * j + i;
-        const bool act = t < n;
-        const uint32_t slot = x & (M - 1u);
-        // last symbol with C_sym <= slot (C is padded with M past m)
-        uint32_t sym = 0;
-#pragma unroll
-        for (uint32_t h = kMaxS / 2; h; h >>= 1)
-            if (cum[bl][sym + h] <= slot) sym += h;
-        if (act) x = frq[bl][sym] * (x >> k) + slot - cum[bl][sym];
-        const bool need = act && x < kStateLow;
-        const uint32_t bits = group_bits(__ballot(need), lane);
-        if (need) x = (x << 16) | wd[ptr + __popc(bits & ((1u << i) - 1u))];
-        ptr += __popc(bits);
-        if (act) out[t] = q[bl][sym];
+    const uint32_t hdr = (uint32_t)m + 2 * kAL;
+    if (nwd < hdr) {
+        atomicOr(&ws->status, kStatusAnsCorrupt);
+        return;
     }
-    if (x != kStateLow) atomicOr(&ws->status, kStatusAnsCorrupt);
+    const bool ok = staged ? decode_steps(reinterpret_cast<const uint16_t*>(lds_words) + wbeg, nwd, cum[bl],
+                                          frq[bl], q[bl], m, n, k, i, tid & 63, xhat + r * (int64_t)n)
+                           : decode_steps(wd, nwd, cum[bl], frq[bl], q[bl], m, n, k, i, tid & 63,
+                                          xhat + r * (int64_t)n);
+    if (!ok) atomicOr(&ws->status, kStatusAnsCorrupt);
 }
 
 hipError_t launch_ans_encode(const uint32_t* codes, const uint8_t* m, const uint64_t* word_off,
@@ -252,8 +303,8 @@ hipError_t launch_ans_decode(const uint8_t* stream, const uint64_t* block_off, c
                              hipStream_t st) {
     if (R == 0) return hipSuccess;
     const int k = n <= 1 ? 1 : 32 - __builtin_clz((unsigned)(n - 1));
-    const unsigned grid = (unsigned)((R + kAB - 1) / kAB);
-    hipLaunchKernelGGL(ans_decode_kernel, dim3(grid), dim3(kAT), 0, st, stream, block_off, codebook, m, R,
+    const unsigned grid = (unsigned)((R + kDB - 1) / kDB);
+    hipLaunchKernelGGL(ans_decode_kernel, dim3(grid), dim3(kDT), 0, st, stream, block_off, codebook, m, R,
                        n, s, k, xhat, (WsHeader*)ws);
     return hipGetLastError();
 }
