@@ -80,14 +80,14 @@ ans_encode_kernel(const uint32_t* __restrict__ codes, const uint8_t* __restrict_
     const uint32_t nwords = (uint32_t)(w1 - w0);
     const int steps = (n + kAL - 1) / kAL;
     __syncthreads();
-    // ---- symbol counts
+    // ---- symbol counts: lane i takes steps i, i + 8, ... (all 8 codes of a
+    //      step from one read of the stream)
     if (valid) {
-        for (int j = 0; j < steps; ++j) {
-            const int t = kAL * j + i;
-            if (t < n) {
-                const uint32_t sym = w ? (step_bits(cw, nwords, w, j) >> (w * i)) & mask : 0u;
-                atomicAdd(&cnt[bl][sym], 1u);
-            }
+        for (int j = i; j < steps; j += kAL) {
+            const uint32_t b8 = w ? step_bits(cw, nwords, w, j) : 0u;
+#pragma unroll
+            for (int e = 0; e < kAL; ++e)
+                if (kAL * j + e < n) atomicAdd(&cnt[bl][(b8 >> (w * e)) & mask], 1u);
         }
     }
     __syncthreads();
@@ -118,10 +118,14 @@ ans_encode_kernel(const uint32_t* __restrict__ codes, const uint8_t* __restrict_
     int64_t ptr = (int64_t)(base + capw);
     uint32_t x = kStateLow;
     bool overflow = false;
+    // the stream bits of step j - 1 are read while step j is coded
+    uint32_t b_next = (w && steps > 0) ? step_bits(cw, nwords, w, steps - 1) : 0u;
     for (int j = steps - 1; j >= 0; --j) {
         const int t = kAL * j + i;
         const bool act = t < n;
-        const uint32_t sym = (act && w) ? (step_bits(cw, nwords, w, j) >> (w * i)) & mask : 0u;
+        const uint32_t b_cur = b_next;
+        if (w && j > 0) b_next = step_bits(cw, nwords, w, j - 1);
+        const uint32_t sym = (act && w) ? (b_cur >> (w * i)) & mask : 0u;
         const AnsSym e = tab[bl][sym];
         const bool emit = act && (x >> (32 - k)) >= e.f;
         const uint32_t bits = group_bits(__ballot(emit), lane);
@@ -172,9 +176,25 @@ ans_compact_kernel(const uint16_t* __restrict__ scratch, const uint64_t* __restr
     const uint64_t capw = (4u * (w1 - w0) + ans_margin_bytes(n)) / 2;
     const uint64_t start = base + reinterpret_cast<const uint32_t*>(scratch + base)[0];
     const uint64_t words = base + capw - start;
-    uint16_t* out = reinterpret_cast<uint16_t*>(stream + block_off[r]);
-    const uint64_t padded = (block_off[r + 1] - block_off[r]) / 2;
-    for (uint64_t q = threadIdx.x; q < padded; q += kAT) out[q] = q < words ? scratch[start + q] : 0;
+    // 4-byte units: the destination is 4-byte aligned, the source start may
+    // sit on a 2-byte boundary (then each unit straddles two aligned words)
+    uint32_t* out = reinterpret_cast<uint32_t*>(stream + block_off[r]);
+    const uint64_t units = (block_off[r + 1] - block_off[r]) / 4;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(scratch);
+    const uint64_t a0 = start >> 1;
+    const bool odd = start & 1u;
+    for (uint64_t q = threadIdx.x; q < units; q += kAT) {
+        uint32_t v;
+        if (2 * q + 1 < words) {
+            // both halves are data; with an odd start u16 start + 2q is the
+            // high half of word a0 + q (regions have even ends, so word
+            // a0 + q + 1 still lies inside this block's region)
+            v = odd ? __builtin_amdgcn_alignbit(src[a0 + q + 1], src[a0 + q], 16) : src[a0 + q];
+        } else {
+            v = scratch[start + 2 * q];   // the last data word, then the zero fill word
+        }
+        out[q] = v;
+    }
 }
 
 // Decode every block and write its codepoints (fp32, entries row-major).
