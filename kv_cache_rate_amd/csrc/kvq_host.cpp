@@ -159,8 +159,9 @@ kvq_status kvq_plan_blocks(const kvq_tensor* t, int32_t nt, const kvq_block_spec
     int64_t R = 0;
     for (int i = 0; i < nt; ++i) {
         if (t[i].dtype != p.dtype) return fail(KVQ_EINVAL, "tensors must share a dtype");
-        for (int d = 0; d < 4; ++d) {
+        for (int d = 0; d < 4; ++d)
             if (t[i].shape[d] <= 0) return fail(KVQ_EINVAL, "tensor %d: empty or negative dimension", i);
+        for (int d = 0; d < 4; ++d) {
             if (t[i].shape[d] != t[0].shape[d]) return fail(KVQ_EINVAL, "tensors must share a shape");
             if (t[i].stride[d] <= 0) return fail(KVQ_EINVAL, "tensor %d: non-positive stride", i);
             p.shape[i][d] = t[i].shape[d];

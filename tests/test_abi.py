@@ -98,6 +98,12 @@ def test_plan_rejects_bad_arguments(L):
         kvq.kvq_plan_blocks([t], 32, 128, 8, kvq.KVQ_EXACT_DP, 1)  # alphabet < 2
     with pytest.raises(ValueError):
         kvq.kvq_plan_blocks([t.astype(np.float64)], 32, 128, 16)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_plan_blocks([np.zeros((1, 2, 0, 128), dtype=np.float16)], 32, 128, 16)  # no tokens
+    assert e.value.status == kvq.KVQ_EINVAL and "empty" in e.value.detail
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_plan_blocks([], 32, 128, 16)  # no tensor
+    assert e.value.status == kvq.KVQ_EINVAL
 
 
 def test_plan_larger_alphabet(L):

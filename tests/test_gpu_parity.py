@@ -137,6 +137,21 @@ def test_ties_constant_and_negative_zero(kernel_path):
     assert g["m"][0] == 1 and g["off"][1] == 0
 
 
+@pytest.mark.parametrize("dtype,s,B,mode", [(np.float16, 16, 1.0, "bisect"), (np.float32, 8, 1.2, "bisect"),
+                                             (np.float16, 16, 2.0, "subgrad")])
+def test_single_block(dtype, s, B, mode):
+    """One block (R = 1): the solve's single-workgroup path, the bisection
+    on one block, and a subgradient step from a nonzero multiplier."""
+    rng = np.random.default_rng(41)
+    x = (rng.standard_normal((1, 1, 32, 128)) * 1.5).astype(dtype)
+    w = W.Workload(name="single", index=0, tensors=(("K", x.shape),), dtype="f16" if dtype == np.float16 else "f32",
+                   tokens_per_block=32, dims_per_block=128, s=s, search="grids", B=B, mode=mode)
+    g, o, rep = _check(w, [x], lam=0.37)
+    assert g["m"].shape == (1,)
+    if mode == "bisect":
+        assert g["lam"] > 0.0 and g["rate_per_entry"] <= B
+
+
 def test_strided_input():
     """A non-contiguous view (every other head of a larger tensor)."""
     import torch
