@@ -274,9 +274,11 @@ kvq_status kvq_ans_encode(const kvq_plan* p, const uint32_t* codes, const uint8_
                           void* workspace, uint64_t* total_bytes_out, hipStream_t s);
 
 /* Decode the coded stream and write each block's codepoints, fp32
-   xhat[r][t] = codebook[r][symbol] (decode before attention).  A block
-   whose states do not end at 2^16 (a damaged stream) sets a bit in the
-   workspace status word.  Asynchronous on stream s. */
+   xhat[r][t] = codebook[r][symbol] (decode before attention).  stream and
+   block_off as written by kvq_ans_encode (stream 4-byte aligned, else
+   KVQ_EINVAL).  A block whose states do not end at 2^16 or whose words run
+   out (a damaged stream) sets a bit in the workspace status word; reads
+   stay inside the block's bytes.  Asynchronous on stream s. */
 kvq_status kvq_ans_decode(const kvq_plan* p, const void* stream, const uint64_t* block_off,
                           const float* codebook, const uint8_t* m, float* xhat, void* workspace,
                           hipStream_t s);
