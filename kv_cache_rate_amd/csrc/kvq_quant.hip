@@ -119,7 +119,8 @@ dequantize_kernel(int n, int s, const uint32_t* __restrict__ codes, const float*
 
 // quantize: one wave per block, 8 chunks of 8 entries per lane (256 threads
 // with 2 chunks each was 10% slower: the per-block set-up is paid per wave);
-// dequantize: 256 threads, 2 chunks per lane
+// dequantize: 256 threads, lane t writing float4s t, t + 256, t + 512, t + 768
+// of its block, so every store instruction covers 4 KB without gaps
 constexpr int kQT = 64;
 constexpr int kDQT = 256;
 
@@ -241,22 +242,28 @@ dequantize4096_kernel(int s, const uint32_t* __restrict__ codes, const float* __
     if (tid < kMaxS) q[tid] = tid < m ? codebook[r * s + tid] : 0.0f;
     __syncthreads();
     const int w = code_width(m);
-    const uint8_t* in = reinterpret_cast<const uint8_t*>(codes + off[r]);
+    const uint32_t* cw = codes + off[r];
     const uint32_t mask = (1u << w) - 1u;
+    float4* o = reinterpret_cast<float4*>(xhat + r * 4096);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const int ch = tid + half * kDQT;
-        const uint32_t bits = w ? load_bytes(in + w * ch, w) : 0u;
-        float v[8];
+    for (int k = 0; k < 4; ++k) {
+        const int j = tid + k * kDQT;           // float4 j = entries 4j .. 4j + 3
+        uint32_t bits = 0;
+        if (w) {
+            const uint32_t b0 = 4u * (uint32_t)w * (uint32_t)j;
+            const uint32_t q0 = b0 >> 5, sh = b0 & 31u;
+            uint64_t win = cw[q0];
+            if (sh + 4u * (uint32_t)w > 32u) win |= (uint64_t)cw[q0 + 1] << 32;
+            bits = (uint32_t)(win >> sh);
+        }
+        float v[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 4; ++e) {
             int code = (int)((bits >> (w * e)) & mask);
             code = code < m ? code : m - 1;
             v[e] = q[code];
         }
-        float4* o = reinterpret_cast<float4*>(xhat + r * 4096 + 8 * ch);
-        o[0] = make_float4(v[0], v[1], v[2], v[3]);
-        o[1] = make_float4(v[4], v[5], v[6], v[7]);
+        o[j] = make_float4(v[0], v[1], v[2], v[3]);
     }
 }
 
