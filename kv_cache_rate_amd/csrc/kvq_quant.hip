@@ -109,18 +109,18 @@ dequantize_kernel(int n, int s, const uint32_t* __restrict__ codes, const float*
 }
 
 // ---------------------------------------------------------------------------
-// Blocks of 4096 contiguous entries.  Lane t of the 256-thread workgroup owns
-// the 8-entry chunks t and t + 256.  A chunk's eight w-bit codes are exactly
-// w bytes of the block's little-endian stream (chunk c at byte w c), so loads
-// are 16-byte coalesced and stores are byte-granular with no cross-lane
-// packing.  Codepoints live in LDS padded with +inf to 16 slots, so the
+// Blocks of 4096 contiguous entries.  In the quantizer lane t of the block's
+// wave owns the 8-entry chunks t, t + 64, ..., t + 448.  A chunk's eight
+// w-bit codes are exactly w bytes of the block's little-endian stream (chunk
+// c at byte w c), so loads are 16-byte coalesced and stores are
+// byte-granular with no cross-lane packing.  Codepoints live in LDS padded with +inf to 16 slots, so the
 // interval search is a fixed four-step binary search; p uses the reciprocal
 // of the interval width.
 
 // quantize: one wave per block, 8 chunks of 8 entries per lane (256 threads
 // with 2 chunks each was 10% slower: the per-block set-up is paid per wave);
 // dequantize: 256 threads, lane t writing float4s t, t + 256, t + 512, t + 768
-// of its block, so every store instruction covers 4 KB without gaps
+// of its block, so each wave store writes 1 KB without gaps
 constexpr int kQT = 64;
 constexpr int kDQT = 256;
 
