@@ -67,7 +67,10 @@ def algorithmic_bytes(plan, words_total, in_bytes_per_entry):
     }
 
 
-def load_traffic(kernel, sha):
+def load_profile(kernel, sha):
+    """The rocprofv3 record of a kernel in profiles/traffic.json (HBM bytes
+    and VALU instructions per launch), or None once the kernel's sources no
+    longer hash to the recorded value."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -78,7 +81,12 @@ def load_traffic(kernel, sha):
     k = rec.get(kernel)
     if not k or k.get("source_sha") != sha:
         return None
-    return k.get("bytes_per_launch")
+    return k
+
+
+# VALU issue peak: 256 CUs x 4 SIMDs, one wave64 VALU instruction per SIMD
+# every 4 cycles (16 lanes per cycle), at 2.4 GHz
+VALU_PEAK_WAVE_INSTR_PER_S = 256 * 4 * 2.4e9 / 4
 
 
 def copy_bandwidth(torch, nbytes=1 << 30, reps=5):
@@ -375,7 +383,8 @@ def main():
     dom = max(per, key=per.get)
     achieved = alg[dom] / (per[dom] * 1e-3) / 1e9
     sha = kernel_sources_sha()
-    traffic = load_traffic(dom, kernel_sources_sha(KERNEL_SOURCES[dom]))
+    prof = load_profile(dom, kernel_sources_sha(KERNEL_SOURCES[dom]))
+    traffic = prof.get("bytes_per_launch") if prof else None
     value = w.input_bytes / (ms_per_step * 1e-3) / 1e9
     admit_ms = per["eval"] + per["quantize_pack"]
     extras = {}
@@ -402,6 +411,7 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": alg[dom]},
         "kernels_ms": per,
+        "valu_issue": None,
         "eval_plus_quantize": {"ms": admit_ms,
                                "kv_GBps": w.input_bytes / (admit_ms * 1e-3) / 1e9,
                                "elements_per_s": w.n_entries / (admit_ms * 1e-3),
@@ -412,6 +422,14 @@ def main():
         "source_sha": sha,
         "kernel_source_sha": {k: kernel_sources_sha(v) for k, v in KERNEL_SOURCES.items()},
     }
+    if prof and prof.get("valu_wave_instructions_per_launch"):
+        ins = prof["valu_wave_instructions_per_launch"]
+        rate = ins / (per[dom] * 1e-3)
+        # the dominant kernel's second roof: VALU issue (profiled instruction
+        # count per launch over this run's kernel time)
+        rec["valu_issue"] = {"kernel": dom, "wave_instructions_per_launch": ins,
+                             "achieved_per_s": rate, "peak_per_s": VALU_PEAK_WAVE_INSTR_PER_S,
+                             "frac": rate / VALU_PEAK_WAVE_INSTR_PER_S}
     if extras:
         rec["copy_GBps"] = extras["copy_GBps"]
         rec["eval_plus_quantize"]["frac_of_copy"] = (alg["eval"] + alg["quantize_pack"]) / \
