@@ -46,7 +46,7 @@ constexpr int kW = kT / 64;        // waves per block
 constexpr int kPer = 16;           // entries per thread
 constexpr int kCL = 256;           // candidate-interval lanes
 constexpr int kNC = 1024;          // coarse bins
-constexpr int kMaxSlots = 144;     // every target and threshold bin fits
+constexpr int kMaxSlots = 112;     // claimed bins held at once (see the rounds below)
 constexpr int kFW = 32;            // per-key count words of a slot (64 x 16 bit)
 constexpr int kSW = 40;            // words per slot: 32 per-key + 8 group totals
 constexpr int kNU = 71;            // distinct interior uniform fractions, s = 16
@@ -56,6 +56,8 @@ constexpr int kPQ = kPU + kNU;     //   then uniform thresholds, then order stat
 constexpr int kNP = kPQ + kNQ;     // 146 points
 constexpr int kRows = 15;          // 16-lane rows of candidate intervals
 constexpr uint32_t kNoSlot = 0xffffffffu, kClaim = 0xfffffffeu;
+constexpr uint32_t kSlotOff = 0x3fffffffu;    // slot map: byte offset ...
+constexpr uint32_t kRound2 = 0x40000000u;     // ... | this bit for the second round
 constexpr uint32_t kCnt1 = 1u << 19;       // one entry in a packed (count, sum f) word
 constexpr uint32_t kLowF = kCnt1 - 1u;     // sum-of-f field
 constexpr uint32_t kNoLane = 0xffffu;      // lane without an interval
@@ -121,6 +123,20 @@ __device__ __forceinline__ uint32_t key_ceil(float t) {
     return key;
 }
 
+// Order-preserving 16-bit keys of the two fp16 values of a 32-bit word;
+// x + (+0) maps -0 to +0 and leaves every other value (NaN stays NaN).
+__device__ __forceinline__ uint32_t pair_keys(uint32_t hw, half2_t& hv) {
+    hv = __builtin_bit_cast(half2_t, hw) + (half2_t){(_Float16)0.0f, (_Float16)0.0f};
+    const uint32_t w = __builtin_bit_cast(uint32_t, hv);
+    const short2_t sg = __builtin_bit_cast(short2_t, w) >> (short2_t){15, 15};
+    const uint32_t msk = (__builtin_bit_cast(uint32_t, sg) & 0x7fff7fffu) | 0x80008000u;
+    return w ^ msk;
+}
+__device__ __forceinline__ uint32_t pair_keys(uint32_t hw) {
+    half2_t hv;
+    return pair_keys(hw, hv);
+}
+
 // 1/x to ~1 ulp: hardware reciprocal estimate and two Newton steps.
 __device__ __forceinline__ double recip(double x) {
     double r = __builtin_amdgcn_rcp(x);
@@ -168,11 +184,15 @@ __device__ __forceinline__ double point_entropy(double m, const double* lg_c, co
     return pi > 0.0 ? -pi * log2_unit(pi, lg_c, lg_inv) : 0.0;
 }
 
-// Claim a slot for coarse bin `bin` (first caller wins; the slot's byte
-// offset is visible after the next barrier).
+// Claim a slot for coarse bin `bin` (first caller wins; the slot's entry is
+// visible after the next barrier).  Claims past kMaxSlots are served by a
+// second round that reuses the slot memory: entry = byte offset | kRound2.
 __device__ __forceinline__ void claim_slot(Shared& sh, uint32_t bin) {
-    if (atomicCAS(&sh.slot[bin], kNoSlot, kClaim) == kNoSlot)
-        sh.slot[bin] = atomicAdd(&sh.nslots, 1u) * (uint32_t)(4 * kSW);
+    if (atomicCAS(&sh.slot[bin], kNoSlot, kClaim) == kNoSlot) {
+        const uint32_t k = atomicAdd(&sh.nslots, 1u);
+        sh.slot[bin] = k < (uint32_t)kMaxSlots ? k * (uint32_t)(4 * kSW)
+                                               : (k - kMaxSlots) * (uint32_t)(4 * kSW) | kRound2;
+    }
 }
 
 // 16-byte quad q of the slot at byte offset sb (q 0..7: per-key counts of
@@ -214,7 +234,7 @@ struct Eval16Tables {
     double lg_inv[64];              // 1 / (1 + (2i+1)/128)
 };
 
-__global__ void __launch_bounds__(kT, 5)
+__global__ void __launch_bounds__(kT, 6)
 eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int64_t nb0,
               Eval16Tables tb, double* __restrict__ Dout, double* __restrict__ Hout,
               float* __restrict__ stats, WsHeader* ws) {
@@ -251,12 +271,8 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     uint32_t keys2[kPer / 2];
 #pragma unroll
     for (int p = 0; p < kPer / 2; ++p) {
-        // x + (+0) maps -0 to +0 and leaves every other value (NaN stays NaN)
-        half2_t hv = __builtin_bit_cast(half2_t, hw[p]) + (half2_t){(_Float16)0.0f, (_Float16)0.0f};
-        const uint32_t w = __builtin_bit_cast(uint32_t, hv);
-        const short2_t sg = __builtin_bit_cast(short2_t, w) >> (short2_t){15, 15};
-        const uint32_t msk = (__builtin_bit_cast(uint32_t, sg) & 0x7fff7fffu) | 0x80008000u;
-        const uint32_t k2 = w ^ msk;  // order-preserving keys of both halves
+        half2_t hv;
+        const uint32_t k2 = pair_keys(hw[p], hv);  // order-preserving keys of both halves
         keys2[p] = k2;
         const ushort2_t kv = __builtin_bit_cast(ushort2_t, k2);
         kmin2 = __builtin_elementwise_min(kmin2, kv);
@@ -386,26 +402,40 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         sh.P[1].s1 = sh.u.a.ps1[kNC];
     }
     __syncthreads();
-    const uint32_t nslots = sh.nslots;  // <= 144 = kMaxSlots
-    for (uint32_t i = tid; i < nslots * (kSW / 4); i += kT)
+    const uint32_t nslots = sh.nslots;
+
+    // ---- sweep 2 and the in-bin finish, per round for the slots tagged
+    //      `tag` (the keys pass through an empty asm so that sweep 1's
+    //      payloads are recomputed here rather than held in registers across
+    //      the phases).
+    //      At most kNQ + kNU <= 2 kMaxSlots bins are claimed.  Up to kMaxSlots of
+    //      them fit the slot memory; a block with more (common for
+    //      unit-scale normal or Laplace data, not for data whose outliers
+    //      stretch the uniform grid) runs sweep 2 and the finish a second
+    //      time for the rest, with its keys recomputed from a second read
+    //      of the block.  kMaxSlots keeps the LDS at 6 workgroups per CU.
+    const int rounds = nslots > (uint32_t)kMaxSlots ? 2 : 1;
+    uint32_t k2s[kPer / 2];
+#pragma unroll
+    for (int p = 0; p < kPer / 2; ++p) k2s[p] = keys2[p];
+    for (int rnd = 0;; ++rnd) {
+    const uint32_t tag = rnd ? kRound2 : 0u;  // slot entries served this round
+    const uint32_t ns = rnd ? nslots - (uint32_t)kMaxSlots : min(nslots, (uint32_t)kMaxSlots);
+    for (uint32_t i = tid; i < ns * (kSW / 4); i += kT)
         reinterpret_cast<uint4*>(sh.u.b.w)[i] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
-
-    // ---- sweep 2: per-key counts and group totals in the claimed bins
-    //      (the keys pass through an empty asm so that sweep 1's payloads are
-    //      recomputed here rather than held in registers across the phases)
     uint32_t sl[kPer];
 #pragma unroll
     for (int p = 0; p < kPer / 2; ++p) {
-        asm volatile("" : "+v"(keys2[p]));
-        sl[2 * p] = sh.slot[(keys2[p] & 0xffffu) >> 6];
-        sl[2 * p + 1] = sh.slot[keys2[p] >> 22];
+        asm volatile("" : "+v"(k2s[p]));
+        sl[2 * p] = sh.slot[(k2s[p] & 0xffffu) >> 6];
+        sl[2 * p + 1] = sh.slot[k2s[p] >> 22];
     }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        if (sl[i] != kNoSlot) {
-            const uint32_t key = (i & 1) ? keys2[i >> 1] >> 16 : keys2[i >> 1];
-            char* base = reinterpret_cast<char*>(sh.u.b.w) + sl[i];
+        if ((sl[i] & ~kSlotOff) == tag) {  // kNoSlot has both high bits set
+            const uint32_t key = (i & 1) ? k2s[i >> 1] >> 16 : k2s[i >> 1];
+            char* base = reinterpret_cast<char*>(sh.u.b.w) + (sl[i] & kSlotOff);
             // key (f = key & 63) counts 1 in the 16-bit half f & 1 of word f >> 1
             atomicAdd(reinterpret_cast<uint32_t*>(base + ((key & 62u) << 1)),
                       1u + (key & 1u) * 0xffffu);
@@ -414,11 +444,12 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         }
     }
     __syncthreads();
-
     // ---- finish the prefixes inside the bins
-    if (tid < kNQ) {
+    const uint32_t sv = tid < kNQ ? sh.slot[sh.tbin[tid]]
+                      : (tid >= 128 && tid < 128 + kNU ? sh.slot[sh.ukey[tid - 128] >> 6] : kNoSlot);
+    const uint32_t s = sv & kSlotOff;
+    if (tid < kNQ && (sv & ~kSlotOff) == tag) {
         const uint32_t bin = sh.tbin[tid];
-        const uint32_t s = sh.slot[bin];
         const uint32_t loc = sh.tloc[tid];
         const uint4 ga = slot_quad(sh, s, 8), gb = slot_quad(sh, s, 9);
         // group holding local rank loc: groups whose running count <= loc
@@ -453,12 +484,11 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         sh.P[kPQ + tid].cnt += N;
         if (N) sh.P[kPQ + tid].s1 += (double)B * (double)N + (double)U * (double)F;
         stats[tid * R + r] = v;
-    } else if (tid >= 128 && tid < 128 + kNU) {
+    } else if (tid >= 128 && tid < 128 + kNU && (sv & ~kSlotOff) == tag) {
         const int u = tid - 128;
         const uint32_t key = sh.ukey[u];
         const uint32_t bin = key >> 6;
-        const uint32_t s = sh.slot[bin];
-        if (s != kNoSlot) {
+        {
             const uint32_t f = key & 63u;
             const uint32_t gs = f >> 3, fs = f & 7u;
             const uint4 ga = slot_quad(sh, s, 8), gb = slot_quad(sh, s, 9);
@@ -479,7 +509,16 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
             if (N) sh.P[kPU + u].s1 += (double)B * (double)N + (double)U * (double)F;
         }
     }
-    __syncthreads();  // phase-B storage is reused below
+    __syncthreads();  // phase-B storage is reused by the next round or below
+    if (rnd + 1 >= rounds) break;
+    {
+        const uint4 a = reinterpret_cast<const uint4*>(src)[tid];
+        const uint4 b = reinterpret_cast<const uint4*>(src)[256 + tid];
+        const uint32_t hw2[kPer / 2] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int p = 0; p < kPer / 2; ++p) k2s[p] = pair_keys(hw2[p]);
+    }
+    }
 
     // ---- candidate intervals, one per lane: masses to both ends, the
     //      distortion term a^2 M_a + b^2 M_b and the entropy term of the

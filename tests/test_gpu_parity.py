@@ -152,6 +152,20 @@ def test_single_block(dtype, s, B, mode):
         assert g["lam"] > 0.0 and g["rate_per_entry"] <= B
 
 
+def test_many_threshold_bins(kernel_path):
+    """Log-uniform fp16 data (magnitudes over 2^-11 .. 2^11, random signs):
+    the order statistics and the uniform thresholds of a block fall in
+    more distinct coarse bins (about 127) than the fp16 scoring kernel
+    holds at once, so it scores them in two rounds."""
+    rng = np.random.default_rng(43)
+    mag = np.exp2(rng.uniform(-11.0, 11.0, size=(1, 4, 128, 128)))
+    x = (mag * rng.choice([-1.0, 1.0], size=mag.shape)).astype(np.float16)
+    w = W.Workload(name="many_bins", index=0, tensors=(("K", x.shape),), dtype="f16",
+                   tokens_per_block=32, dims_per_block=128, s=16, search="grids", B=1.5,
+                   mode="bisect")
+    _check(w, [x])
+
+
 def test_strided_input():
     """A non-contiguous view (every other head of a larger tensor)."""
     import torch
