@@ -308,8 +308,11 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     // ---- coarse prefix: thread owns bins [4 tid, 4 tid + 4) = keys
     //      [256 tid, 256 tid + 256), one binade: value = B0 + (key offset) U
     {
-        const float B0 = key_value((uint32_t)tid << 8);
-        const double U = (double)(key_value(((uint32_t)tid << 8) | 1u) - B0);
+        // the Inf/NaN code bins (threads 0..3, 252..255) get base and ulp 0:
+        // they hold no finite entry, so every prefix term they add is 0
+        const bool finite_bins = tid >= 4 && tid < kT - 4;
+        const float B0 = finite_bins ? key_value((uint32_t)tid << 8) : 0.0f;
+        const double U = finite_bins ? (double)(key_value(((uint32_t)tid << 8) | 1u) - B0) : 0.0;
         const uint4 pw = reinterpret_cast<const uint4*>(sh.u.a.cnt)[tid];
         const uint32_t c[4] = {pw.x >> 19, pw.y >> 19, pw.z >> 19, pw.w >> 19};
         const uint32_t acc[4] = {pw.x & kLowF, 64u * c[1] + (pw.y & kLowF),
@@ -317,8 +320,7 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         const uint32_t ct = (c[0] + c[1]) + (c[2] + c[3]);
         const uint32_t at = (acc[0] + acc[1]) + (acc[2] + acc[3]);
         if ((tid < 4 || tid >= kT - 4) && ct != 0u) atomicOr(&ws->status, kStatusNonFinite);
-        // empty threads add exactly 0 (the Inf/NaN code bins have no finite base)
-        const double st = ct ? (double)ct * (double)B0 + U * (double)at : 0.0;
+        const double st = (double)ct * (double)B0 + U * (double)at;
         const uint32_t ic = wave_scan_add_u32(ct);
         const double is = wave_scan_add_f64(st);
         if (lane == 63) {
@@ -329,10 +331,9 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         const int wv = __builtin_amdgcn_readfirstlane(wave);
         uint32_t oc = 0;
         double os = 0.0;
-#pragma unroll
-        for (int w = 0; w < kW - 1; ++w) {
-            oc += w < wv ? sh.wtot[w] : 0u;
-            os += w < wv ? sh.wts1[w] : 0.0;
+        for (int w = 0; w < wv; ++w) {  // uniform trip count
+            oc += sh.wtot[w];
+            os += sh.wts1[w];
         }
         const uint32_t base_c = oc + ic - ct;
         const double base_s = os + (is - st);
@@ -342,7 +343,7 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             pc[k] = base_c + runc;
-            ps[k] = runc ? base_s + (double)runc * (double)B0 + U * (double)runa : base_s;
+            ps[k] = base_s + (double)runc * (double)B0 + U * (double)runa;
             runc += c[k];
             runa += acc[k];
         }
