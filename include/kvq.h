@@ -24,8 +24,11 @@
  *
  * Conventions for every entry point:
  *   - Device pointers are HIP device memory owned by the caller; the library
- *     allocates no device memory and keeps no global state.  Sizes of every
- *     buffer come from kvq_plan (filled by kvq_plan_blocks).
+ *     allocates no device memory.  Its only state is one 8 KB pinned host
+ *     buffer per calling thread (hipHostMalloc on first use, kept until the
+ *     process ends) through which the synchronising calls read back their
+ *     small results.  Sizes of every buffer come from kvq_plan (filled by
+ *     kvq_plan_blocks).
  *   - Host pointers are marked "(host)".
  *   - Arguments are validated on the host before any launch; a failed check
  *     returns KVQ_EINVAL or KVQ_ENOSPC and launches nothing.  Calls are

@@ -309,6 +309,12 @@ hipError_t launch_eval16(const void* x0, const void* x1, int64_t nb0, int64_t R,
 hipError_t launch_eval_alphabet(const Geom& g, int64_t R, int alpha_m, double* D, double* H,
                                 float* stats, void* ws, hipStream_t st);
 hipError_t launch_ws_reset(void* ws, hipStream_t st);
+// Read `bytes` (<= kStagingBytes) of device memory into host memory `dst`
+// on stream st and wait for it, through the calling thread's pinned staging
+// buffer (hipHostMalloc'd on first use and kept until the process ends; a
+// plain pageable copy if the allocation fails).
+constexpr size_t kStagingBytes = 8192;
+hipError_t read_back(void* dst, const void* src, size_t bytes, hipStream_t st);
 hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
                         const double* H, const double* wgt, const float* stats, double B,
                         int mode, int iters,

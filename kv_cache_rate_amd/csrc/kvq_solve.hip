@@ -1052,8 +1052,7 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
         // lambda = 0 first; the bracket passes run only when it is infeasible
         rates_pass();
         int32_t done = 0;
-        hipError_t e = hipMemcpyAsync(&done, &h->done, sizeof done, hipMemcpyDeviceToHost, st);
-        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        const hipError_t e = read_back(&done, &h->done, sizeof done, st);
         if (e != hipSuccess) return e;
         if (!done) {
             // doubling passes up to 2^62, the 2^63 / 2^64 pass if needed,
