@@ -46,7 +46,7 @@ constexpr int kW = kT / 64;        // waves per block
 constexpr int kPer = 16;           // entries per thread
 constexpr int kCL = 256;           // candidate-interval lanes
 constexpr int kNC = 1024;          // coarse bins
-constexpr int kMaxSlots = 112;     // claimed bins held at once (see the rounds below)
+constexpr int kSlotsLarge = 112;   // claimed bins held at once in large launches (see the rounds below)
 constexpr int kFW = 32;            // per-key count words of a slot (64 x 16 bit)
 constexpr int kSW = 40;            // words per slot: 32 per-key + 8 group totals
 constexpr int kNU = 71;            // distinct interior uniform fractions, s = 16
@@ -54,6 +54,8 @@ constexpr int kNQ = 73;            // order statistics, s = 16, n = 4096
 constexpr int kPU = 2;             // point table: 0 = min, 1 = max,
 constexpr int kPQ = kPU + kNU;     //   then uniform thresholds, then order statistics
 constexpr int kNP = kPQ + kNQ;     // 146 points
+constexpr int kSlotsAll = kNQ + kNU;   // 144: every claimable bin (small launches)
+constexpr int64_t kEvalSmallLaunch = 16384;  // blocks below which kSlotsAll is used
 constexpr int kRows = 15;          // 16-lane rows of candidate intervals
 constexpr uint32_t kNoSlot = 0xffffffffu, kClaim = 0xfffffffeu;
 constexpr uint32_t kSlotOff = 0x3fffffffu;    // slot map: byte offset ...
@@ -73,8 +75,9 @@ struct PhaseA {                    // sweep 1 .. threshold search
     uint32_t cnt[kNC + 4];         // payload, then exclusive prefix counts
     double ps1[kNC + 1];           // exclusive prefix sums
 };
+template <int kSlots>
 struct PhaseB {                    // sweep 2 .. prefix finish
-    uint32_t w[kMaxSlots * kSW];
+    uint32_t w[kSlots * kSW];
 };
 struct PhaseC {                    // candidate intervals
     double dterm[kCL];
@@ -84,10 +87,11 @@ struct PhaseC {                    // candidate intervals
     float bv[kCL];                 // right point
 };
 
+template <int kSlots>
 struct Shared {
     union alignas(16) {
         PhaseA a;
-        PhaseB b;
+        PhaseB<kSlots> b;
         PhaseC c;
     } u;
     alignas(16) uint32_t slot[kNC];  // bin -> byte offset of its slot, or kNoSlot
@@ -185,19 +189,21 @@ __device__ __forceinline__ double point_entropy(double m, const double* lg_c, co
 }
 
 // Claim a slot for coarse bin `bin` (first caller wins; the slot's entry is
-// visible after the next barrier).  Claims past kMaxSlots are served by a
+// visible after the next barrier).  Claims past kSlots are served by a
 // second round that reuses the slot memory: entry = byte offset | kRound2.
-__device__ __forceinline__ void claim_slot(Shared& sh, uint32_t bin) {
+template <int kSlots>
+__device__ __forceinline__ void claim_slot(Shared<kSlots>& sh, uint32_t bin) {
     if (atomicCAS(&sh.slot[bin], kNoSlot, kClaim) == kNoSlot) {
         const uint32_t k = atomicAdd(&sh.nslots, 1u);
-        sh.slot[bin] = k < (uint32_t)kMaxSlots ? k * (uint32_t)(4 * kSW)
-                                               : (k - kMaxSlots) * (uint32_t)(4 * kSW) | kRound2;
+        sh.slot[bin] = k < (uint32_t)kSlots ? k * (uint32_t)(4 * kSW)
+                                            : (k - kSlots) * (uint32_t)(4 * kSW) | kRound2;
     }
 }
 
 // 16-byte quad q of the slot at byte offset sb (q 0..7: per-key counts of
 // group q; 8, 9: the group totals).
-__device__ __forceinline__ uint4 slot_quad(const Shared& sh, uint32_t sb, uint32_t q) {
+template <int kSlots>
+__device__ __forceinline__ uint4 slot_quad(const Shared<kSlots>& sh, uint32_t sb, uint32_t q) {
     const char* p = reinterpret_cast<const char*>(sh.u.b.w) + sb + 16u * q;
     return *reinterpret_cast<const uint4*>(__builtin_assume_aligned(p, 16));
 }
@@ -234,11 +240,15 @@ struct Eval16Tables {
     double lg_inv[64];              // 1 / (1 + (2i+1)/128)
 };
 
-__global__ void __launch_bounds__(kT, 6)
+// kSlots = kSlotsAll (one round, 5 workgroups per CU) for small launches,
+// where a block's latency matters; kSlotsLarge (6 workgroups per CU) for
+// large ones, where throughput does.
+template <int kSlots>
+__global__ void __launch_bounds__(kT, kSlots == kSlotsAll ? 5 : 6)
 eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int64_t nb0,
               Eval16Tables tb, double* __restrict__ Dout, double* __restrict__ Hout,
               float* __restrict__ stats, WsHeader* ws) {
-    __shared__ Shared sh;
+    __shared__ Shared<kSlots> sh;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -409,19 +419,19 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     //      `tag` (the keys pass through an empty asm so that sweep 1's
     //      payloads are recomputed here rather than held in registers across
     //      the phases).
-    //      At most kNQ + kNU <= 2 kMaxSlots bins are claimed.  Up to kMaxSlots of
+    //      At most kNQ + kNU <= 2 kSlots bins are claimed.  Up to kSlots of
     //      them fit the slot memory; a block with more (common for
     //      unit-scale normal or Laplace data, not for data whose outliers
     //      stretch the uniform grid) runs sweep 2 and the finish a second
     //      time for the rest, with its keys recomputed from a second read
-    //      of the block.  kMaxSlots keeps the LDS at 6 workgroups per CU.
-    const int rounds = nslots > (uint32_t)kMaxSlots ? 2 : 1;
+    //      of the block.  kSlotsLarge keeps the LDS at 6 workgroups per CU.
+    const int rounds = nslots > (uint32_t)kSlots ? 2 : 1;
     uint32_t k2s[kPer / 2];
 #pragma unroll
     for (int p = 0; p < kPer / 2; ++p) k2s[p] = keys2[p];
     for (int rnd = 0;; ++rnd) {
     const uint32_t tag = rnd ? kRound2 : 0u;  // slot entries served this round
-    const uint32_t ns = rnd ? nslots - (uint32_t)kMaxSlots : min(nslots, (uint32_t)kMaxSlots);
+    const uint32_t ns = rnd ? nslots - (uint32_t)kSlots : min(nslots, (uint32_t)kSlots);
     for (uint32_t i = tid; i < ns * (kSW / 4); i += kT)
         reinterpret_cast<uint4*>(sh.u.b.w)[i] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
@@ -674,7 +684,11 @@ hipError_t launch_eval16(const void* x0, const void* x1, int64_t nb0, int64_t R,
         tb.lg_c[i] = log2(c);
         tb.lg_inv[i] = 1.0 / c;
     }
-    hipLaunchKernelGGL(eval16_kernel, dim3((unsigned)R), dim3(kT), 0, st, (const __half*)x0,
+    if (R < kEvalSmallLaunch)
+        hipLaunchKernelGGL(eval16_kernel<kSlotsAll>, dim3((unsigned)R), dim3(kT), 0, st, (const __half*)x0,
+                       (const __half*)x1, nb0, tb, D, H, stats, (WsHeader*)ws);
+    else
+        hipLaunchKernelGGL(eval16_kernel<kSlotsLarge>, dim3((unsigned)R), dim3(kT), 0, st, (const __half*)x0,
                        (const __half*)x1, nb0, tb, D, H, stats, (WsHeader*)ws);
     return hipGetLastError();
 }

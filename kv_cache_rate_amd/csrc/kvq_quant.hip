@@ -117,11 +117,15 @@ dequantize_kernel(int n, int s, const uint32_t* __restrict__ codes, const float*
 // interval search is a fixed four-step binary search; p uses the reciprocal
 // of the interval width.
 
-// quantize: one wave per block, 8 chunks of 8 entries per lane (256 threads
-// with 2 chunks each was 10% slower: the per-block set-up is paid per wave);
+// quantize: one wave per block, 8 chunks of 8 entries per lane, when the
+// launch has blocks enough to fill the GPU (256 threads with 2 chunks each
+// was 10% slower there: the per-block set-up is paid per wave); 256 threads
+// for small launches (a decode step), where a block's latency dominates.
 // dequantize: 256 threads, lane t writing float4s t, t + 256, t + 512, t + 768
 // of its block, so each wave store writes 1 KB without gaps
 constexpr int kQT = 64;
+constexpr int kQTSmall = 256;
+constexpr int64_t kQSmallLaunch = 16384;  // blocks below which kQTSmall is used
 constexpr int kDQT = 256;
 
 __device__ __forceinline__ void load8(const void* src, int dtype, int64_t e0, float* x) {
@@ -170,7 +174,8 @@ __device__ __forceinline__ uint32_t load_bytes(const uint8_t* src, int w) {
     }
 }
 
-__global__ void __launch_bounds__(kQT)
+template <int kThreads>
+__global__ void __launch_bounds__(kThreads)
 quantize4096_kernel(const void* __restrict__ x0, const void* __restrict__ x1, int64_t nb0, int dtype,
                     int s, const float* __restrict__ codebook, const uint8_t* __restrict__ m_in,
                     const uint64_t* __restrict__ off, uint32_t k0, uint32_t k1,
@@ -193,8 +198,8 @@ quantize4096_kernel(const void* __restrict__ x0, const void* __restrict__ x1, in
     uint8_t* out = reinterpret_cast<uint8_t*>(codes + off[r]);
     const uint32_t rlo = (uint32_t)r, rhi = (uint32_t)((uint64_t)r >> 32);
 #pragma unroll
-    for (int half = 0; half < 512 / kQT; ++half) {
-        const int ch = tid + half * kQT;
+    for (int half = 0; half < 512 / kThreads; ++half) {
+        const int ch = tid + half * kThreads;
         float x[8];
         load8(src, dtype, e_base + 8 * ch, x);
         uint32_t wd[8];
@@ -285,9 +290,15 @@ hipError_t launch_quantize(const Geom& g, int64_t R, int s, const float* codeboo
                            const uint64_t* off, uint64_t seed, uint32_t* codes, hipStream_t st) {
     if (R == 0) return hipSuccess;
     if (fast_layout(g)) {
-        hipLaunchKernelGGL(quantize4096_kernel, dim3((unsigned)R), dim3(kQT), 0, st, g.data[0],
-                           g.data[1] ? g.data[1] : g.data[0], g.nb0, g.dtype, s, codebook, m, off,
-                           (uint32_t)seed, (uint32_t)(seed >> 32), codes);
+        const void* x1 = g.data[1] ? g.data[1] : g.data[0];
+        if (R < kQSmallLaunch)
+            hipLaunchKernelGGL(quantize4096_kernel<kQTSmall>, dim3((unsigned)R), dim3(kQTSmall), 0, st,
+                               g.data[0], x1, g.nb0, g.dtype, s, codebook, m, off, (uint32_t)seed,
+                               (uint32_t)(seed >> 32), codes);
+        else
+            hipLaunchKernelGGL(quantize4096_kernel<kQT>, dim3((unsigned)R), dim3(kQT), 0, st, g.data[0],
+                               x1, g.nb0, g.dtype, s, codebook, m, off, (uint32_t)seed,
+                               (uint32_t)(seed >> 32), codes);
     } else {
         hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)R), dim3(kQuantThreads), 0, st, g, s,
                            codebook, m, off, (uint32_t)seed, (uint32_t)(seed >> 32), codes);
