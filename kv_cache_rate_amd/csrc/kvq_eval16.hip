@@ -141,6 +141,22 @@ __device__ __forceinline__ uint32_t pair_keys(uint32_t hw) {
     return pair_keys(hw, hv);
 }
 
+// Fixed instruction forms for sweep 2's per-entry address arithmetic (the
+// compiler rewrites the builtins into longer shift/mask sequences).
+// (x >> off) & ((1 << w) - 1), off and w immediate:
+template <uint32_t kOff, uint32_t kWid>
+__device__ __forceinline__ uint32_t bfe_u32(uint32_t x) {
+    uint32_t r;
+    asm("v_bfe_u32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "i"(kOff), "i"(kWid));
+    return r;
+}
+// a * b + c on the low 24 bits of a and b:
+__device__ __forceinline__ uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t r;
+    asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(b), "i"(c));
+    return r;
+}
+
 // 1/x to ~1 ulp: hardware reciprocal estimate and two Newton steps.
 __device__ __forceinline__ double recip(double x) {
     double r = __builtin_amdgcn_rcp(x);
@@ -444,14 +460,29 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        if ((sl[i] & ~kSlotOff) == tag) {  // kNoSlot has both high bits set
-            const uint32_t key = (i & 1) ? k2s[i >> 1] >> 16 : k2s[i >> 1];
-            char* base = reinterpret_cast<char*>(sh.u.b.w) + (sl[i] & kSlotOff);
-            // key (f = key & 63) counts 1 in the 16-bit half f & 1 of word f >> 1
-            atomicAdd(reinterpret_cast<uint32_t*>(base + ((key & 62u) << 1)),
-                      1u + (key & 1u) * 0xffffu);
-            atomicAdd(reinterpret_cast<uint32_t*>(base + 4 * kFW + ((key >> 1) & 28u)),
-                      (key & 63u) + kCnt1);
+        // served this round iff the entry's two high bits equal `tag`; then
+        // so is the slot's byte offset (kNoSlot ^ tag has a high bit set)
+        const uint32_t so = sl[i] ^ tag;
+        if (so < kRound2) {
+            // key f = bits [kb, kb + 6) of the word holding both keys; it
+            // counts 1 in the 16-bit half f & 1 of word f >> 1 of the
+            // slot, and (1, f) in the total of its 8-key group f >> 3
+            const uint32_t k2 = k2s[i >> 1];
+            uint32_t cword, one, gword, gval;
+            if (i & 1) {
+                cword = bfe_u32<17, 5>(k2);
+                one = mad_u24(bfe_u32<16, 1>(k2), 0xffffu, 1u);
+                gword = bfe_u32<19, 3>(k2);
+                gval = bfe_u32<16, 6>(k2) | kCnt1;
+            } else {
+                cword = bfe_u32<1, 5>(k2);
+                one = mad_u24(k2 & 1u, 0xffffu, 1u);
+                gword = bfe_u32<3, 3>(k2);
+                gval = (k2 & 63u) | kCnt1;
+            }
+            uint32_t* slotw = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(sh.u.b.w) + so);
+            atomicAdd(slotw + cword, one);
+            atomicAdd(slotw + kFW + gword, gval);
         }
     }
     __syncthreads();
