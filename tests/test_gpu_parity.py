@@ -155,8 +155,9 @@ def test_single_block(dtype, s, B, mode):
 def test_many_threshold_bins(kernel_path):
     """Log-uniform fp16 data (magnitudes over 2^-11 .. 2^11, random signs):
     the order statistics and the uniform thresholds of a block fall in
-    more distinct coarse bins (about 127) than the fp16 scoring kernel
-    holds at once, so it scores them in two rounds."""
+    about 127 distinct coarse bins, more than a large launch holds at
+    once; this small launch holds all 144 and scores them in one round
+    (the two-round case is the next test)."""
     rng = np.random.default_rng(43)
     mag = np.exp2(rng.uniform(-11.0, 11.0, size=(1, 4, 128, 128)))
     x = (mag * rng.choice([-1.0, 1.0], size=mag.shape)).astype(np.float16)
@@ -164,6 +165,75 @@ def test_many_threshold_bins(kernel_path):
                    tokens_per_block=32, dims_per_block=128, s=16, search="grids", B=1.5,
                    mode="bisect")
     _check(w, [x])
+
+
+def _fp16_keys(v):
+    """Order-preserving 16-bit keys of fp16 values (-0 as +0)."""
+    h = np.asarray(v, dtype=np.float16).view(np.uint16).astype(np.int64)
+    h = np.where(h == 0x8000, 0, h)
+    return np.where(h & 0x8000, 0xFFFF ^ h, h | 0x8000)
+
+
+def _key_value(key):
+    h = (key & 0x7FFF) if key & 0x8000 else (0xFFFF ^ key)
+    return float(np.array([h], dtype=np.uint16).view(np.float16)[0])
+
+
+def _claimed_bins(x, s):
+    """Coarse bins (top 10 key bits) that the fp16 scoring kernel gives a
+    slot: every bin holding an order statistic, and every bin holding data
+    and the smallest fp16 key at or above a uniform threshold."""
+    flat = np.asarray(x, dtype=np.float16).ravel()
+    data_bins = set((_fp16_keys(flat) >> 6).tolist())
+    xs = np.sort(flat.astype(np.float64))
+    stats = xs[ecasq.quantile_ranks(xs.size, s)]
+    claimed = set((_fp16_keys(stats) >> 6).tolist())
+    for k in range(3, s + 1):
+        for t in ecasq.uniform_points(xs[0], xs[-1], k)[1:-1]:
+            key = int(_fp16_keys(np.float16(t)))
+            if _key_value(key) < t:
+                key += 1
+            if (key >> 6) in data_bins:
+                claimed.add(key >> 6)
+    return claimed
+
+
+def test_two_slot_rounds_in_large_launches():
+    """16384 log-uniform fp16 blocks: a launch this large holds 112 slots
+    per block, and these blocks claim more (checked here from the oracle's
+    points), so the scoring kernel finishes them in two rounds.  The
+    eval tables of sampled blocks are compared with the oracle's."""
+    import torch
+    from kv_cache_rate_amd import kvq
+    rng = np.random.default_rng(47)
+    shape = (2, 8, 32768, 128)
+    x = np.exp2(rng.uniform(-11.0, 11.0, size=shape)).astype(np.float16)
+    x *= rng.choice(np.array([-1.0, 1.0], dtype=np.float16), size=shape)
+    t = [torch.from_numpy(x).cuda()]
+    plan = kvq.kvq_plan_blocks(t, 32, 128, 16)
+    R = plan.n_blocks
+    assert R == 16384
+    buf = kvq.allocate(plan)
+    _say(f"two slot rounds: eval of {R} blocks")
+    kvq.kvq_eval_candidates(plan, t, buf["D"], buf["H"], buf["stats"], buf["workspace"])
+    torch.cuda.synchronize()
+    D = buf["D"].cpu().numpy()
+    H = buf["H"].cpu().numpy()
+    stats = buf["stats"].cpu().numpy()
+    sample = sorted(set([0, 1, R // 2, R - 1] + rng.integers(0, R, size=44).tolist()))
+    over = 0
+    for r in sample:
+        xb = oblocks.block_of([x], 32, 128, r)
+        if len(_claimed_bins(xb, 16)) > 112:
+            over += 1
+        Do, Ho, So, _ = ecasq.eval_block(xb.astype(np.float64), 16)
+        floor = 1e-9 * max(Do.max(), 1e-300) / parity.D_RTOL
+        eD = np.max(np.abs(D[:, r] - Do) / np.maximum(np.abs(Do), floor))
+        eH = np.max(np.abs(H[:, r] - Ho) / np.maximum(np.abs(Ho), 1e-9 / parity.D_RTOL))
+        assert eD <= parity.D_RTOL and eH <= parity.D_RTOL, (r, eD, eH)
+        assert np.array_equal(stats[:, r].astype(np.float64), So), r
+    _say(f"two slot rounds: {over} of {len(sample)} sampled blocks claim more than 112 bins")
+    assert over >= len(sample) // 2
 
 
 def test_strided_input():
