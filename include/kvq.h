@@ -27,8 +27,9 @@
  *     allocates no device memory.  Its only state is one 8 KB pinned host
  *     buffer per calling thread (hipHostMalloc on first use, kept until the
  *     process ends) through which the synchronising calls read back their
- *     small results.  Sizes of every buffer come from kvq_plan (filled by
- *     kvq_plan_blocks).
+ *     small results (for up to 1024 grid-search blocks the solve's last
+ *     kernel writes them into it directly).  Sizes of every buffer come from
+ *     kvq_plan (filled by kvq_plan_blocks).
  *   - Host pointers are marked "(host)".
  *   - Arguments are validated on the host before any launch; a failed check
  *     returns KVQ_EINVAL or KVQ_ENOSPC and launches nothing.  Calls are

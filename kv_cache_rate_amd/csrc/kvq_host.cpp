@@ -13,16 +13,24 @@
 
 namespace kvq {
 
-hipError_t read_back(void* dst, const void* src, size_t bytes, hipStream_t st) {
+void* staging_buffer(void** dev) {
     // One pinned buffer per host thread: a copy into pageable memory costs a
     // staged transfer (about 10 us more per call on MI355X).  It is never
     // freed, so no HIP call runs while the process shuts down.
     thread_local void* buf = nullptr;
+    thread_local void* dbuf = nullptr;
     thread_local bool tried = false;
     if (!tried) {
         tried = true;
         if (hipHostMalloc(&buf, kStagingBytes, hipHostMallocDefault) != hipSuccess) buf = nullptr;
+        if (buf && hipHostGetDevicePointer(&dbuf, buf, 0) != hipSuccess) dbuf = nullptr;
     }
+    if (dev) *dev = dbuf;
+    return buf;
+}
+
+hipError_t read_back(void* dst, const void* src, size_t bytes, hipStream_t st) {
+    void* buf = staging_buffer(nullptr);
     if (!buf || bytes > kStagingBytes) {
         const hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, st);
         return e == hipSuccess ? hipStreamSynchronize(st) : e;
@@ -291,11 +299,27 @@ kvq_status kvq_solve_lambda_weighted(const kvq_plan* p, const double* D, const d
         return fail(KVQ_EINVAL, "subgradient needs finite lambda >= 0 and finite eta");
     kvq::RankTable rt;
     rank_table(*p, rt);
+    void* dev_out = nullptr;
+    kvq::SolveOut* out = static_cast<kvq::SolveOut*>(kvq::staging_buffer(&dev_out));
+    bool direct = false;
     hipError_t e = kvq::launch_solve(*p, rt, D, H, weight, stats, B, mode, iters, lam_in, choice,
-                                     codebook, m, word_off, workspace, s);
+                                     codebook, m, word_off, workspace,
+                                     out ? static_cast<kvq::SolveOut*>(dev_out) : nullptr, &direct, s);
     if (e != hipSuccess) return hip_fail(e, "solve launch");
-    kvq::WsHeader hdr;
-    e = kvq::read_back(&hdr, workspace, sizeof hdr, s);
+    kvq::SolveOut hdr;
+    if (direct) {
+        // the last kernel wrote the result into the pinned buffer
+        e = hipStreamSynchronize(s);
+        if (e == hipSuccess) memcpy(&hdr, out, sizeof hdr);
+    } else {
+        kvq::WsHeader full;
+        e = kvq::read_back(&full, workspace, sizeof full, s);
+        hdr.status = full.status;
+        hdr.err = full.err;
+        hdr.pool_overflow = full.pool_overflow;
+        hdr.lam_final = full.lam_final;
+        hdr.rate_final = full.rate_final;
+    }
     if (e != hipSuccess) return hip_fail(e, "status read-back");
     if (hdr.status & kvq::kStatusNonFinite) return fail(KVQ_ENONFINITE, "NaN or Inf among the KV entries");
     if (hdr.err == KVQ_EINFEASIBLE)

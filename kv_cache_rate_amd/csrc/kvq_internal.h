@@ -48,6 +48,7 @@ struct WsHeader {
     uint32_t pool_overflow;   // 1 if they exceeded the pool
     uint32_t swaps;           // upgrades applied
     uint32_t pad1;
+    uint64_t part_rate[16];   // few-block final pass: fixed-point rate per workgroup
 };
 constexpr size_t kWsHeaderBytes = 4096;
 constexpr uint32_t kGreedyPool = 16384;  // (block, candidate) pairs in the workspace pool
@@ -315,11 +316,27 @@ hipError_t launch_ws_reset(void* ws, hipStream_t st);
 // plain pageable copy if the allocation fails).
 constexpr size_t kStagingBytes = 8192;
 hipError_t read_back(void* dst, const void* src, size_t bytes, hipStream_t st);
+// The calling thread's pinned staging buffer (kStagingBytes, allocated on
+// first use), or null if it cannot be allocated; *dev (if dev is not null)
+// receives its device-side address, or null.
+void* staging_buffer(void** dev);
+// The header fields the host reads after a solve.  The one-workgroup final
+// pass writes them straight into pinned host memory, which saves the copy.
+struct SolveOut {
+    uint32_t status;
+    int32_t err;
+    uint32_t pool_overflow;
+    uint32_t pad;
+    double lam_final;
+    uint64_t rate_final;
+};
+// `out` (pinned host memory, may be null): if the solve's last kernel wrote
+// the result there, *direct is set and the caller only has to synchronise.
 hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
                         const double* H, const double* wgt, const float* stats, double B,
                         int mode, int iters,
                         double lam_in, int32_t* choice, float* codebook, uint8_t* m,
-                        uint64_t* off, void* ws, hipStream_t st);
+                        uint64_t* off, void* ws, SolveOut* out, bool* direct, hipStream_t st);
 hipError_t launch_quantize(const Geom& g, int64_t R, int s, const float* codebook,
                            const uint8_t* m, const uint64_t* off, uint64_t seed,
                            uint32_t* codes, hipStream_t st);

@@ -225,13 +225,27 @@ rates_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
     }
 }
 
-// Codepoints of grid candidate c of a block from its order statistics.
-__device__ int build_grid_codebook(int c, const float* st, int64_t stride, const RankTable& rt, int n,
-                                   float* q) {
-    const float mn = st[0];
-    const float mx = st[(rt.n_stats - 1) * stride];
+// Codepoints of grid candidate c of a block from its minimum, maximum and
+// order statistics (st: the block's first statistic, `stride` apart; col:
+// RankTable::col as a (kMaxS + 1) x kMaxS table, in LDS where it matters),
+// written as the block's codebook row (s entries, zero after the m distinct
+// points); returns m.  The k points are gathered unrolled to kMaxS with
+// unconditional loads (statistic 0 where a point needs none), so the loads
+// are in flight together.  The points are non-decreasing, so equal ones are
+// adjacent: each distinct point is stored at a running position, straight
+// to memory (a register array indexed by a per-lane position compiles into
+// long select chains).
+__device__ int write_grid_codebook(int c, float mn, float mx, const float* st, int64_t stride,
+                                   const uint8_t* col, int s, float* row) {
+    if ((s & 3) == 0 && ((uintptr_t)row & 15u) == 0) {
+#pragma unroll
+        for (int j4 = 0; j4 < kMaxS / 4; ++j4)
+            if (4 * j4 < s) reinterpret_cast<float4*>(row)[j4] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    } else {
+        for (int j = 0; j < s; ++j) row[j] = 0.0f;
+    }
     if (mn == mx) {
-        q[0] = mn;
+        row[0] = mn;
         return 1;
     }
     int k;
@@ -242,54 +256,95 @@ __device__ int build_grid_codebook(int c, const float* st, int64_t stride, const
         k = 3 + (c - 1) / 2;
         uni = ((c - 1) & 1) == 0;
     }
+    const bool quant = c != 0 && !uni;
+    int idx[kMaxS];
+#pragma unroll
+    for (int j = 0; j < kMaxS; ++j) idx[j] = quant && j < k ? (int)col[k * kMaxS + j] : 0;
+    float g[kMaxS];
+#pragma unroll
+    for (int j = 0; j < kMaxS; ++j) g[j] = st[idx[j] * stride];
     int m = 0;
-    for (int j = 0; j < k; ++j) {
-        float v;
-        if (c == 0) v = j == 0 ? mn : mx;
-        else if (uni) v = uniform_point(mn, mx, j, k);
-        else v = st[rt.col[k][j] * stride];
-        if (m == 0 || v != q[m - 1]) q[m++] = v;
+    float prev = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxS; ++j) {
+        float v = c == 0 ? (j == 0 ? mn : mx) : g[j];
+        if (uni && j < k) v = uniform_point(mn, mx, j, k);  // fp64 division: only where needed
+        const bool keep = j < k && (j == 0 || v != prev);
+        if (keep) row[m] = v;
+        m += keep ? 1 : 0;
+        prev = v;
     }
     return m;
 }
 
-// One block's choice at multiplier lam (grid search): candidate, codebook,
-// levels and code words; returns the block's fixed-point rate.
+// One block's choice at multiplier lam (grid search) from its table row
+// (Dv[c], Hv[c] for c < C, already loaded): candidate, codebook, levels and
+// code words; returns the block's fixed-point rate.  Ties go to the lowest
+// candidate index.
+template <int kN>
+__device__ __forceinline__ unsigned long long choose_grid_block(
+    int64_t r, const double (&Dv)[kN], const double (&Hv)[kN], int C, double wr, double lamd, float mn,
+    float mx, const float* __restrict__ stats, int64_t R, int s, int n, int shift, const uint8_t* col,
+    int32_t* __restrict__ choice, float* __restrict__ codebook, uint8_t* __restrict__ m_out,
+    uint64_t& words) {
+    double best = 0.0, bestH = 0.0;
+    int bc = -1;
+#pragma unroll
+    for (int c = 0; c < kN; ++c) {
+        if (c < C) {
+            const double o = objective(wr * Dv[c], Hv[c], lamd);
+            if (bc < 0 || o < best) {
+                best = o;
+                bestH = Hv[c];
+                bc = c;
+            }
+        }
+    }
+    const int m = write_grid_codebook(bc, mn, mx, stats + r, R, col, s, codebook + r * s);
+    choice[r] = bc;
+    m_out[r] = (uint8_t)m;
+    words = ((uint64_t)n * (uint64_t)code_width(m) + 31u) / 32u;
+    return rate_fx((double)n, bestH, shift);
+}
+
+// A block with no feasible multiplier: a well-formed empty result.
+__device__ __forceinline__ void empty_grid_block(int64_t r, int s, int32_t* __restrict__ choice,
+                                                 float* __restrict__ codebook, uint8_t* __restrict__ m_out) {
+    choice[r] = -1;
+    m_out[r] = 1;
+    for (int j = 0; j < s; ++j) codebook[r * s + j] = 0.0f;
+}
+
+// The same, loading the table row in chunks of 15 candidates whose loads are
+// in flight together (a loop bounded by the run-time C waits out one load
+// latency per candidate).
 __device__ unsigned long long final_grid_block(int64_t r, const double* __restrict__ D,
                                                const double* __restrict__ H, const double* __restrict__ wgt,
                                                const float* __restrict__ stats, int64_t R, int C, int s,
-                                               int n, int shift, const RankTable& rt, bool err, double lam,
+                                               int n, int shift, const uint8_t* col, int n_stats,
+                                               bool err, double lam,
                                                int32_t* __restrict__ choice, float* __restrict__ codebook,
                                                uint8_t* __restrict__ m_out, uint64_t& words) {
     if (err) {
-        // no feasible multiplier: leave a well-formed empty result
-        choice[r] = -1;
-        m_out[r] = 1;
-        for (int j = 0; j < s; ++j) codebook[r * s + j] = 0.0f;
+        empty_grid_block(r, s, choice, codebook, m_out);
         words = 0;
         return 0;
     }
-    const double d = (double)n;
-    const double lamd = lam * d;
-    const double* Dr = D + r;
-    const double* Hr = H + r;
     const double wr = wgt ? wgt[r] : 1.0;
-    double best = objective(wr * Dr[0], Hr[0], lamd);
-    int bc = 0;
-    for (int c = 1; c < C; ++c) {
-        const double o = objective(wr * Dr[c * R], Hr[c * R], lamd);
-        if (o < best) {
-            best = o;
-            bc = c;
+    const float mn = stats[r];
+    const float mx = stats[(int64_t)(n_stats - 1) * R + r];
+    double Dv[kMaxCand], Hv[kMaxCand];
+    constexpr int kChunk = 15;
+#pragma unroll
+    for (int c0 = 0; c0 < kMaxCand; c0 += kChunk) {
+#pragma unroll
+        for (int c = c0; c < c0 + kChunk && c < kMaxCand; ++c) {
+            Dv[c] = c < C ? D[c * R + r] : 0.0;
+            Hv[c] = c < C ? H[c * R + r] : 0.0;
         }
     }
-    float q[kMaxS];
-    const int m = build_grid_codebook(bc, stats + r, R, rt, n, q);
-    choice[r] = bc;
-    m_out[r] = (uint8_t)m;
-    for (int j = 0; j < s; ++j) codebook[r * s + j] = j < m ? q[j] : 0.0f;
-    words = ((uint64_t)n * (uint64_t)code_width(m) + 31u) / 32u;
-    return rate_fx(d, Hr[bc * R], shift);
+    return choose_grid_block(r, Dv, Hv, C, wr, lam * (double)n, mn, mx, stats, R, s, n, shift, col, choice,
+                             codebook, m_out, words);
 }
 
 __global__ void __launch_bounds__(kSolveThreads)
@@ -300,13 +355,16 @@ final_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
                    float* __restrict__ codebook, uint8_t* __restrict__ m_out,
                    uint64_t* __restrict__ off) {
     __shared__ unsigned long long part[kSolveThreads / 64];
+    __shared__ uint8_t col[(kMaxS + 1) * kMaxS];
+    for (int i = threadIdx.x; i < (kMaxS + 1) * kMaxS; i += blockDim.x) col[i] = (&rt.col[0][0])[i];
+    __syncthreads();
     const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r == 0) off[0] = 0;
     unsigned long long v = 0;
     if (r < R) {
         uint64_t words;
-        v = final_grid_block(r, D, H, wgt, stats, R, C, s, n, shift, rt, h->err != 0, h->lam_final, choice,
-                             codebook, m_out, words);
+        v = final_grid_block(r, D, H, wgt, stats, R, C, s, n, shift, col, rt.n_stats, h->err != 0,
+                             h->lam_final, choice, codebook, m_out, words);
         off[r + 1] = words;
     }
     v = wave_sum_u64(v);
@@ -934,10 +992,9 @@ greedy_apply_kernel(const double* __restrict__ D, const double* __restrict__ H,
                 h->rate_final += rn - ru;
                 h->swaps += 1u;
                 __hip_atomic_store(&choice[r], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                float q[kMaxS];
-                const int m = build_grid_codebook(c, stats + r, R, rt, n, q);
+                const int m = write_grid_codebook(c, stats[r], stats[(int64_t)(rt.n_stats - 1) * R + r],
+                                                  stats + r, R, &rt.col[0][0], s, codebook + r * s);
                 m_out[r] = (uint8_t)m;
-                for (int j = 0; j < s; ++j) codebook[r * s + j] = j < m ? q[j] : 0.0f;
                 off[r + 1] = ((uint64_t)n * (uint64_t)code_width(m) + 31u) / 32u;
             }
         }
@@ -949,59 +1006,128 @@ greedy_apply_kernel(const double* __restrict__ D, const double* __restrict__ H,
 
 // ----------------------------------------------------------------- host ----
 
-// Up to kSmallR blocks (grid search) in one workgroup: the final choice,
-// the rate sum and the exclusive scan of the code words in one launch.  In
-// the subgradient mode it also does the header set-up of solve_init_kernel
-// (the blocks are chosen at lam_in), so the call is a single kernel.
+// Up to kSmallR blocks (grid search; a decode step): the final choice in
+// one 64-thread workgroup per 64 blocks, then one workgroup for the scan of
+// the code words, the rate sum and the header.  The choice is a chain of
+// dependent memory round trips over a table just written on every XCD, so
+// each thread first issues all of its block's table loads and the column
+// table is copied to LDS while they are in flight; the codepoints'
+// statistics are then gathered in one batch.  Spreading the blocks over
+// workgroups (CUs) matters: one workgroup for 512 blocks spent 15 us in its
+// CU's memory pipeline on the scattered gathers and row stores.
 constexpr int kSmallR = 1024;
+constexpr int kSmallWG = 64;
+static_assert(kSmallR / kSmallWG <= 16, "WsHeader::part_rate holds one entry per workgroup");
 
-__global__ void __launch_bounds__(kSmallR)
-final_grids_small_kernel(const double* __restrict__ D, const double* __restrict__ H,
-                         const double* __restrict__ wgt, const float* __restrict__ stats, int64_t R, int C,
-                         int s, int n, int shift, RankTable rt, WsHeader* h, int subgrad, double lam_in,
-                         int32_t* __restrict__ choice, float* __restrict__ codebook,
-                         uint8_t* __restrict__ m_out, uint64_t* __restrict__ off) {
-    __shared__ unsigned long long part[kSmallR / 64][2];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ void __launch_bounds__(kSmallWG)
+final_grids_rows_kernel(const double* __restrict__ D, const double* __restrict__ H,
+                        const double* __restrict__ wgt, const float* __restrict__ stats, int64_t R, int C,
+                        int s, int n, int shift, RankTable rt, WsHeader* h, int subgrad, double lam_in,
+                        int32_t* __restrict__ choice, float* __restrict__ codebook,
+                        uint8_t* __restrict__ m_out, uint64_t* __restrict__ off) {
+    __shared__ uint8_t col[(kMaxS + 1) * kMaxS];
+    const int lane = threadIdx.x;
     const bool err = subgrad ? false : h->err != 0;
     const double lam = subgrad ? lam_in : h->lam_final;
+    const int64_t r = (int64_t)blockIdx.x * kSmallWG + lane;
+    const bool live = r < R;
+    double Dv[kMaxCand], Hv[kMaxCand];
+    float mn = 0.0f, mx = 0.0f;
+    double wr = 1.0;
+    if (live && !err) {
+        wr = wgt ? wgt[r] : 1.0;
+        mn = stats[r];
+        mx = stats[(int64_t)(rt.n_stats - 1) * R + r];
+#pragma unroll
+        for (int c = 0; c < kMaxCand; ++c) {
+            Dv[c] = c < C ? D[c * R + r] : 0.0;
+            Hv[c] = c < C ? H[c * R + r] : 0.0;
+        }
+    }
+    for (int i = lane; i < (kMaxS + 1) * kMaxS; i += kSmallWG) col[i] = (&rt.col[0][0])[i];
+    __syncthreads();
     unsigned long long v = 0;
-    uint64_t words = 0;
-    if (tid < R)
-        v = final_grid_block(tid, D, H, wgt, stats, R, C, s, n, shift, rt, err, lam, choice, codebook, m_out,
-                             words);
-    const uint64_t inc = wave_incl_scan_u64(words);
+    if (live) {
+        uint64_t words = 0;
+        if (err) {
+            empty_grid_block(r, s, choice, codebook, m_out);
+        } else {
+            v = choose_grid_block(r, Dv, Hv, C, wr, lam * (double)n, mn, mx, stats, R, s, n, shift, col, choice,
+                                  codebook, m_out, words);
+        }
+        off[r + 1] = words;  // the scan kernel turns these into offsets
+    }
     v = wave_sum_u64(v);
-    if (lane == 63) part[wave][0] = inc;
-    if (lane == 0) part[wave][1] = v;
+    if (lane == 0) h->part_rate[blockIdx.x] = v;
+}
+
+// The offsets scan (R <= kSmallR, one thread per block), the rate sum and
+// the header; in the subgradient mode also the header set-up of
+// solve_init_kernel.  If `out` is given, the fields the host reads go
+// straight into its pinned buffer.
+__global__ void __launch_bounds__(kSmallR)
+final_grids_tail_kernel(int64_t R, WsHeader* h, int subgrad, double lam_in, uint64_t* __restrict__ off,
+                        SolveOut* out) {
+    __shared__ uint64_t wsum[kSmallR / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint64_t words = tid < R ? off[tid + 1] : 0u;
+    const int nwg = (int)((R + kSmallWG - 1) / kSmallWG);
+    const uint64_t pr = tid < nwg ? h->part_rate[tid] : 0u;
+    const uint64_t inc = wave_incl_scan_u64(words);
+    if (lane == 63) wsum[wave] = inc;
     __syncthreads();
     uint64_t pre = 0;
-    for (int w = 0; w < wave; ++w) pre += part[w][0];
+    for (int w = 0; w < wave; ++w) pre += wsum[w];
     if (tid < R) off[tid + 1] = pre + inc;
-    if (tid == 0) {
-        off[0] = 0;
-        unsigned long long t = 0;
-        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += part[w][1];
-        if (subgrad) {
-            h->phase = kPhaseSubgrad;
-            h->nlam = 0;
-            h->done = 1;
-            h->err = 0;
-            h->lam_final = lam_in;
-            h->pool_n = 0;
-            h->pool_overflow = 0;
-            h->swaps = 0;
+    if (wave == 0) {
+        const unsigned long long t = wave_sum_u64(pr);  // nwg <= 16 workgroups: wave 0 holds them all
+        if (lane == 0) {
+            off[0] = 0;
+            if (subgrad) {
+                h->phase = kPhaseSubgrad;
+                h->nlam = 0;
+                h->done = 1;
+                h->err = 0;
+                h->lam_final = lam_in;
+                h->pool_n = 0;
+                h->pool_overflow = 0;
+                h->swaps = 0;
+            }
+            h->rate_final = t;
+            if (out) {
+                SolveOut o;
+                o.status = h->status;
+                o.err = subgrad ? 0 : h->err;
+                o.pool_overflow = 0u;
+                o.pad = 0u;
+                o.lam_final = subgrad ? lam_in : h->lam_final;
+                o.rate_final = t;
+                *out = o;
+                __threadfence_system();
+            }
         }
-        h->rate_final = t;
     }
+}
+
+// Launch the two kernels of the few-block final pass.
+static void launch_final_small(const kvq_plan& p, const RankTable& rt, const double* D, const double* H,
+                               const double* wgt, const float* stats, int64_t R, int n, int shift, WsHeader* h,
+                               int subgrad, double lam_in, int32_t* choice, float* codebook, uint8_t* m,
+                               uint64_t* off, SolveOut* out, hipStream_t st) {
+    const unsigned wgs = (unsigned)((R + kSmallWG - 1) / kSmallWG);
+    hipLaunchKernelGGL(final_grids_rows_kernel, dim3(wgs), dim3(kSmallWG), 0, st, D, H, wgt, stats, R,
+                       p.n_cand, p.s, n, shift, rt, h, subgrad, lam_in, choice, codebook, m, off);
+    const unsigned threads = (unsigned)((R + 63) / 64 * 64);
+    hipLaunchKernelGGL(final_grids_tail_kernel, dim3(1), dim3(threads), 0, st, R, h, subgrad, lam_in, off, out);
 }
 
 hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D, const double* H,
                         const double* wgt, const float* stats, double B, int mode, int iters,
                         double lam_in,
                         int32_t* choice, float* codebook, uint8_t* m, uint64_t* off, void* ws,
-                        hipStream_t st) {
+                        SolveOut* out, bool* direct, hipStream_t st) {
     WsHeader* h = (WsHeader*)ws;
+    *direct = false;
     const int64_t R = p.n_blocks;
     const int n = p.d_block;
     const int shift = p.rate_shift;
@@ -1019,10 +1145,10 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
     const int dbl_n = grids ? kMaxLam - 1 : 8;
     // few blocks (a decode step): choice, rate and offsets in one workgroup
     const bool small = grids && R >= 1 && R <= kSmallR && mode != KVQ_BISECT_GREEDY;
-    const unsigned small_threads = (unsigned)((R + 63) / 64 * 64);
+
     if (small && mode == KVQ_SUBGRAD) {
-        hipLaunchKernelGGL(final_grids_small_kernel, dim3(1), dim3(small_threads), 0, st, D, H, wgt, stats, R,
-                           p.n_cand, p.s, n, shift, rt, h, 1, lam_in, choice, codebook, m, off);
+        launch_final_small(p, rt, D, H, wgt, stats, R, n, shift, h, 1, lam_in, choice, codebook, m, off, out, st);
+        *direct = out != nullptr;
         return hipGetLastError();
     }
     hipLaunchKernelGGL(solve_init_kernel, dim3(1), dim3(64), 0, st, h, mode, lam_in, Btot_fx, iters,
@@ -1063,8 +1189,8 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
         }
     }
     if (small) {
-        hipLaunchKernelGGL(final_grids_small_kernel, dim3(1), dim3(small_threads), 0, st, D, H, wgt, stats, R,
-                           p.n_cand, p.s, n, shift, rt, h, 0, 0.0, choice, codebook, m, off);
+        launch_final_small(p, rt, D, H, wgt, stats, R, n, shift, h, 0, 0.0, choice, codebook, m, off, out, st);
+        *direct = out != nullptr;
         return hipGetLastError();
     }
     if (p.search == KVQ_GRIDS) {

@@ -136,38 +136,42 @@ def _check(st):
         raise KvqError(st, last_error())
 
 
+_DTYPE_CODES = {}  # dtype object -> KVQ_F16 / KVQ_F32, filled on first sight
+
+
 def _dtype_code(t):
-    name = str(getattr(t, "dtype", ""))
-    if name.endswith("float16"):
-        return KVQ_F16
-    if name.endswith("float32"):
-        return KVQ_F32
-    raise ValueError(f"unsupported KV dtype {name}")
+    dt = getattr(t, "dtype", None)
+    code = _DTYPE_CODES.get(dt)
+    if code is None:
+        name = str(dt)
+        if name.endswith("float16"):
+            code = KVQ_F16
+        elif name.endswith("float32"):
+            code = KVQ_F32
+        else:
+            raise ValueError(f"unsupported KV dtype {name}")
+        _DTYPE_CODES[dt] = code
+    return code
+
+
+_I64x4 = ctypes.c_int64 * 4
 
 
 def as_kvq_tensor(t):
     """Describe a 4-D torch tensor (or numpy array, for planning only)."""
     if t.ndim != 4:
         raise ValueError("KV tensors are [outer, heads, tokens, dim]")
-    kt = KvqTensor()
     if hasattr(t, "data_ptr"):
-        kt.data = t.data_ptr()
+        data = t.data_ptr()
         strides = t.stride()
     else:  # numpy: planning reads shapes and strides only
-        kt.data = t.ctypes.data
+        data = t.ctypes.data
         strides = tuple(s // t.itemsize for s in t.strides)
-    kt.dtype = _dtype_code(t)
-    for d in range(4):
-        kt.shape[d] = t.shape[d]
-        kt.stride[d] = strides[d]
-    return kt
+    return KvqTensor(data, _dtype_code(t), 0, _I64x4(*t.shape), _I64x4(*strides))
 
 
 def _tensor_array(tensors):
-    arr = (KvqTensor * len(tensors))()
-    for i, t in enumerate(tensors):
-        arr[i] = as_kvq_tensor(t)
-    return arr
+    return (KvqTensor * len(tensors))(*[as_kvq_tensor(t) for t in tensors])
 
 
 def _ptr(x):
