@@ -9,9 +9,10 @@
 //
 // Device design: a "rates" pass evaluates R at up to 64 multipliers at once
 // (one read of the score table per pass).  A one-thread "select" kernel then
-// advances the bracket held in the workspace header, so the whole search runs
-// without a host round trip:
-//   pass 0: lambda in {0, 2^0, ..., 2^62}; the first feasible power gives the
+// advances the bracket held in the workspace header, so the search runs with
+// one host round trip (after lambda = 0, which is probed alone first: when it
+// is feasible no further pass is launched):
+//   pass 0: lambda in {2^0, ..., 2^62}; the first feasible power gives the
 //           doubling bracket exactly as sequential doubling from [0, 1] would;
 //   pass 1: {2^63, 2^64} only if none of those was feasible;
 //   passes 2..: the 2^b - 1 interior points of a dyadic grid over the
@@ -1143,7 +1144,8 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
     const bool grids = p.search == KVQ_GRIDS;
     const int bits_max = grids ? 6 : 1;
     const int dbl_n = grids ? kMaxLam - 1 : 8;
-    // few blocks (a decode step): choice, rate and offsets in one workgroup
+    // few blocks (a decode step): choice, rate and offsets in two small
+    // launches (launch_final_small), the result written to `out`
     const bool small = grids && R >= 1 && R <= kSmallR && mode != KVQ_BISECT_GREEDY;
 
     if (small && mode == KVQ_SUBGRAD) {

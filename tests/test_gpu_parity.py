@@ -122,6 +122,21 @@ def test_ragged_small_blocks(dtype):
     _check(w, [x])
 
 
+@pytest.mark.parametrize("mode", ["bisect", "subgrad"])
+@pytest.mark.parametrize("heads", [64, 65])
+def test_final_pass_block_count_edges(heads, mode):
+    """16 blocks per head of 2 x 16 entries: 1024 blocks (the most the
+    few-block final pass takes: 16 workgroups of 64 and a 1024-thread scan)
+    and 1040 (the many-block path), under bisection and a subgradient
+    step."""
+    rng = np.random.default_rng(53 + heads)
+    x = _small(np.float32, (1, heads, 32, 16), rng)
+    w = W.Workload(name=f"edge{heads}", index=0, tensors=(("K", x.shape),), dtype="f32",
+                   tokens_per_block=2, dims_per_block=16, s=8, search="grids", B=1.8, mode=mode)
+    g, o, rep = _check(w, [x], lam=0.21)
+    assert g["m"].shape == (heads * 16,)
+
+
 def test_ties_constant_and_negative_zero(kernel_path):
     """fp16 ties (fewer distinct levels than k), constant blocks (one level,
     zero-width codes) and -0 entries (equal to +0)."""
