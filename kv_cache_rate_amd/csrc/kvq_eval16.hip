@@ -157,6 +157,12 @@ __device__ __forceinline__ uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c) 
     return r;
 }
 
+// a.lo * b.lo + a.hi * b.hi + c on the 16-bit halves of a and b (exact:
+// the sums here stay below 2^32).
+__device__ __forceinline__ uint32_t udot2(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_udot2(__builtin_bit_cast(ushort2_t, a), __builtin_bit_cast(ushort2_t, b), c, false);
+}
+
 // 1/x to ~1 ulp: hardware reciprocal estimate and two Newton steps.
 __device__ __forceinline__ double recip(double x) {
     double r = __builtin_amdgcn_rcp(x);
@@ -465,25 +471,39 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         const uint32_t so = sl[i] ^ tag;
         if (so < kRound2) {
             // key f = bits [kb, kb + 6) of the word holding both keys; it
-            // counts 1 in the 16-bit half f & 1 of word f >> 1 of the
-            // slot, and (1, f) in the total of its 8-key group f >> 3
+            // counts 1 in the 16-bit half f & 1 of word f >> 1 of the slot
             const uint32_t k2 = k2s[i >> 1];
-            uint32_t cword, one, gword, gval;
+            uint32_t cword, one;
             if (i & 1) {
                 cword = bfe_u32<17, 5>(k2);
                 one = mad_u24(bfe_u32<16, 1>(k2), 0xffffu, 1u);
-                gword = bfe_u32<19, 3>(k2);
-                gval = bfe_u32<16, 6>(k2) | kCnt1;
             } else {
                 cword = bfe_u32<1, 5>(k2);
                 one = mad_u24(k2 & 1u, 0xffffu, 1u);
-                gword = bfe_u32<3, 3>(k2);
-                gval = (k2 & 63u) | kCnt1;
             }
             uint32_t* slotw = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(sh.u.b.w) + so);
             atomicAdd(slotw + cword, one);
-            atomicAdd(slotw + kFW + gword, gval);
         }
+    }
+    __syncthreads();
+    // ---- group totals of this round's slots, (count << 19) + sum of f over
+    //      each 8-key group, from the per-key counters: one (slot, group) per
+    //      thread and step.  Group g is the slot's quad g (keys 8g .. 8g+7,
+    //      word m holding keys 8g + 2m and 8g + 2m + 1).  Adding these in
+    //      sweep 2 instead, one LDS atomic per entry into 8 words per slot,
+    //      serialises on equal addresses: those atomics alone cost ~9% of
+    //      the kernel; this pass and its barrier give back most of that
+    //      (net 2%, and 1% better than each finishing lane summing its own
+    //      slot's groups).
+    for (uint32_t t = tid; t < ns * 8u; t += kT) {
+        const uint32_t sb = (t >> 3) * (uint32_t)(4 * kSW), g = t & 7u;
+        const uint4 q = slot_quad(sh, sb, g);
+        const uint32_t c = udot2(q.w, 0x00010001u, udot2(q.z, 0x00010001u,
+                                 udot2(q.y, 0x00010001u, udot2(q.x, 0x00010001u, 0u))));
+        const uint32_t fl = udot2(q.w, 0x00070006u, udot2(q.z, 0x00050004u,
+                                  udot2(q.y, 0x00030002u, udot2(q.x, 0x00010000u, 0u))));
+        reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(sh.u.b.w) + sb)[kFW + g] =
+            (c << 19) + 8u * g * c + fl;
     }
     __syncthreads();
     // ---- finish the prefixes inside the bins
