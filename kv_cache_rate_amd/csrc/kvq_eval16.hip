@@ -79,12 +79,10 @@ template <int kSlots>
 struct PhaseB {                    // sweep 2 .. prefix finish
     uint32_t w[kSlots * kSW];
 };
-struct PhaseC {                    // candidate intervals
-    double dterm[kCL];
-    double hterm[kCL];
-    double mr[kCL];                // mass at the interval's right point
-    double ma[kCL];                // mass the interval sends to its left point
-    float bv[kCL];                 // right point
+struct PhaseC {                    // candidate intervals, written only by a wave
+    double mr[kCL];                //   that holds a zero-width interval:
+    double ma[kCL];                // mass at the interval's right point, mass it
+    float bv[kCL];                 // sends to its left point, right point
 };
 
 template <int kSlots>
@@ -210,6 +208,20 @@ __device__ __forceinline__ double point_entropy(double m, const double* lg_c, co
     return pi > 0.0 ? -pi * log2_unit(pi, lg_c, lg_inv) : 0.0;
 }
 
+// One step of three segmented inclusive scans within 16-lane rows: add the
+// values of the lane K back when it belongs to the same run (off >= K).
+template <int CTRL, int K>
+__device__ __forceinline__ void seg_scan_step(uint32_t off, double& a, double& b, uint32_t& z) {
+    const double ta = dpp_f64<CTRL>(0.0, a);
+    const double tb = dpp_f64<CTRL>(0.0, b);
+    const uint32_t tz = dpp_u32<CTRL>(0u, z);
+    if (off >= (uint32_t)K) {
+        a += ta;
+        b += tb;
+        z += tz;
+    }
+}
+
 // Claim a slot for coarse bin `bin` (first caller wins; the slot's entry is
 // visible after the next barrier).  Claims past kSlots are served by a
 // second round that reuses the slot memory: entry = byte offset | kRound2.
@@ -257,6 +269,8 @@ struct Eval16Tables {
     uint8_t uden[kNU];              // denominator
     uint16_t red[kMaxCand];         // candidate c: first lane | interval count << 8
     uint16_t desc[kCL];             // lane: left point | right point << 8, or kNoLane
+    uint16_t lseg[kCL];             // lane: candidate | offset in its run << 5 | last << 9,
+                                    //   or kNoLane
                                     //   (a candidate's last interval ends at point 1)
     double lg_c[64];                // log2(1 + (2i+1)/128)
     double lg_inv[64];              // 1 / (1 + (2i+1)/128)
@@ -585,7 +599,6 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     // ---- candidate intervals, one per lane: masses to both ends, the
     //      distortion term a^2 M_a + b^2 M_b and the entropy term of the
     //      right point (its mass: this interval's share plus the next one's)
-    PhaseC& pc = sh.u.c;
     const bool last = ((d >> 8) & 0xffu) == 1u;  // right point is the maximum
     double ma = 0.0, mb = 0.0, dterm = 0.0;
     float bq = 0.0f;
@@ -609,42 +622,50 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         bq = pb.v;
     }
     const double ma_next = dpp_f64<kDppRowShl1>(0.0, ma);
-    if (tid < kCL) {
-        const double mr = last ? mb : mb + ma_next;
-        pc.dterm[tid] = dterm;
-        pc.hterm[tid] = point_entropy(mr, sh.lg_c, sh.lg_inv);
+    const double mr = last ? mb : mb + ma_next;
+
+    // ---- per candidate: D = sum of its intervals' terms - sum x^2 and
+    //      H = sum of its points' entropy terms.  A candidate's intervals
+    //      are consecutive lanes of one 16-lane row, so both sums are
+    //      segmented inclusive scans within the row (shifts of 1, 2, 4, 8
+    //      lanes, added when the source lane is of the same candidate); the
+    //      candidate's last lane writes them.  The first interval also
+    //      carries the entropy term of its left point.
+    const uint32_t sg = tb.lseg[tid];
+    const bool live = sg != kNoLane;
+    const uint32_t off = (sg >> 5) & 15u;
+    double dsum = live ? dterm : 0.0;
+    double hsum = 0.0;
+    if (live) {
+        hsum = point_entropy(mr, sh.lg_c, sh.lg_inv);
+        if (off == 0u) hsum += point_entropy(ma, sh.lg_c, sh.lg_inv);
+    }
+    uint32_t zw = zero_width ? 1u : 0u;
+    seg_scan_step<kDppRowShr1, 1>(off, dsum, hsum, zw);
+    seg_scan_step<kDppRowShr2, 2>(off, dsum, hsum, zw);
+    seg_scan_step<kDppRowShr4, 4>(off, dsum, hsum, zw);
+    seg_scan_step<kDppRowShr8, 8>(off, dsum, hsum, zw);
+    // equal consecutive points (tied data only): the candidate merges their
+    // masses first, from its intervals' values that its wave leaves in LDS
+    PhaseC& pc = sh.u.c;
+    if (__any(zero_width)) {
         pc.mr[tid] = mr;
         pc.ma[tid] = ma;
         pc.bv[tid] = bq;
+        __builtin_amdgcn_wave_barrier();
     }
-    const bool dup = __syncthreads_or(zero_width);
-
-    // ---- one lane per candidate: D = sum of terms - sum x^2 (threads
-    //      0..28), H = sum of point entropies (threads 64..92)
-    if (tid < kMaxCand) {
-        const uint32_t rd = tb.red[tid];
-        const uint32_t first = rd & 0xffu, n = rd >> 8;
-        double sum = 0.0;
-#pragma unroll
-        for (uint32_t i = 0; i < 15; ++i)
-            sum += i < n ? pc.dterm[first + i] : 0.0;  // first + 14 < kCL
-        Dout[tid * R + r] = mx > mn ? fmax(sum - sumsq, 0.0) : 0.0;
-    } else if (tid >= 64 && tid < 64 + kMaxCand) {
-        const int c = tid - 64;
-        const uint32_t rd = tb.red[c];
-        const uint32_t first = rd & 0xffu, n = rd >> 8;
-        double h = 0.0;
-        if (!dup) {  // every point distinct: one term per right point
-#pragma unroll
-            for (uint32_t i = 0; i < 15; ++i)
-                h += i < n ? pc.hterm[first + i] : 0.0;
-            h += point_entropy(pc.ma[first], sh.lg_c, sh.lg_inv);
-        } else {     // merge the masses of equal consecutive points
+    if (live && (sg >> 9) != 0u) {
+        const uint32_t c = sg & 31u;
+        Dout[c * R + r] = mx > mn ? fmax(dsum - sumsq, 0.0) : 0.0;
+        double h = hsum;
+        if (zw != 0u) {
+            const uint32_t first = (uint32_t)tid - off;
+            h = 0.0;
             double acc = pc.ma[first];
             float val = mn;
-            for (uint32_t i = 0; i < n; ++i) {
-                const float b = pc.bv[first + i];
-                const double m = pc.mr[first + i];
+            for (uint32_t i = first; i <= (uint32_t)tid; ++i) {
+                const float b = pc.bv[i];
+                const double m = pc.mr[i];
                 if (b == val) {
                     acc += m;
                 } else {
@@ -714,7 +735,7 @@ hipError_t launch_eval16(const void* x0, const void* x1, int64_t nb0, int64_t R,
     }
     rows[nr][0] = cand(9, true); rows[nr][1] = cand(9, false); ++nr;
     if (nr != kRows) return hipErrorInvalidValue;
-    for (int l = 0; l < kCL; ++l) tb.desc[l] = (uint16_t)kNoLane;
+    for (int l = 0; l < kCL; ++l) tb.desc[l] = tb.lseg[l] = (uint16_t)kNoLane;
     int placed = 0;
     for (int row = 0; row < kRows; ++row) {
         int lane = 16 * row;
@@ -724,8 +745,10 @@ hipError_t launch_eval16(const void* x0, const void* x1, int64_t nb0, int64_t R,
             const int k = c == 0 ? 2 : 3 + (c - 1) / 2;
             if (lane + (k - 1) > 16 * (row + 1)) return hipErrorInvalidValue;
             tb.red[c] = (uint16_t)(lane | ((k - 1) << 8));
-            for (int j = 0; j < k - 1; ++j, ++lane)
+            for (int j = 0; j < k - 1; ++j, ++lane) {
                 tb.desc[lane] = (uint16_t)(point(c, j) | (point(c, j + 1) << 8));
+                tb.lseg[lane] = (uint16_t)(c | (j << 5) | ((j == k - 2 ? 1 : 0) << 9));
+            }
             ++placed;
         }
     }
