@@ -208,18 +208,21 @@ __device__ __forceinline__ double point_entropy(double m, const double* lg_c, co
     return pi > 0.0 ? -pi * log2_unit(pi, lg_c, lg_inv) : 0.0;
 }
 
-// One step of three segmented inclusive scans within 16-lane rows: add the
-// values of the lane K back when it belongs to the same run (off >= K).
+// One step of segmented inclusive scans within 16-lane rows: add the values
+// of the lane K back when it belongs to the same run (off >= K).
 template <int CTRL, int K>
-__device__ __forceinline__ void seg_scan_step(uint32_t off, double& a, double& b, uint32_t& z) {
+__device__ __forceinline__ void seg_scan_step(uint32_t off, double& a, double& b) {
     const double ta = dpp_f64<CTRL>(0.0, a);
     const double tb = dpp_f64<CTRL>(0.0, b);
-    const uint32_t tz = dpp_u32<CTRL>(0u, z);
     if (off >= (uint32_t)K) {
         a += ta;
         b += tb;
-        z += tz;
     }
+}
+template <int CTRL, int K>
+__device__ __forceinline__ void seg_scan_step(uint32_t off, uint32_t& z) {
+    const uint32_t tz = dpp_u32<CTRL>(0u, z);
+    if (off >= (uint32_t)K) z += tz;
 }
 
 // Claim a slot for coarse bin `bin` (first caller wins; the slot's entry is
@@ -640,15 +643,21 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         hsum = point_entropy(mr, sh.lg_c, sh.lg_inv);
         if (off == 0u) hsum += point_entropy(ma, sh.lg_c, sh.lg_inv);
     }
-    uint32_t zw = zero_width ? 1u : 0u;
-    seg_scan_step<kDppRowShr1, 1>(off, dsum, hsum, zw);
-    seg_scan_step<kDppRowShr2, 2>(off, dsum, hsum, zw);
-    seg_scan_step<kDppRowShr4, 4>(off, dsum, hsum, zw);
-    seg_scan_step<kDppRowShr8, 8>(off, dsum, hsum, zw);
-    // equal consecutive points (tied data only): the candidate merges their
-    // masses first, from its intervals' values that its wave leaves in LDS
+    seg_scan_step<kDppRowShr1, 1>(off, dsum, hsum);
+    seg_scan_step<kDppRowShr2, 2>(off, dsum, hsum);
+    seg_scan_step<kDppRowShr4, 4>(off, dsum, hsum);
+    seg_scan_step<kDppRowShr8, 8>(off, dsum, hsum);
+    // equal consecutive points (tied data only): a candidate with a
+    // zero-width interval merges their masses first, from its intervals'
+    // values that its wave leaves in LDS
     PhaseC& pc = sh.u.c;
+    uint32_t zw = 0u;  // zero-width intervals up to this lane in its candidate
     if (__any(zero_width)) {
+        zw = zero_width ? 1u : 0u;
+        seg_scan_step<kDppRowShr1, 1>(off, zw);
+        seg_scan_step<kDppRowShr2, 2>(off, zw);
+        seg_scan_step<kDppRowShr4, 4>(off, zw);
+        seg_scan_step<kDppRowShr8, 8>(off, zw);
         pc.mr[tid] = mr;
         pc.ma[tid] = ma;
         pc.bv[tid] = bq;
