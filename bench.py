@@ -114,7 +114,9 @@ def decode_latency(torch, kvq, W, steps=1000, warmup=20):
     admitted by bisection to give lambda_prev; each measured step admits the
     next batch with one projected subgradient step from the running lambda.
     Per-call times are HIP events; the step time is wall clock around
-    eval -> solve (synchronising) -> quantize_pack -> synchronize."""
+    eval -> solve (synchronising) -> quantize_pack -> synchronize.  The same
+    steps are then timed through kvq_admit (one call, one wait per step),
+    from the same starting multiplier."""
     w = W.DECODE_ADMIT_FP16
     prev = [torch.from_numpy(h).cuda() for h in W.generate(w, which=0)]
     cur = [torch.from_numpy(h).cuda() for h in W.generate(w, which=1)]
@@ -123,6 +125,7 @@ def decode_latency(torch, kvq, W, steps=1000, warmup=20):
     st = torch.cuda.current_stream()
     lam, _ = kvq.admit(plan, prev, buf, w.B, kvq.KVQ_BISECT, w.iters, w.eta, 0.0,
                        w.extra["prev_seed"], st)
+    lam0 = lam
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     step_us, per = [], {"eval": [], "solve": [], "quantize_pack": []}
     for i in range(warmup + steps):
@@ -143,9 +146,19 @@ def decode_latency(torch, kvq, W, steps=1000, warmup=20):
             step_us.append((t1 - t0) * 1e6)
             for j, k in enumerate(per):
                 per[k].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)
+    # the same steps through kvq_admit: one C call and one wait per step
+    lam_f = lam0
+    fused_us = []
+    for i in range(warmup + steps):
+        t0 = time.perf_counter()
+        lam_f, _ = kvq.kvq_admit(plan, cur, buf, w.B, kvq.KVQ_SUBGRAD, w.iters, w.eta, lam_f, w.seed, st)
+        t1 = time.perf_counter()
+        if i >= warmup:
+            fused_us.append((t1 - t0) * 1e6)
     q = lambda v: {"p50": float(np.percentile(v, 50)), "p90": float(np.percentile(v, 90))}
     return {"workload": w.name, "steps": steps, "step_us": q(step_us),
-            "calls_us": {k: q(v) for k, v in per.items()}, "lambda_final": lam}
+            "calls_us": {k: q(v) for k, v in per.items()}, "lambda_final": lam,
+            "kvq_admit_step_us": q(fused_us), "kvq_admit_lambda_final": lam_f}
 
 
 def extensions(torch, kvq, W, w, plan, dev, buf, stream):

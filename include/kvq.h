@@ -242,6 +242,25 @@ kvq_status kvq_quantize_pack(const kvq_plan* p, const kvq_tensor* t, int32_t n_t
                              const uint64_t* word_off, uint64_t seed, uint32_t* codes,
                              uint64_t codes_capacity_words, hipStream_t s);
 
+/* One admission step in one call: kvq_eval_candidates, kvq_solve_lambda and
+   kvq_quantize_pack in that order on stream s, with the same arguments and
+   results as the three calls (the page's admission: score the candidates,
+   choose them under one multiplier, quantize; Key formulas (1)-(4)).  The
+   codebooks and offsets the solve writes stay on the device, so the
+   quantization is enqueued right behind it and the call waits once, at the
+   end, for lambda, the modelled rate and the status (KVQ_BISECT also waits
+   for its lambda = 0 probe).  For a decode loop this saves a host round trip
+   per admitted batch.  mode: KVQ_BISECT or KVQ_SUBGRAD (KVQ_EINVAL
+   otherwise).  On KVQ_ENONFINITE or KVQ_EINFEASIBLE the codes are written
+   from the solve's placeholder result and have no meaning.  Errors: those of
+   the three calls; arguments are all checked before anything is launched. */
+kvq_status kvq_admit(const kvq_plan* p, const kvq_tensor* t, int32_t n_tensors, double* D,
+                     double* H, float* stats, double B_bits_per_entry, int32_t mode,
+                     int32_t iters, double eta, double* lambda_io,
+                     double* rate_bits_per_entry_out, int32_t* choice, float* codebook,
+                     uint8_t* m, uint64_t* word_off, uint64_t seed, uint32_t* codes,
+                     uint64_t codes_capacity_words, void* workspace, hipStream_t s);
+
 /* Decode before attention (Implementation notes): xhat[r][t] = Q_r[code_t]
    in fp32, blocks in plan order, entries row-major in the block.
    Asynchronous. */

@@ -247,12 +247,12 @@ kvq_status kvq_plan_blocks(const kvq_tensor* t, int32_t nt, const kvq_block_spec
     return ok();
 }
 
-kvq_status kvq_eval_candidates(const kvq_plan* p, const kvq_tensor* t, int32_t nt, double* D, double* H,
-                               float* stats, void* workspace, hipStream_t s) {
-    kvq::Geom g;
-    kvq_status st = make_geom(p, t, nt, g);
-    if (st) return st;
-    if (!D || !H || !stats || !workspace) return fail(KVQ_EINVAL, "null output or workspace");
+namespace {
+
+// ---- the steps of the three admission calls, shared by kvq_admit ----
+
+kvq_status eval_enqueue(const kvq_plan* p, const kvq_tensor* t, int32_t nt, const kvq::Geom& g, double* D,
+                        double* H, float* stats, void* workspace, hipStream_t s) {
     hipError_t e = kvq::launch_ws_reset(workspace, s);
     if (e != hipSuccess) return hip_fail(e, "ws_reset");
     if (p->search == KVQ_GRIDS) {
@@ -270,19 +270,11 @@ kvq_status kvq_eval_candidates(const kvq_plan* p, const kvq_tensor* t, int32_t n
     return ok();
 }
 
-kvq_status kvq_solve_lambda(const kvq_plan* p, const double* D, const double* H, const float* stats,
-                            double B, int32_t mode, int32_t iters, double eta, double* lambda_io,
-                            double* rate_out, int32_t* choice, float* codebook, uint8_t* m,
-                            uint64_t* word_off, void* workspace, hipStream_t s) {
-    return kvq_solve_lambda_weighted(p, D, H, nullptr, stats, B, mode, iters, eta, lambda_io, rate_out,
-                                     choice, codebook, m, word_off, workspace, s);
-}
-
-kvq_status kvq_solve_lambda_weighted(const kvq_plan* p, const double* D, const double* H,
-                                     const double* weight, const float* stats, double B, int32_t mode,
-                                     int32_t iters, double eta, double* lambda_io, double* rate_out,
-                                     int32_t* choice, float* codebook, uint8_t* m, uint64_t* word_off,
-                                     void* workspace, hipStream_t s) {
+kvq_status solve_check(const kvq_plan* p, const double* D, const double* H, const double* weight,
+                       const float* stats, double B, int32_t mode, int32_t iters, double eta,
+                       const double* lambda_io, const double* rate_out, const int32_t* choice,
+                       const float* codebook, const uint8_t* m, const uint64_t* word_off,
+                       const void* workspace) {
     if (!valid_plan(p)) return fail(KVQ_EINVAL, "invalid plan");
     if (weight && p->search != KVQ_GRIDS) return fail(KVQ_EINVAL, "distortion weights need KVQ_GRIDS");
     if (!D || !H || !stats || !choice || !codebook || !m || !word_off || !workspace)
@@ -297,20 +289,43 @@ kvq_status kvq_solve_lambda_weighted(const kvq_plan* p, const double* D, const d
     const double lam_in = *lambda_io;
     if (mode == KVQ_SUBGRAD && (!isfinite(lam_in) || lam_in < 0.0 || !isfinite(eta)))
         return fail(KVQ_EINVAL, "subgradient needs finite lambda >= 0 and finite eta");
+    return ok();
+}
+
+// Where the solve's result will be found once the stream has reached it.
+struct SolveState {
+    kvq::SolveOut* out;  // pinned host buffer written by the last kernel, if `direct`
+    bool direct;
+};
+
+kvq_status solve_enqueue(const kvq_plan* p, const double* D, const double* H, const double* weight,
+                         const float* stats, double B, int32_t mode, int32_t iters, double lam_in,
+                         int32_t* choice, float* codebook, uint8_t* m, uint64_t* word_off, void* workspace,
+                         hipStream_t s, SolveState& ss) {
     kvq::RankTable rt;
     rank_table(*p, rt);
     void* dev_out = nullptr;
-    kvq::SolveOut* out = static_cast<kvq::SolveOut*>(kvq::staging_buffer(&dev_out));
-    bool direct = false;
-    hipError_t e = kvq::launch_solve(*p, rt, D, H, weight, stats, B, mode, iters, lam_in, choice,
-                                     codebook, m, word_off, workspace,
-                                     out ? static_cast<kvq::SolveOut*>(dev_out) : nullptr, &direct, s);
+    ss.out = static_cast<kvq::SolveOut*>(kvq::staging_buffer(&dev_out));
+    ss.direct = false;
+    const hipError_t e = kvq::launch_solve(*p, rt, D, H, weight, stats, B, mode, iters, lam_in, choice,
+                                           codebook, m, word_off, workspace,
+                                           ss.out ? static_cast<kvq::SolveOut*>(dev_out) : nullptr,
+                                           &ss.direct, s);
     if (e != hipSuccess) return hip_fail(e, "solve launch");
+    return ok();
+}
+
+// Wait for the stream, read the solve's result and turn it into lambda,
+// the modelled rate and a status.
+kvq_status solve_result(const kvq_plan* p, double B, int32_t mode, double eta, double lam_in,
+                        void* workspace, hipStream_t s, const SolveState& ss, double* lambda_io,
+                        double* rate_out) {
     kvq::SolveOut hdr;
-    if (direct) {
+    hipError_t e;
+    if (ss.direct) {
         // the last kernel wrote the result into the pinned buffer
         e = hipStreamSynchronize(s);
-        if (e == hipSuccess) memcpy(&hdr, out, sizeof hdr);
+        if (e == hipSuccess) memcpy(&hdr, ss.out, sizeof hdr);
     } else {
         kvq::WsHeader full;
         e = kvq::read_back(&full, workspace, sizeof full, s);
@@ -338,20 +353,90 @@ kvq_status kvq_solve_lambda_weighted(const kvq_plan* p, const double* D, const d
     return ok();
 }
 
+kvq_status quantize_check(const kvq_plan* p, const float* codebook, const uint8_t* m, const uint64_t* word_off,
+                          const uint32_t* codes, uint64_t cap) {
+    if (!codebook || !m || !word_off || (!codes && p->max_code_words))
+        return fail(KVQ_EINVAL, "null device pointer");
+    if (cap < p->max_code_words)
+        return fail(KVQ_ENOSPC, "codes capacity %llu words < plan.max_code_words %llu",
+                    (unsigned long long)cap, (unsigned long long)p->max_code_words);
+    return ok();
+}
+
+}  // namespace
+
+kvq_status kvq_eval_candidates(const kvq_plan* p, const kvq_tensor* t, int32_t nt, double* D, double* H,
+                               float* stats, void* workspace, hipStream_t s) {
+    kvq::Geom g;
+    kvq_status st = make_geom(p, t, nt, g);
+    if (st) return st;
+    if (!D || !H || !stats || !workspace) return fail(KVQ_EINVAL, "null output or workspace");
+    return eval_enqueue(p, t, nt, g, D, H, stats, workspace, s);
+}
+
+kvq_status kvq_solve_lambda(const kvq_plan* p, const double* D, const double* H, const float* stats,
+                            double B, int32_t mode, int32_t iters, double eta, double* lambda_io,
+                            double* rate_out, int32_t* choice, float* codebook, uint8_t* m,
+                            uint64_t* word_off, void* workspace, hipStream_t s) {
+    return kvq_solve_lambda_weighted(p, D, H, nullptr, stats, B, mode, iters, eta, lambda_io, rate_out,
+                                     choice, codebook, m, word_off, workspace, s);
+}
+
+kvq_status kvq_solve_lambda_weighted(const kvq_plan* p, const double* D, const double* H,
+                                     const double* weight, const float* stats, double B, int32_t mode,
+                                     int32_t iters, double eta, double* lambda_io, double* rate_out,
+                                     int32_t* choice, float* codebook, uint8_t* m, uint64_t* word_off,
+                                     void* workspace, hipStream_t s) {
+    kvq_status st = solve_check(p, D, H, weight, stats, B, mode, iters, eta, lambda_io, rate_out, choice,
+                                codebook, m, word_off, workspace);
+    if (st) return st;
+    const double lam_in = *lambda_io;
+    SolveState ss;
+    st = solve_enqueue(p, D, H, weight, stats, B, mode, iters, lam_in, choice, codebook, m, word_off,
+                       workspace, s, ss);
+    if (st) return st;
+    return solve_result(p, B, mode, eta, lam_in, workspace, s, ss, lambda_io, rate_out);
+}
+
 kvq_status kvq_quantize_pack(const kvq_plan* p, const kvq_tensor* t, int32_t nt, const float* codebook,
                              const uint8_t* m, const uint64_t* word_off, uint64_t seed, uint32_t* codes,
                              uint64_t cap, hipStream_t s) {
     kvq::Geom g;
     kvq_status st = make_geom(p, t, nt, g);
     if (st) return st;
-    if (!codebook || !m || !word_off || (!codes && p->max_code_words))
-        return fail(KVQ_EINVAL, "null device pointer");
-    if (cap < p->max_code_words)
-        return fail(KVQ_ENOSPC, "codes capacity %llu words < plan.max_code_words %llu",
-                    (unsigned long long)cap, (unsigned long long)p->max_code_words);
+    st = quantize_check(p, codebook, m, word_off, codes, cap);
+    if (st) return st;
     hipError_t e = kvq::launch_quantize(g, p->n_blocks, p->s, codebook, m, word_off, seed, codes, s);
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
     return ok();
+}
+
+kvq_status kvq_admit(const kvq_plan* p, const kvq_tensor* t, int32_t nt, double* D, double* H, float* stats,
+                     double B, int32_t mode, int32_t iters, double eta, double* lambda_io, double* rate_out,
+                     int32_t* choice, float* codebook, uint8_t* m, uint64_t* word_off, uint64_t seed,
+                     uint32_t* codes, uint64_t cap, void* workspace, hipStream_t s) {
+    kvq::Geom g;
+    kvq_status st = make_geom(p, t, nt, g);
+    if (st) return st;
+    if (!D || !H || !stats || !workspace) return fail(KVQ_EINVAL, "null output or workspace");
+    if (mode == KVQ_BISECT_GREEDY) return fail(KVQ_EINVAL, "kvq_admit takes KVQ_BISECT or KVQ_SUBGRAD");
+    st = solve_check(p, D, H, nullptr, stats, B, mode, iters, eta, lambda_io, rate_out, choice, codebook, m,
+                     word_off, workspace);
+    if (st) return st;
+    st = quantize_check(p, codebook, m, word_off, codes, cap);
+    if (st) return st;
+    const double lam_in = *lambda_io;
+    st = eval_enqueue(p, t, nt, g, D, H, stats, workspace, s);
+    if (st) return st;
+    SolveState ss;
+    st = solve_enqueue(p, D, H, nullptr, stats, B, mode, iters, lam_in, choice, codebook, m, word_off,
+                       workspace, s, ss);
+    if (st) return st;
+    // the codebooks and offsets stay on the device, so quantize_pack needs no
+    // host round trip after the solve; one wait at the end returns lambda
+    const hipError_t e = kvq::launch_quantize(g, p->n_blocks, p->s, codebook, m, word_off, seed, codes, s);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    return solve_result(p, B, mode, eta, lam_in, workspace, s, ss, lambda_io, rate_out);
 }
 
 kvq_status kvq_dequantize(const kvq_plan* p, const uint32_t* codes, const float* codebook, const uint8_t* m,

@@ -31,7 +31,8 @@ KVQ_SUBGRAD = 1
 KVQ_BISECT_GREEDY = 2
 
 EXPORTED = ("kvq_status_string", "kvq_last_error", "kvq_plan_blocks", "kvq_eval_candidates",
-            "kvq_solve_lambda", "kvq_solve_lambda_weighted", "kvq_quantize_pack", "kvq_dequantize",
+            "kvq_solve_lambda", "kvq_solve_lambda_weighted", "kvq_quantize_pack", "kvq_admit",
+            "kvq_dequantize",
             "kvq_ans_sizes",
             "kvq_ans_encode", "kvq_ans_decode", "kvq_decode_attention_workspace",
             "kvq_decode_attention")
@@ -105,6 +106,10 @@ def lib():
         L.kvq_quantize_pack.restype = i32
         L.kvq_quantize_pack.argtypes = [ctypes.POINTER(KvqPlan), ctypes.POINTER(KvqTensor), i32,
                                         vp, vp, vp, u64, vp, u64, vp]
+        L.kvq_admit.restype = i32
+        L.kvq_admit.argtypes = [ctypes.POINTER(KvqPlan), ctypes.POINTER(KvqTensor), i32, vp, vp, vp, f64,
+                                i32, i32, f64, ctypes.POINTER(f64), ctypes.POINTER(f64), vp, vp, vp, vp,
+                                u64, vp, u64, vp, vp]
         L.kvq_dequantize.restype = i32
         L.kvq_dequantize.argtypes = [ctypes.POINTER(KvqPlan), vp, vp, vp, vp, vp, vp]
         L.kvq_ans_sizes.restype = i32
@@ -316,6 +321,22 @@ def allocate(plan, device="cuda", dequant=False):
     if dequant:
         buf["xhat"] = torch.empty((R, plan.d_block), dtype=torch.float32, device=device)
     return buf
+
+
+def kvq_admit(plan, tensors, buf, B, mode=KVQ_BISECT, iters=40, eta=1e-3, lam=0.0, seed=0, stream=None):
+    """kvq_eval_candidates, kvq_solve_lambda and kvq_quantize_pack in one C
+    call with one wait at the end, on the buffers of ``buf`` (as allocate()
+    returns them).  Returns ``(lambda, rate_bits_per_entry)``."""
+    arr = _tensor_array(tensors)
+    lam_io = ctypes.c_double(lam)
+    rate = ctypes.c_double(0.0)
+    codes = buf["codes"]
+    _check(lib().kvq_admit(ctypes.byref(plan), arr, len(tensors), _ptr(buf["D"]), _ptr(buf["H"]),
+                           _ptr(buf["stats"]), float(B), mode, iters, float(eta), ctypes.byref(lam_io),
+                           ctypes.byref(rate), _ptr(buf["choice"]), _ptr(buf["codebook"]), _ptr(buf["m"]),
+                           _ptr(buf["off"]), int(seed), _ptr(codes), int(codes.numel()),
+                           _ptr(buf["workspace"]), _stream(stream)))
+    return lam_io.value, rate.value
 
 
 def admit(plan, tensors, buf, B, mode=KVQ_BISECT, iters=40, eta=1e-3, lam=0.0, seed=0,

@@ -159,6 +159,30 @@ def test_calls_validate_before_launch(L):
     assert Lb.kvq_dequantize(ctypes.byref(p), 8, None, 8, 8, 8, None) == kvq.KVQ_EINVAL
 
 
+def test_admit_validates_before_launch(L):
+    """kvq_admit checks the arguments of all three steps before it launches
+    anything: null tables, a greedy or unknown mode, a negative budget and a
+    short code buffer are refused on the host (the pointers are not
+    dereferenced, so no GPU is needed)."""
+    t = np.zeros((1, 2, 64, 128), dtype=np.float16)
+    p = kvq.kvq_plan_blocks([t], 32, 128, 16)
+    lam = ctypes.c_double(0.0)
+    rate = ctypes.c_double(0.0)
+    Lb = kvq.lib()
+    arr = kvq._tensor_array([t])
+
+    def call(D=8, B=2.0, mode=kvq.KVQ_BISECT, cap=None):
+        return Lb.kvq_admit(ctypes.byref(p), arr, 1, D, 8, 8, B, mode, 40, 1e-3, ctypes.byref(lam),
+                            ctypes.byref(rate), 8, 8, 8, 8, 0, 8,
+                            p.max_code_words if cap is None else cap, 8, None)
+    assert call(D=None) == kvq.KVQ_EINVAL
+    assert call(mode=kvq.KVQ_BISECT_GREEDY) == kvq.KVQ_EINVAL
+    assert "kvq_admit" in kvq.last_error()
+    assert call(mode=7) == kvq.KVQ_EINVAL
+    assert call(B=-1.0) == kvq.KVQ_EINVAL
+    assert call(cap=p.max_code_words - 1) == kvq.KVQ_ENOSPC
+
+
 def test_entropy_coding_sizes_and_validation(L):
     """kvq_ans_sizes: 4 bytes per fixed-width word plus a per-block margin
     (table, final states, and the coder's slack); encode and decode refuse
