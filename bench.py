@@ -168,7 +168,7 @@ def extensions(torch, kvq, W, w, plan, dev, buf, stream):
     uncompressed cache, and a decode stream's multiplier trace."""
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
 
-    def timed(fn, reps=5):
+    def timed(fn, reps=20):
         fn()
         torch.cuda.synchronize()
         ts = []

@@ -33,15 +33,31 @@ constexpr int kChunkSplit = 16;           // chunks (32-token blocks) per workgr
 constexpr int kHD = 128;                  // head dim
 constexpr int kTB = 32;                   // tokens per block
 
-// The 8 codes of width w of entries 8u .. 8u + 7 of a block's code stream
-// (8 w <= 32 bits, so one funnel shift gathers them).
-__device__ __forceinline__ uint32_t codes8(const uint32_t* cw, uint32_t nwords, int w, int u) {
-    if (w == 0) return 0u;
-    const uint32_t byte = (uint32_t)w * (uint32_t)u;  // w bytes per 8 codes
-    const uint32_t q = byte >> 2, sh = 8u * (byte & 3u);
-    const uint32_t a = cw[q];
-    const uint32_t b = (sh + 8u * (uint32_t)w > 32u && q + 1 < nwords) ? cw[q + 1] : 0u;
-    return (uint32_t)((((uint64_t)b << 32) | a) >> sh);
+// The 8 codes of width w >= 1 of entries 8u .. 8u + 7 of a block's code
+// stream of nwords >= 1 words sit in words q = (w u) / 4 and q + 1, shifted
+// by sh = 8 ((w u) mod 4) bits (8 w <= 32 bits, so one funnel shift gathers
+// them).  The second word is needed only when the group straddles a word
+// boundary, which never happens in the block's last word, so its index is
+// clamped into the stream and both loads are issued unconditionally.  The
+// words are kept apart from the shift so that a load is waited on only where
+// its codes are used.
+struct CodeWords {
+    uint32_t a, b;
+};
+
+__device__ __forceinline__ CodeWords load_codes8(const uint32_t* cw, uint32_t nwords, int w, int u) {
+    const uint32_t q = ((uint32_t)w * (uint32_t)u) >> 2;
+    return {cw[q], cw[min(q + 1, nwords - 1)]};
+}
+
+__device__ __forceinline__ uint32_t codes8(CodeWords x, int w, int u) {
+    const uint32_t sh = 8u * (((uint32_t)w * (uint32_t)u) & 3u);
+    return (uint32_t)((((uint64_t)x.b << 32) | x.a) >> sh);
+}
+
+// Field [off, off + w) of x.
+__device__ __forceinline__ uint32_t field(uint32_t x, uint32_t off, uint32_t w) {
+    return __builtin_amdgcn_ubfe(x, off, w);
 }
 
 // Sum over a 16-lane row, the same bits in every lane: partner swaps inside
@@ -53,18 +69,26 @@ constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2, 3, 0, 1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
 
+// Every source lane of these patterns lies in the row, so bound_ctrl never
+// takes effect; it lets the move fold into the add (v_add_f32_dpp).
 template <int kCtrl>
 __device__ __forceinline__ float dpp_f32(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ float xor_sum16(float v) {
-    v += dpp_f32<kDppQuadXor1>(v);
-    v += dpp_f32<kDppQuadXor2>(v);
-    v += dpp_f32<kDppRowHalfMirror>(v);
-    v += dpp_f32<kDppRowMirror>(v);
+    v = dpp_f32<kDppQuadXor1>(v) + v;
+    v = dpp_f32<kDppQuadXor2>(v) + v;
+    v = dpp_f32<kDppRowHalfMirror>(v) + v;
+    v = dpp_f32<kDppRowMirror>(v) + v;
     return v;
 }
+
+// 2^x on the transcendental unit (scores live in base-2 units: q is
+// pre-scaled by log2 e, so 2^(s - m) is the softmax weight e^(s' - m')).
+__device__ __forceinline__ float pow2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace
 
@@ -106,7 +130,7 @@ attn_split_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ 
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            qv[g][i] = scale * q[((int64_t)o * heads * G + h * G + g) * kHD + 8 * f + i];
+            qv[g][i] = (scale * kLog2e) * q[((int64_t)o * heads * G + h * G + g) * kHD + 8 * f + i];
     __syncthreads();
     float mx[G], sl[G], acc[G][8];
 #pragma unroll
@@ -116,41 +140,72 @@ attn_split_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ 
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[g][i] = 0.0f;
     }
-    for (int c = 0; c < c1 - c0; ++c) {
-        const int wk = wdt[0][c], wv = wdt[1][c];
-        const uint32_t mk = (1u << wk) - 1u, mv = (1u << wv) - 1u;
+    // Per chunk: the K codes of tokens j and j + 16 give two partial scores
+    // per query head, summed over the row's 16 feature groups; one maximum
+    // update covers both tokens; then the V codes are weighted in.  The next
+    // chunk's codes are loaded before this chunk's work, hiding their latency.
+    const int nc = c1 - c0;
+    const int ug[2] = {16 * j + f, 16 * (j + 16) + f};  // 8-entry groups of tokens j, j + 16
+    CodeWords kn[2] = {}, vn[2] = {};
+    auto load = [&](int c, CodeWords (&kw)[2], CodeWords (&vw)[2]) {
+        const int wk = __builtin_amdgcn_readfirstlane(wdt[0][c]);
+        const int wv = __builtin_amdgcn_readfirstlane(wdt[1][c]);
+        if (wk) {
+            const uint32_t* cw = codes + wof[0][c];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int u = 16 * (j + 16 * half) + f;  // 8-entry group of token j + 16 half
-            const uint32_t kc = codes8(codes + wof[0][c], nwd[0][c], wk, u);
-            float sc[G];
+            for (int t = 0; t < 2; ++t) kw[t] = load_codes8(cw, nwd[0][c], wk, ug[t]);
+        }
+        if (wv) {
+            const uint32_t* cw = codes + wof[1][c];
 #pragma unroll
-            for (int g = 0; g < G; ++g) sc[g] = 0.0f;
+            for (int t = 0; t < 2; ++t) vw[t] = load_codes8(cw, nwd[1][c], wv, ug[t]);
+        }
+    };
+    if (nc > 0) load(0, kn, vn);
+    for (int c = 0; c < nc; ++c) {
+        const uint32_t wk = (uint32_t)__builtin_amdgcn_readfirstlane(wdt[0][c]);
+        const uint32_t wv = (uint32_t)__builtin_amdgcn_readfirstlane(wdt[1][c]);
+        const CodeWords kw[2] = {kn[0], kn[1]}, vw[2] = {vn[0], vn[1]};
+        if (c + 1 < nc) load(c + 1, kn, vn);
+        // width 0 (a one-point codebook) leaves the words unread; field()
+        // of width 0 is 0 whatever they hold
+        const uint32_t kc[2] = {codes8(kw[0], wk, ug[0]), codes8(kw[1], wk, ug[1])};
+        const uint32_t vc[2] = {codes8(vw[0], wv, ug[0]), codes8(vw[1], wv, ug[1])};
+        float sc[2][G];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) sc[t][g] = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float kv = cb[0][c][(kc >> (wk * i)) & mk];
+                const float kv = cb[0][c][field(kc[t], wk * i, wk)];
 #pragma unroll
-                for (int g = 0; g < G; ++g) sc[g] = fmaf(qv[g][i], kv, sc[g]);
+                for (int g = 0; g < G; ++g) sc[t][g] = fmaf(qv[g][i], kv, sc[t][g]);
             }
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float sg = xor_sum16(sc[g]);
-                if (sg > mx[g]) {  // new maximum: rescale the running sums
-                    const float corr = __expf(mx[g] - sg);
-                    mx[g] = sg;
-                    sl[g] *= corr;
+            for (int g = 0; g < G; ++g) sc[t][g] = xor_sum16(sc[t][g]);
+        }
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[g][i] *= corr;
-                }
-                sc[g] = __expf(sg - mx[g]);
-                sl[g] += sc[g];
+        for (int g = 0; g < G; ++g) {
+            const float mn = fmaxf(mx[g], fmaxf(sc[0][g], sc[1][g]));
+            if (mn > mx[g]) {  // new maximum: rescale the running sums
+                const float corr = pow2(mx[g] - mn);
+                mx[g] = mn;
+                sl[g] *= corr;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[g][i] *= corr;
             }
-            const uint32_t vc = codes8(codes + wof[1][c], nwd[1][c], wv, u);
+            sc[0][g] = pow2(sc[0][g] - mx[g]);
+            sc[1][g] = pow2(sc[1][g] - mx[g]);
+            sl[g] += sc[0][g] + sc[1][g];
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float vv = cb[1][c][(vc >> (wv * i)) & mv];
+                const float vv = cb[1][c][field(vc[t], wv * i, wv)];
 #pragma unroll
-                for (int g = 0; g < G; ++g) acc[g][i] = fmaf(sc[g], vv, acc[g][i]);
+                for (int g = 0; g < G; ++g) acc[g][i] = fmaf(sc[t][g], vv, acc[g][i]);
             }
         }
     }
@@ -160,7 +215,7 @@ attn_split_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ 
         float M = mx[g];
         M = fmaxf(M, __shfl_xor(M, 16, 64));
         M = fmaxf(M, __shfl_xor(M, 32, 64));
-        const float e = mx[g] == -__builtin_huge_valf() ? 0.0f : __expf(mx[g] - M);
+        const float e = mx[g] == -__builtin_huge_valf() ? 0.0f : pow2(mx[g] - M);
         float L = sl[g] * e;
         L += __shfl_xor(L, 16, 64);
         L += __shfl_xor(L, 32, 64);
@@ -190,11 +245,12 @@ attn_split_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ 
         float L = 0.0f, A = 0.0f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const float e2 = xm[w][g] == -__builtin_huge_valf() ? 0.0f : __expf(xm[w][g] - M);
+            const float e2 = xm[w][g] == -__builtin_huge_valf() ? 0.0f : pow2(xm[w][g] - M);
             L = fmaf(xl[w][g], e2, L);
             A = fmaf(xa[w][g][d], e2, A);
         }
-        // partial layout: [o][head h * G + g][split][kHD + 2] = (A..., M, L)
+        // partial layout: [o][head h * G + g][split][kHD + 2] = (A..., M, L),
+        // M in base-2 units
         float* pp = part + (((int64_t)o * heads * G + h * G + g) * splits + sp) * (kHD + 2);
         pp[d] = A;
         if (d == 0) {
@@ -214,7 +270,7 @@ attn_merge_kernel(const float* __restrict__ part, int splits, float* __restrict_
     float L = 0.0f, A = 0.0f;
     for (int sp = 0; sp < splits; ++sp) {
         const float m = pp[sp * (kHD + 2) + kHD];
-        const float e = m == -__builtin_huge_valf() ? 0.0f : __expf(m - M);
+        const float e = m == -__builtin_huge_valf() ? 0.0f : pow2(m - M);
         L = fmaf(pp[sp * (kHD + 2) + kHD + 1], e, L);
         A = fmaf(pp[sp * (kHD + 2) + d], e, A);
     }
