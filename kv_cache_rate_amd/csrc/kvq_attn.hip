@@ -45,13 +45,14 @@ struct CodeWords {
     uint32_t a, b;
 };
 
+// (w u < 2^24: a 24-bit multiply suffices)
 __device__ __forceinline__ CodeWords load_codes8(const uint32_t* cw, uint32_t nwords, int w, int u) {
-    const uint32_t q = ((uint32_t)w * (uint32_t)u) >> 2;
+    const uint32_t q = __umul24((uint32_t)w, (uint32_t)u) >> 2;
     return {cw[q], cw[min(q + 1, nwords - 1)]};
 }
 
 __device__ __forceinline__ uint32_t codes8(CodeWords x, int w, int u) {
-    const uint32_t sh = 8u * (((uint32_t)w * (uint32_t)u) & 3u);
+    const uint32_t sh = 8u * (__umul24((uint32_t)w, (uint32_t)u) & 3u);
     return (uint32_t)((((uint64_t)x.b << 32) | x.a) >> sh);
 }
 

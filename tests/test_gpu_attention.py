@@ -56,7 +56,7 @@ def _run(w, tensors, q_heads, seed=3):
     vmax = np.abs(V).max()
     _say(f"{w.name} q_heads={q_heads}: max |o - o_ref| = {err:.3g} (max|v| {vmax:.3g})")
     assert err <= 2e-3 * vmax
-    return err / vmax
+    return buf["m"].cpu().numpy()
 
 
 @pytest.mark.parametrize("q_heads", [32, 64])
@@ -82,4 +82,31 @@ def test_ragged_tail_split():
     w = W.Workload(name="attn_ragged", index=0, tensors=(("K", x.shape), ("V", v.shape)),
                    dtype="f16", tokens_per_block=32, dims_per_block=128, s=16, search="grids",
                    B=2.0, mode="bisect")
+    _run(w, [x, v], 8)
+
+
+def test_narrow_and_constant_blocks():
+    """Code widths 0 to 4 in one cache: constant chunks (one-point
+    codebooks, no code words), chunks of two or three distinct values, and a
+    low budget that pushes the rest to two or three points; K and V chunks
+    of one token range get different widths."""
+    rng = np.random.default_rng(22)
+    shape = (2, 2, 37 * 32, 128)
+    x = rng.standard_normal(shape).astype(np.float16)
+    v = rng.laplace(size=shape).astype(np.float16)
+    xc = x.reshape(2, 2, 37, 32, 128)
+    vc = v.reshape(2, 2, 37, 32, 128)
+    xc[0, 0, 3] = 0.5
+    xc[1, 1, 36] = -2.0
+    vc[0, 1, 0] = 1.25
+    vc[1, 0, 20] = 0.0
+    xc[0, 1, 7] = rng.choice(np.array([-1.0, 2.0], dtype=np.float16), size=(32, 128))
+    vc[1, 1, 9] = rng.choice(np.array([-0.5, 0.25, 3.0], dtype=np.float16), size=(32, 128))
+    w = W.Workload(name="attn_narrow", index=0, tensors=(("K", x.shape), ("V", v.shape)),
+                   dtype="f16", tokens_per_block=32, dims_per_block=128, s=16, search="grids",
+                   B=1.2, mode="bisect")
+    m = _run(w, [x, v], 4)
+    widths = set(int(np.ceil(np.log2(k))) for k in np.unique(m))
+    _say(f"code widths {sorted(widths)}")
+    assert {0, 1, 2} <= widths
     _run(w, [x, v], 8)
