@@ -152,6 +152,40 @@ def test_ties_constant_and_negative_zero(kernel_path):
     assert g["m"][0] == 1 and g["off"][1] == 0
 
 
+def test_fp16_range_extremes(kernel_path):
+    """The ends of the fp16 range: blocks of subnormals only (the lowest
+    binade, where a value is its mantissa times 2^-24), subnormals mixed with
+    small normals, magnitudes log-uniform over 2^-24 .. 65504 with both
+    extremes present, values packed just below 65504, the three levels
+    {-65504, 0, 65504}, and negative subnormals with -0; two Gaussian
+    blocks as a control."""
+    rng = np.random.default_rng(61)
+    T, D = 32, 128
+    sub = rng.integers(1, 1024, size=(T, D)) * 2.0 ** -24          # subnormal magnitudes
+    sgn = rng.choice([-1.0, 1.0], size=(T, D))
+    blocks = [
+        sgn * sub,
+        sgn * np.where(rng.random((T, D)) < 0.5, sub, np.exp2(rng.uniform(-14.0, -10.0, (T, D)))),
+        sgn * np.exp2(rng.uniform(-24.0, np.log2(65504.0), (T, D))),
+        rng.uniform(32768.0, 65504.0, (T, D)),
+        rng.choice([-65504.0, 0.0, 65504.0], size=(T, D)),
+        -sub * (rng.random((T, D)) < 0.7),
+        rng.standard_normal((T, D)),
+        rng.standard_normal((T, D)) * 3.0,
+    ]
+    blocks[2][0, :4] = [65504.0, -65504.0, 2.0 ** -24, -(2.0 ** -24)]
+    blocks[2][1, :2] = [2.0 ** -14, -(2.0 ** -14)]                   # smallest normals
+    x = np.stack(blocks)[None].astype(np.float16)                     # (1, 8, 32, 128)
+    assert np.isfinite(x).all()
+    assert (x.view(np.uint16)[0, 5] == 0x8000).any()                  # -0 present
+    w = W.Workload(name="fp16_extremes", index=0, tensors=(("K", x.shape),), dtype="f16",
+                   tokens_per_block=T, dims_per_block=D, s=16, search="grids", B=1.5,
+                   mode="bisect")
+    g, o, rep = _check(w, [x])
+    assert g["m"].shape == (8,)
+    assert g["m"][4] <= 3  # three distinct levels
+
+
 @pytest.mark.parametrize("dtype,s,B,mode", [(np.float16, 16, 1.0, "bisect"), (np.float32, 8, 1.2, "bisect"),
                                              (np.float16, 16, 2.0, "subgrad")])
 def test_single_block(dtype, s, B, mode):
