@@ -270,20 +270,29 @@ ans_decode_kernel(const uint8_t* __restrict__ stream, const uint64_t* __restrict
     const int m = valid ? min(max((int)m_in[r], 1), s) : 1;
     const uint32_t M = 1u << k;
     __syncthreads();
-    const uint16_t* lw = staged ? reinterpret_cast<const uint16_t*>(lds_words)
-                                : reinterpret_cast<const uint16_t*>(stream + b0);
     const uint64_t wbeg = valid ? (block_off[r] - b0) / 2 : 0;   // block start, in words
     const uint64_t wend = valid ? (block_off[r + 1] - b0) / 2 : 0;
-    const uint16_t* wd = lw + wbeg;
+    // kept apart so that each path's refills use its own memory's loads
+    const uint16_t* ld = reinterpret_cast<const uint16_t*>(lds_words) + wbeg;
+    const uint16_t* gd = reinterpret_cast<const uint16_t*>(stream + b0) + wbeg;
     const uint32_t nwd = (uint32_t)min(wend - wbeg, (uint64_t)0xffffffffu);
     if (valid && i == 0) {
+        // the 16 table words first (independent loads), then the prefix
+        uint32_t fw[kMaxS];
+        if (staged) {
+#pragma unroll
+            for (int j = 0; j < kMaxS; ++j) fw[j] = j < m && (uint32_t)j < nwd ? ld[j] : 0u;
+        } else {
+#pragma unroll
+            for (int j = 0; j < kMaxS; ++j) fw[j] = j < m && (uint32_t)j < nwd ? gd[j] : 0u;
+        }
         uint32_t c = 0;
+#pragma unroll
         for (int j = 0; j < kMaxS; ++j) {
-            const uint32_t f = j < m && (uint32_t)j < nwd ? wd[j] : 0u;
             cum[bl][j] = j < m ? c : M;
-            frq[bl][j] = f;
+            frq[bl][j] = fw[j];
             q[bl][j] = j < m ? codebook[r * s + j] : 0.0f;
-            c += f;
+            c += fw[j];
         }
         cum[bl][kMaxS] = M;
     }
@@ -294,9 +303,9 @@ ans_decode_kernel(const uint8_t* __restrict__ stream, const uint64_t* __restrict
         atomicOr(&ws->status, kStatusAnsCorrupt);
         return;
     }
-    const bool ok = staged ? decode_steps(reinterpret_cast<const uint16_t*>(lds_words) + wbeg, nwd, cum[bl],
-                                          frq[bl], q[bl], m, n, k, i, tid & 63, xhat + r * (int64_t)n)
-                           : decode_steps(wd, nwd, cum[bl], frq[bl], q[bl], m, n, k, i, tid & 63,
+    const bool ok = staged ? decode_steps(ld, nwd, cum[bl], frq[bl], q[bl], m, n, k, i, tid & 63,
+                                          xhat + r * (int64_t)n)
+                           : decode_steps(gd, nwd, cum[bl], frq[bl], q[bl], m, n, k, i, tid & 63,
                                           xhat + r * (int64_t)n);
     if (!ok) atomicOr(&ws->status, kStatusAnsCorrupt);
 }
