@@ -312,7 +312,9 @@ kvq_status kvq_ans_decode(const kvq_plan* p, const void* stream, const uint64_t*
    o = sum_t softmax_t(scale q . k_t) v_t over every cached token, k_t and v_t
    the stored codepoints.  The plan must hold K (tensor 0) and V (tensor 1)
    [outer, heads, tokens, 128] cut into head x 32-token blocks; query head g
-   reads KV head g / G, G = q_heads / heads in {1, 2, 4}.  fp32 arithmetic. */
+   reads KV head g / G, G = q_heads / heads any whole number >= 1 (run as
+   passes over 4, 2 and 1 query heads, each reading the codes once); K and V
+   of equal shape, outer and heads at most 65535.  fp32 arithmetic. */
 
 /* Bytes of the split-partials workspace for q_heads query heads (host). */
 kvq_status kvq_decode_attention_workspace(const kvq_plan* p, int32_t q_heads, uint64_t* bytes);

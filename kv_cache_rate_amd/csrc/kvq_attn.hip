@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(kAT2)
 attn_split_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ codebook,
                   const uint8_t* __restrict__ m_in, const uint64_t* __restrict__ word_off,
                   int64_t nbK, int heads, int chunks, int s, const float* __restrict__ q,
-                  float scale, float* __restrict__ part, int splits) {
+                  float scale, float* __restrict__ part, int splits, int gtot, int goff) {
     __shared__ float cb[2][kChunkSplit][kMaxS];
     __shared__ int wdt[2][kChunkSplit];
     __shared__ uint64_t wof[2][kChunkSplit];
@@ -131,7 +131,7 @@ attn_split_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ 
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            qv[g][i] = (scale * kLog2e) * q[((int64_t)o * heads * G + h * G + g) * kHD + 8 * f + i];
+            qv[g][i] = (scale * kLog2e) * q[((int64_t)o * heads * gtot + h * gtot + goff + g) * kHD + 8 * f + i];
     __syncthreads();
     float mx[G], sl[G], acc[G][8];
 #pragma unroll
@@ -250,9 +250,9 @@ attn_split_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ 
             L = fmaf(xl[w][g], e2, L);
             A = fmaf(xa[w][g][d], e2, A);
         }
-        // partial layout: [o][head h * G + g][split][kHD + 2] = (A..., M, L),
-        // M in base-2 units
-        float* pp = part + (((int64_t)o * heads * G + h * G + g) * splits + sp) * (kHD + 2);
+        // partial layout: [o][query head h * gtot + goff + g][split][kHD + 2]
+        // = (A..., M, L), M in base-2 units
+        float* pp = part + (((int64_t)o * heads * gtot + h * gtot + goff + g) * splits + sp) * (kHD + 2);
         pp[d] = A;
         if (d == 0) {
             pp[kHD] = M;
@@ -291,24 +291,28 @@ hipError_t launch_decode_attention(const uint32_t* codes, const float* codebook,
     const int splits = (chunks + kChunkSplit - 1) / kChunkSplit;
     const dim3 grid((unsigned)splits, (unsigned)heads, (unsigned)outer);
     float* part = (float*)work;
-    switch (group) {
-    case 1:
-        hipLaunchKernelGGL(attn_split_kernel<1>, grid, dim3(kAT2), 0, st, codes, codebook, m, word_off,
-                           nbK, heads, chunks, s, q, scale, part, splits);
-        break;
-    case 2:
-        hipLaunchKernelGGL(attn_split_kernel<2>, grid, dim3(kAT2), 0, st, codes, codebook, m, word_off,
-                           nbK, heads, chunks, s, q, scale, part, splits);
-        break;
-    case 4:
-        hipLaunchKernelGGL(attn_split_kernel<4>, grid, dim3(kAT2), 0, st, codes, codebook, m, word_off,
-                           nbK, heads, chunks, s, q, scale, part, splits);
-        break;
-    default:
-        return hipErrorInvalidValue;
+    // a group of any size runs as launches over 4, 2 and 1 of its query
+    // heads (each reads the codes once); 4 is the most that the registers
+    // hold at full occupancy
+    if (group < 1) return hipErrorInvalidValue;
+    for (int goff = 0; goff < group;) {
+        const int left = group - goff;
+        if (left >= 4) {
+            hipLaunchKernelGGL(attn_split_kernel<4>, grid, dim3(kAT2), 0, st, codes, codebook, m, word_off,
+                               nbK, heads, chunks, s, q, scale, part, splits, group, goff);
+            goff += 4;
+        } else if (left >= 2) {
+            hipLaunchKernelGGL(attn_split_kernel<2>, grid, dim3(kAT2), 0, st, codes, codebook, m, word_off,
+                               nbK, heads, chunks, s, q, scale, part, splits, group, goff);
+            goff += 2;
+        } else {
+            hipLaunchKernelGGL(attn_split_kernel<1>, grid, dim3(kAT2), 0, st, codes, codebook, m, word_off,
+                               nbK, heads, chunks, s, q, scale, part, splits, group, goff);
+            goff += 1;
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)(outer * heads * group)), dim3(kHD), 0, st,
                        part, splits, out);
     return hipGetLastError();

@@ -505,11 +505,13 @@ static kvq_status attention_shape(const kvq_plan* p, int32_t q_heads, int& group
     if (p->n_tensors != 2) return fail(KVQ_EINVAL, "decode attention needs the K and V tensors");
     if (p->tokens_per_block != 32 || p->dims_per_block != 128 || p->shape[0][3] != 128)
         return fail(KVQ_EINVAL, "decode attention supports head x 32-token blocks of head_dim 128");
+    for (int d = 0; d < 4; ++d)
+        if (p->shape[1][d] != p->shape[0][d]) return fail(KVQ_EINVAL, "K and V must have the same shape");
     const int64_t heads = p->shape[0][1];
+    if (p->shape[0][0] > 65535 || heads > 65535)
+        return fail(KVQ_EINVAL, "decode attention takes at most 65535 outer slices and KV heads");
     if (q_heads <= 0 || q_heads % heads) return fail(KVQ_EINVAL, "query heads must be a multiple of KV heads");
     group = (int)(q_heads / heads);
-    if (group != 1 && group != 2 && group != 4)
-        return fail(KVQ_EINVAL, "query heads per KV head must be 1, 2 or 4 (got %d)", group);
     return ok();
 }
 

@@ -211,8 +211,11 @@ def test_decode_attention_validation(L):
     assert kvq.kvq_decode_attention_workspace(p, 32) == 1 * 8 * 4 * 1 * (128 + 2) * 4
     Lb = kvq.lib()
     b = ctypes.c_uint64(0)
-    assert Lb.kvq_decode_attention_workspace(ctypes.byref(p), 24, ctypes.byref(b)) == kvq.KVQ_EINVAL
+    # any whole number of query heads per KV head (here 3 and 8)
+    assert kvq.kvq_decode_attention_workspace(p, 24) == 1 * 8 * 3 * 1 * (128 + 2) * 4
+    assert kvq.kvq_decode_attention_workspace(p, 64) == 1 * 8 * 8 * 1 * (128 + 2) * 4
     assert Lb.kvq_decode_attention_workspace(ctypes.byref(p), 20, ctypes.byref(b)) == kvq.KVQ_EINVAL
+    assert Lb.kvq_decode_attention_workspace(ctypes.byref(p), 0, ctypes.byref(b)) == kvq.KVQ_EINVAL
     p1 = kvq.kvq_plan_blocks([k], 32, 128, 16)
     assert Lb.kvq_decode_attention_workspace(ctypes.byref(p1), 8, ctypes.byref(b)) == kvq.KVQ_EINVAL
     p2 = kvq.kvq_plan_blocks([k, k], 16, 128, 16)

@@ -108,5 +108,18 @@ def test_narrow_and_constant_blocks():
     m = _run(w, [x, v], 4)
     widths = set(int(np.ceil(np.log2(k))) for k in np.unique(m))
     _say(f"code widths {sorted(widths)}")
-    assert {0, 1, 2} <= widths
+    assert widths == {0, 1, 2, 3, 4}
     _run(w, [x, v], 8)
+
+
+@pytest.mark.parametrize("group", [3, 8])
+def test_larger_and_odd_groups(group):
+    """8 query heads per KV head (run as two passes of 4) and 3 (a pass of
+    2 and one of 1): query head g reads KV head g // G."""
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((2, 2, 40 * 32, 128)).astype(np.float16)
+    v = rng.laplace(size=(2, 2, 40 * 32, 128)).astype(np.float16)
+    w = W.Workload(name=f"attn_g{group}", index=0, tensors=(("K", x.shape), ("V", v.shape)),
+                   dtype="f16", tokens_per_block=32, dims_per_block=128, s=16, search="grids",
+                   B=2.0, mode="bisect")
+    _run(w, [x, v], 2 * group)
