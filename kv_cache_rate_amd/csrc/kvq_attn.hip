@@ -166,12 +166,13 @@ attn_split_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ 
     for (int c = 0; c < nc; ++c) {
         const uint32_t wk = (uint32_t)__builtin_amdgcn_readfirstlane(wdt[0][c]);
         const uint32_t wv = (uint32_t)__builtin_amdgcn_readfirstlane(wdt[1][c]);
-        const CodeWords kw[2] = {kn[0], kn[1]}, vw[2] = {vn[0], vn[1]};
+        // this chunk's codes from the words loaded one iteration ago (width 0,
+        // a one-point codebook, leaves them unread; field() of width 0 is 0
+        // whatever they hold), then the next chunk's loads into the same
+        // registers
+        const uint32_t kc[2] = {codes8(kn[0], wk, ug[0]), codes8(kn[1], wk, ug[1])};
+        const uint32_t vc[2] = {codes8(vn[0], wv, ug[0]), codes8(vn[1], wv, ug[1])};
         if (c + 1 < nc) load(c + 1, kn, vn);
-        // width 0 (a one-point codebook) leaves the words unread; field()
-        // of width 0 is 0 whatever they hold
-        const uint32_t kc[2] = {codes8(kw[0], wk, ug[0]), codes8(kw[1], wk, ug[1])};
-        const uint32_t vc[2] = {codes8(vw[0], wv, ug[0]), codes8(vw[1], wv, ug[1])};
         float sc[2][G];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
