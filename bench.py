@@ -211,21 +211,23 @@ def extensions(torch, kvq, W, w, plan, dev, buf, stream):
         out["decode_attention"] = {"query_heads": Hq, "tokens": T, "layers": L, "fused_quantized_ms": t_att,
                                    "torch_sdpa_fp16_uncompressed_ms": t_sdpa,
                                    "codes_GB": 4.0 * float(buf["off"][-1].item()) / 1e9}
-    # sensitivity-weighted distortion against the plain solve, on the same
-    # score table at a budget that binds (the step's own budget leaves the
-    # multiplier at 0 here); last, since it rewrites the step's choices
+    # sensitivity-weighted distortion and the greedy fill against the plain
+    # solve, on the same score table at a budget that binds (the step's own
+    # budget leaves the multiplier at 0 here); last, since they rewrite the
+    # step's choices
     if plan.search == kvq.KVQ_GRIDS:
         Bw = 1.5
         wd = torch.from_numpy(W.sensitivity_weights(w)).cuda()
         res = {}
-        for name, weighted in (("plain", False), ("weighted", True)):
+        for name, weighted, mode in (("plain", False, kvq.KVQ_BISECT), ("weighted", True, kvq.KVQ_BISECT),
+                                     ("plain_greedy_fill", False, kvq.KVQ_BISECT_GREEDY)):
             def solve():
                 if weighted:
                     return kvq.kvq_solve_lambda_weighted(plan, buf["D"], buf["H"], wd, buf["stats"], Bw,
                                                          kvq.KVQ_BISECT, 40, 0.0, 0.0, buf["choice"],
                                                          buf["codebook"], buf["m"], buf["off"],
                                                          buf["workspace"], stream)
-                return kvq.kvq_solve_lambda(plan, buf["D"], buf["H"], buf["stats"], Bw, kvq.KVQ_BISECT, 40,
+                return kvq.kvq_solve_lambda(plan, buf["D"], buf["H"], buf["stats"], Bw, mode, 40,
                                             0.0, 0.0, buf["choice"], buf["codebook"], buf["m"], buf["off"],
                                             buf["workspace"], stream)
             solve()
@@ -237,8 +239,8 @@ def extensions(torch, kvq, W, w, plan, dev, buf, stream):
                 torch.cuda.synchronize()
                 ts.append(1e3 * (time.perf_counter() - t0))
             res[name] = {"solve_ms_incl_sync": float(np.median(ts)), "lambda": lam, "rate_bits_per_entry": rate}
-        out["weighted_distortion"] = {"B_bits_per_entry": Bw, "weights": "log-normal(0, 0.5) per (tensor, layer, head)",
-                                      **res}
+        out["binding_budget_solves"] = {"B_bits_per_entry": Bw,
+                                        "weights": "log-normal(0, 0.5) per (tensor, layer, head)", **res}
     return out
 
 
