@@ -212,8 +212,8 @@ __device__ __forceinline__ double point_entropy(double m, const double* lg_c, co
 // of the lane K back when it belongs to the same run (off >= K).
 template <int CTRL, int K>
 __device__ __forceinline__ void seg_scan_step(uint32_t off, double& a, double& b) {
-    const double ta = dpp_f64<CTRL>(0.0, a);
-    const double tb = dpp_f64<CTRL>(0.0, b);
+    const double ta = dpp_zero_f64<CTRL>(a);  // lanes without a source read 0
+    const double tb = dpp_zero_f64<CTRL>(b);
     if (off >= (uint32_t)K) {
         a += ta;
         b += tb;
@@ -221,7 +221,7 @@ __device__ __forceinline__ void seg_scan_step(uint32_t off, double& a, double& b
 }
 template <int CTRL, int K>
 __device__ __forceinline__ void seg_scan_step(uint32_t off, uint32_t& z) {
-    const uint32_t tz = dpp_u32<CTRL>(0u, z);
+    const uint32_t tz = dpp_zero_u32<CTRL>(z);
     if (off >= (uint32_t)K) z += tz;
 }
 
@@ -624,7 +624,7 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         dterm = A * A * ma + Bq * Bq * mb;
         bq = pb.v;
     }
-    const double ma_next = dpp_f64<kDppRowShl1>(0.0, ma);
+    const double ma_next = dpp_zero_f64<kDppRowShl1>(ma);  // 0 in a row's last lane
     const double mr = last ? mb : mb + ma_next;
 
     // ---- per candidate: D = sum of its intervals' terms - sum x^2 and
