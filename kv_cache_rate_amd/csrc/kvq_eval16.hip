@@ -310,6 +310,16 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     }
     if (tid == 0) sh.nslots = 0u;
     const uint32_t d = tid < kCL ? tb.desc[tid] : kNoLane;  // this lane's candidate interval
+    // and its run (read here, with the other table words, so the candidate
+    // phase does not wait on a memory load)
+    const uint32_t sg = tb.lseg[tid];
+    // this lane's threshold parameters: an order statistic's rank, or a
+    // uniform threshold's numerator | denominator << 8
+    uint32_t tpar = 0u;
+    if (tid < kNQ)
+        tpar = (uint32_t)tb.rt.rank[tid];
+    else if (tid >= 128 && tid < 128 + kNU)
+        tpar = (uint32_t)tb.unum[tid - 128] | ((uint32_t)tb.uden[tid - 128] << 8);
     __syncthreads();
 
     // ---- sweep 1 (two entries per 32-bit word): canonical -0, keys,
@@ -410,7 +420,7 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     // ---- order statistics on threads 0..72, uniform thresholds on threads
     //      128..198: find the bin, read its prefix, claim a slot
     if (tid < kNQ) {
-        const uint32_t rank = (uint32_t)tb.rt.rank[tid];
+        const uint32_t rank = tpar;
         // last bin with prefix count <= rank: 4-way search, the three
         // probes of a step are independent reads
         uint32_t lo = 0;
@@ -433,7 +443,7 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
 #pragma clang fp contract(off)
             const double dmn = (double)mn;
             const double span = (double)mx - dmn;
-            t = (float)(dmn + (span * (double)tb.unum[u]) / (double)tb.uden[u]);
+            t = (float)(dmn + (span * (double)(tpar & 0xffu)) / (double)(tpar >> 8));
         }
         const uint32_t key = key_ceil(t);
         const uint32_t bin = key >> 6;
@@ -634,7 +644,6 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     //      lanes, added when the source lane is of the same candidate); the
     //      candidate's last lane writes them.  The first interval also
     //      carries the entropy term of its left point.
-    const uint32_t sg = tb.lseg[tid];
     const bool live = sg != kNoLane;
     const uint32_t off = (sg >> 5) & 15u;
     double dsum = live ? dterm : 0.0;
