@@ -187,8 +187,17 @@ quantize4096_kernel(const void* __restrict__ x0, const void* __restrict__ x1, in
     __shared__ float inv[kMaxS];  // 2^24 / (q[i+1] - q[i]); 0 at the last point
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x;
-    const int m = min(max((int)m_in[r], 1), s);
-    if (tid <= kMaxS) q[tid] = tid < m ? codebook[r * s + tid] : __builtin_huge_valf();
+    // issue the block's independent loads before anything waits on one: the
+    // codebook row (whole, s points), the size m and this lane's first chunk
+    const float cbv = tid < s ? codebook[r * s + tid] : __builtin_huge_valf();
+    const int mraw = m_in[r];
+    const uint64_t ob = off[r];
+    const void* src = r < nb0 ? x0 : x1;
+    const int64_t e_base = (r < nb0 ? r : r - nb0) * 4096;
+    float x0v[8];
+    load8(src, dtype, e_base + 8 * tid, x0v);
+    const int m = min(max(mraw, 1), s);
+    if (tid <= kMaxS) q[tid] = tid < m ? cbv : __builtin_huge_valf();
     __syncthreads();
     // slot m-1 (the maximum) faces +inf: its inverse width is 0, so an entry
     // equal to the maximum keeps code m-1 and needs no clamp below
@@ -196,15 +205,18 @@ quantize4096_kernel(const void* __restrict__ x0, const void* __restrict__ x1, in
     __syncthreads();
     const int w = code_width(m);
     if (w == 0) return;
-    const void* src = r < nb0 ? x0 : x1;
-    const int64_t e_base = (r < nb0 ? r : r - nb0) * 4096;
-    uint8_t* out = reinterpret_cast<uint8_t*>(codes + off[r]);
+    uint8_t* out = reinterpret_cast<uint8_t*>(codes + ob);
     const uint32_t rlo = (uint32_t)r, rhi = (uint32_t)((uint64_t)r >> 32);
 #pragma unroll
     for (int half = 0; half < 512 / kThreads; ++half) {
         const int ch = tid + half * kThreads;
         float x[8];
-        load8(src, dtype, e_base + 8 * ch, x);
+        if (half == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = x0v[e];
+        } else {
+            load8(src, dtype, e_base + 8 * ch, x);
+        }
         uint32_t wd[8];
         {
             uint32_t a0 = (uint32_t)(2 * ch), a1 = rlo, a2 = rhi, a3 = 0u;
