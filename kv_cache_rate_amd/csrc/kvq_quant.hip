@@ -258,11 +258,15 @@ dequantize4096_kernel(int s, const uint32_t* __restrict__ codes, const float* __
     __shared__ float q[kMaxS];
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x;
-    const int m = min(max((int)m_in[r], 1), s);
-    if (tid < kMaxS) q[tid] = tid < m ? codebook[r * s + tid] : 0.0f;
+    // m, the word offset and the codebook row are requested together
+    const float cbv = tid < s ? codebook[r * s + tid] : 0.0f;
+    const int mraw = m_in[r];
+    const uint64_t ob = off[r];
+    const int m = min(max(mraw, 1), s);
+    if (tid < kMaxS) q[tid] = tid < m ? cbv : 0.0f;
     __syncthreads();
     const int w = code_width(m);
-    const uint32_t* cw = codes + off[r];
+    const uint32_t* cw = codes + ob;
     const uint32_t mask = (1u << w) - 1u;
     float4* o = reinterpret_cast<float4*>(xhat + r * 4096);
 #pragma unroll
