@@ -139,6 +139,12 @@ __device__ __forceinline__ uint32_t pair_keys(uint32_t hw) {
     return pair_keys(hw, hv);
 }
 
+// A round's slot tag as a compile-time value.
+template <uint32_t V>
+struct RoundTag {
+    static constexpr uint32_t value = V;
+};
+
 // Fixed instruction forms for sweep 2's per-entry address arithmetic (the
 // compiler rewrites the builtins into longer shift/mask sequences).
 // (x >> off) & ((1 << w) - 1), off and w immediate:
@@ -491,11 +497,15 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         sl[2 * p] = sh.slot[(k2s[p] & 0xffffu) >> 6];
         sl[2 * p + 1] = sh.slot[k2s[p] >> 22];
     }
+    // the per-entry loop is compiled once per round tag, so the first
+    // round (tag 0, the only one for most blocks) needs no XOR
+    auto sweep2 = [&](auto tagc) {
+    constexpr uint32_t kTag = decltype(tagc)::value;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        // served this round iff the entry's two high bits equal `tag`; then
+        // served this round iff the entry's two high bits equal the tag; then
         // so is the slot's byte offset (kNoSlot ^ tag has a high bit set)
-        const uint32_t so = sl[i] ^ tag;
+        const uint32_t so = sl[i] ^ kTag;
         if (so < kRound2) {
             // key f = bits [kb, kb + 6) of the word holding both keys; it
             // counts 1 in the 16-bit half f & 1 of word f >> 1 of the slot
@@ -512,6 +522,11 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
             atomicAdd(slotw + cword, one);
         }
     }
+    };
+    if (rnd == 0)
+        sweep2(RoundTag<0u>{});
+    else
+        sweep2(RoundTag<kRound2>{});
     __syncthreads();
     // ---- group totals of this round's slots, (count << 19) + sum of f over
     //      each 8-key group, from the per-key counters: one (slot, group) per
