@@ -267,9 +267,12 @@ attn_merge_kernel(const float* __restrict__ part, int splits, float* __restrict_
     const int64_t row = blockIdx.x;  // (o, query head)
     const int d = threadIdx.x;
     const float* pp = part + row * splits * (kHD + 2);
+    // unrolled so that several splits' loads are in flight at once
     float M = -__builtin_huge_valf();
+#pragma unroll 8
     for (int sp = 0; sp < splits; ++sp) M = fmaxf(M, pp[sp * (kHD + 2) + kHD]);
     float L = 0.0f, A = 0.0f;
+#pragma unroll 8
     for (int sp = 0; sp < splits; ++sp) {
         const float m = pp[sp * (kHD + 2) + kHD];
         const float e = m == -__builtin_huge_valf() ? 0.0f : pow2(m - M);
