@@ -487,9 +487,8 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     for (int rnd = 0;; ++rnd) {
     const uint32_t tag = rnd ? kRound2 : 0u;  // slot entries served this round
     const uint32_t ns = rnd ? nslots - (uint32_t)kSlots : min(nslots, (uint32_t)kSlots);
-    for (uint32_t i = tid; i < ns * (kSW / 4); i += kT)
-        reinterpret_cast<uint4*>(sh.u.b.w)[i] = make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
+    // each entry's slot entry (the slot table lies outside the memory
+    // cleared next, so these reads overlap the clearing and its barrier)
     uint32_t sl[kPer];
 #pragma unroll
     for (int p = 0; p < kPer / 2; ++p) {
@@ -497,6 +496,9 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         sl[2 * p] = sh.slot[(k2s[p] & 0xffffu) >> 6];
         sl[2 * p + 1] = sh.slot[k2s[p] >> 22];
     }
+    for (uint32_t i = tid; i < ns * (kSW / 4); i += kT)
+        reinterpret_cast<uint4*>(sh.u.b.w)[i] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
     // the per-entry loop is compiled once per round tag, so the first
     // round (tag 0, the only one for most blocks) needs no XOR
     auto sweep2 = [&](auto tagc) {
