@@ -131,20 +131,33 @@ constexpr int64_t kQSmallLaunch = 16384;  // blocks below which kQTSmall is used
 constexpr int kDQT = 128;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void load8(const void* src, int dtype, int64_t e0, float* x) {
-    if (dtype == KVQ_F16) {
-        const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(src) + e0);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+// An 8-entry chunk as loaded (fp16: 16 bytes in w[0]; fp32: 32 bytes), kept
+// apart from its conversion so that the next chunk's load can be issued
+// before this chunk is used.
+template <int kDt>
+__device__ __forceinline__ void load_raw8(const void* src, int64_t e0, uint4 (&w)[2]) {
+    if (kDt == KVQ_F16) {
+        w[0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(src) + e0);
+    } else {
+        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(src) + e0);
+        w[0] = p[0];
+        w[1] = p[1];
+    }
+}
+
+template <int kDt>
+__device__ __forceinline__ void unpack8(const uint4 (&w)[2], float* x) {
+    if (kDt == KVQ_F16) {
+        const uint32_t h[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            x[2 * k] = __half2float(__ushort_as_half((unsigned short)(w[k] & 0xffffu)));
-            x[2 * k + 1] = __half2float(__ushort_as_half((unsigned short)(w[k] >> 16)));
+            x[2 * k] = __half2float(__ushort_as_half((unsigned short)(h[k] & 0xffffu)));
+            x[2 * k + 1] = __half2float(__ushort_as_half((unsigned short)(h[k] >> 16)));
         }
     } else {
-        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + e0);
-        const float4 a = p[0], b = p[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        const uint32_t f[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = __uint_as_float(f[k]);
     }
 }
 
@@ -177,9 +190,9 @@ __device__ __forceinline__ uint32_t load_bytes(const uint8_t* src, int w) {
     }
 }
 
-template <int kThreads>
+template <int kThreads, int kDt>
 __global__ void __launch_bounds__(kThreads)
-quantize4096_kernel(const void* __restrict__ x0, const void* __restrict__ x1, int64_t nb0, int dtype,
+quantize4096_kernel(const void* __restrict__ x0, const void* __restrict__ x1, int64_t nb0,
                     int s, const float* __restrict__ codebook, const uint8_t* __restrict__ m_in,
                     const uint64_t* __restrict__ off, uint32_t k0, uint32_t k1,
                     uint32_t* __restrict__ codes) {
@@ -194,8 +207,8 @@ quantize4096_kernel(const void* __restrict__ x0, const void* __restrict__ x1, in
     const uint64_t ob = off[r];
     const void* src = r < nb0 ? x0 : x1;
     const int64_t e_base = (r < nb0 ? r : r - nb0) * 4096;
-    float x0v[8];
-    load8(src, dtype, e_base + 8 * tid, x0v);
+    uint4 cur[2] = {}, nxt[2] = {};
+    load_raw8<kDt>(src, e_base + 8 * tid, cur);
     const int m = min(max(mraw, 1), s);
     if (tid <= kMaxS) q[tid] = tid < m ? cbv : __builtin_huge_valf();
     __syncthreads();
@@ -210,13 +223,9 @@ quantize4096_kernel(const void* __restrict__ x0, const void* __restrict__ x1, in
 #pragma unroll
     for (int half = 0; half < 512 / kThreads; ++half) {
         const int ch = tid + half * kThreads;
+        if (half + 1 < 512 / kThreads) load_raw8<kDt>(src, e_base + 8 * (ch + kThreads), nxt);
         float x[8];
-        if (half == 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = x0v[e];
-        } else {
-            load8(src, dtype, e_base + 8 * ch, x);
-        }
+        unpack8<kDt>(cur, x);
         uint32_t wd[8];
         {
             uint32_t a0 = (uint32_t)(2 * ch), a1 = rlo, a2 = rhi, a3 = 0u;
@@ -248,6 +257,8 @@ quantize4096_kernel(const void* __restrict__ x0, const void* __restrict__ x1, in
             bits |= code << (w * e);
         }
         store_bytes(out + w * ch, bits, w);
+        cur[0] = nxt[0];
+        cur[1] = nxt[1];
     }
 }
 
@@ -310,14 +321,23 @@ hipError_t launch_quantize(const Geom& g, int64_t R, int s, const float* codeboo
     if (R == 0) return hipSuccess;
     if (fast_layout(g)) {
         const void* x1 = g.data[1] ? g.data[1] : g.data[0];
-        if (R < kQSmallLaunch)
-            hipLaunchKernelGGL(quantize4096_kernel<kQTSmall>, dim3((unsigned)R), dim3(kQTSmall), 0, st,
-                               g.data[0], x1, g.nb0, g.dtype, s, codebook, m, off, (uint32_t)seed,
-                               (uint32_t)(seed >> 32), codes);
-        else
-            hipLaunchKernelGGL(quantize4096_kernel<kQT>, dim3((unsigned)R), dim3(kQT), 0, st, g.data[0],
-                               x1, g.nb0, g.dtype, s, codebook, m, off, (uint32_t)seed,
-                               (uint32_t)(seed >> 32), codes);
+        const bool f16 = g.dtype == KVQ_F16;
+        const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+        if (R < kQSmallLaunch) {
+            if (f16)
+                hipLaunchKernelGGL((quantize4096_kernel<kQTSmall, KVQ_F16>), dim3((unsigned)R), dim3(kQTSmall), 0,
+                                   st, g.data[0], x1, g.nb0, s, codebook, m, off, k0, k1, codes);
+            else
+                hipLaunchKernelGGL((quantize4096_kernel<kQTSmall, KVQ_F32>), dim3((unsigned)R), dim3(kQTSmall), 0,
+                                   st, g.data[0], x1, g.nb0, s, codebook, m, off, k0, k1, codes);
+        } else {
+            if (f16)
+                hipLaunchKernelGGL((quantize4096_kernel<kQT, KVQ_F16>), dim3((unsigned)R), dim3(kQT), 0, st,
+                                   g.data[0], x1, g.nb0, s, codebook, m, off, k0, k1, codes);
+            else
+                hipLaunchKernelGGL((quantize4096_kernel<kQT, KVQ_F32>), dim3((unsigned)R), dim3(kQT), 0, st,
+                                   g.data[0], x1, g.nb0, s, codebook, m, off, k0, k1, codes);
+        }
     } else {
         hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)R), dim3(kQuantThreads), 0, st, g, s,
                            codebook, m, off, (uint32_t)seed, (uint32_t)(seed >> 32), codes);
