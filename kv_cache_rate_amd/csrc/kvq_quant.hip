@@ -280,16 +280,29 @@ dequantize4096_kernel(int s, const uint32_t* __restrict__ codes, const float* __
     const uint32_t* cw = codes + ob;
     const uint32_t mask = (1u << w) - 1u;
     float4* o = reinterpret_cast<float4*>(xhat + r * 4096);
+    // every code word first: a load waited on between two stores would also
+    // wait for the earlier store (one counter serves both).  The second word
+    // is needed only when a group straddles a word boundary, never in the
+    // block's last word (128 w words), so its index is clamped and both loads
+    // are unconditional.
+    constexpr int kIt = 1024 / kDQT;
+    uint32_t wa[kIt] = {}, wb[kIt] = {};
+    if (w) {
+        const uint32_t last = 128u * (uint32_t)w - 1u;
 #pragma unroll
-    for (int k = 0; k < 1024 / kDQT; ++k) {
+        for (int k = 0; k < kIt; ++k) {
+            const uint32_t q0 = (4u * (uint32_t)w * (uint32_t)(tid + k * kDQT)) >> 5;
+            wa[k] = cw[q0];
+            wb[k] = cw[min(q0 + 1u, last)];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kIt; ++k) {
         const int j = tid + k * kDQT;           // float4 j = entries 4j .. 4j + 3
         uint32_t bits = 0;
         if (w) {
-            const uint32_t b0 = 4u * (uint32_t)w * (uint32_t)j;
-            const uint32_t q0 = b0 >> 5, sh = b0 & 31u;
-            uint64_t win = cw[q0];
-            if (sh + 4u * (uint32_t)w > 32u) win |= (uint64_t)cw[q0 + 1] << 32;
-            bits = (uint32_t)(win >> sh);
+            const uint32_t sh = (4u * (uint32_t)w * (uint32_t)j) & 31u;
+            bits = (uint32_t)((((uint64_t)wb[k] << 32) | wa[k]) >> sh);
         }
         float v[4];
 #pragma unroll
