@@ -207,8 +207,20 @@ quantize4096_kernel(const void* __restrict__ x0, const void* __restrict__ x1, in
     const uint64_t ob = off[r];
     const void* src = r < nb0 ? x0 : x1;
     const int64_t e_base = (r < nb0 ? r : r - nb0) * 4096;
+    // fp16: every chunk of the lane is loaded here, before any code store
+    // (one counter tracks loads and stores, so a load waited on after a
+    // store would wait for that store too); fp32 chunks are twice the
+    // registers and are loaded one step ahead instead
+    constexpr int kNH = 512 / kThreads;
+    constexpr bool kAllAhead = kDt == KVQ_F16;
+    uint4 all[kAllAhead ? kNH : 1][2] = {};
     uint4 cur[2] = {}, nxt[2] = {};
-    load_raw8<kDt>(src, e_base + 8 * tid, cur);
+    if (kAllAhead) {
+#pragma unroll
+        for (int h = 0; h < kNH; ++h) load_raw8<kDt>(src, e_base + 8 * (tid + h * kThreads), all[h]);
+    } else {
+        load_raw8<kDt>(src, e_base + 8 * tid, cur);
+    }
     const int m = min(max(mraw, 1), s);
     if (tid <= kMaxS) q[tid] = tid < m ? cbv : __builtin_huge_valf();
     __syncthreads();
@@ -221,11 +233,15 @@ quantize4096_kernel(const void* __restrict__ x0, const void* __restrict__ x1, in
     uint8_t* out = reinterpret_cast<uint8_t*>(codes + ob);
     const uint32_t rlo = (uint32_t)r, rhi = (uint32_t)((uint64_t)r >> 32);
 #pragma unroll
-    for (int half = 0; half < 512 / kThreads; ++half) {
+    for (int half = 0; half < kNH; ++half) {
         const int ch = tid + half * kThreads;
-        if (half + 1 < 512 / kThreads) load_raw8<kDt>(src, e_base + 8 * (ch + kThreads), nxt);
         float x[8];
-        unpack8<kDt>(cur, x);
+        if (kAllAhead) {
+            unpack8<kDt>(all[half], x);
+        } else {
+            if (half + 1 < kNH) load_raw8<kDt>(src, e_base + 8 * (ch + kThreads), nxt);
+            unpack8<kDt>(cur, x);
+        }
         uint32_t wd[8];
         {
             uint32_t a0 = (uint32_t)(2 * ch), a1 = rlo, a2 = rhi, a3 = 0u;
