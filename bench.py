@@ -55,9 +55,13 @@ def kernel_sources_sha(files=None):
 
 def algorithmic_bytes(plan, words_total, in_bytes_per_entry):
     """Bytes each call must move at minimum (inputs read once, outputs
-    written once)."""
+    written once).  The score table is counted at 4 bytes per D and per H
+    entry (8 bytes per candidate and block), the size the method needs; the
+    library stores them in fp64 for exact agreement with the oracle, and
+    that choice's extra bytes are reported separately
+    (:func:`table_fp64_excess_bytes`), never as algorithmic traffic."""
     R, n = plan.n_blocks, plan.n_entries
-    table = plan.D_bytes + plan.H_bytes
+    table = 8 * R * plan.n_cand
     meta = plan.codebook_bytes + plan.m_bytes + plan.offsets_bytes
     return {
         "eval": n * in_bytes_per_entry + table + plan.stats_bytes,
@@ -65,6 +69,11 @@ def algorithmic_bytes(plan, words_total, in_bytes_per_entry):
         "quantize_pack": n * in_bytes_per_entry + meta + 4 * words_total,
         "dequantize": 4 * words_total + meta + 4 * n,
     }
+
+
+def table_fp64_excess_bytes(plan):
+    """Bytes the fp64 D and H tables write beyond 4-byte entries."""
+    return plan.D_bytes + plan.H_bytes - 8 * plan.n_blocks * plan.n_cand
 
 
 def load_profile(kernel, sha):
@@ -305,11 +314,55 @@ def exact_search(torch, kvq, W, reps=5):
     return out
 
 
-def cpu_baseline(w, tensors, target_s=10.0):
-    """The oracle, as it stands, on the first blocks of the workload: eval,
-    bisection, quantize+pack and decode, on all host cores."""
-    from oracle import blocks as oblocks
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_stages(w, b, procs):
+    """The oracle, as it stands, on blocks ``b`` ([R, n] fp64) of workload
+    ``w``, stage by stage: scoring (``procs`` worker processes), the
+    multiplier, quantize + pack and decode (one core each).  Returns the
+    per-stage wall times in seconds."""
     from oracle import codes as ocodes
+    from oracle import ecasq, pipeline
+    t = {}
+    if w.search != "grids":
+        t0 = time.perf_counter()
+        out = pipeline.run(b, search=w.search, s=w.s, alphabet_m=w.alphabet_m, B=w.B, mode="bisect",
+                           iters=w.iters, seed=w.seed, processes=procs)
+        t["all_stages"] = time.perf_counter() - t0
+        return t
+    R, n = b.shape
+    t0 = time.perf_counter()
+    D, H, S, books = pipeline.eval_grids(b, w.s, procs)
+    t1 = time.perf_counter()
+    if w.mode == "bisect":
+        lam, choice, rate, Btot, probes = ecasq.solve_bisect(D, H, float(n), w.B, w.iters)
+    else:
+        choice, rbar, lam = ecasq.subgrad_step(D, H, float(n), w.B, 0.5, w.eta)
+    t2 = time.perf_counter()
+    chosen = [books[r][choice[r]] for r in range(R)]
+    cs = [ocodes.quantize_block(b[r], chosen[r], w.seed, r)[0] for r in range(R)]
+    ocodes.pack(cs, [ocodes.code_width(Q.size) for Q in chosen])
+    t3 = time.perf_counter()
+    for r in range(R):
+        ocodes.dequantize_block(cs[r], chosen[r])
+    t4 = time.perf_counter()
+    t.update(eval=t1 - t0, solve=t2 - t1, quantize_pack=t3 - t2, dequantize=t4 - t3)
+    return t
+
+
+def cpu_baseline(w, tensors, target_s=10.0):
+    """The oracle, as it stands, on the first blocks of the workload: eval
+    (all host cores), bisection, quantize+pack and decode (one core), with
+    the time of each stage."""
+    from oracle import blocks as oblocks
     from oracle import pipeline
     procs = pipeline.default_processes()
     per_tensor = tensors[0].shape[1] * (tensors[0].shape[2] // w.tokens_per_block) * \
@@ -321,23 +374,81 @@ def cpu_baseline(w, tensors, target_s=10.0):
         b = oblocks.partition(sub, w.tokens_per_block, w.dims_per_block)
         return b[:nb]
 
-    def run(b):
-        t0 = time.perf_counter()
-        out = pipeline.run(b, search=w.search, s=w.s, alphabet_m=w.alphabet_m, B=w.B,
-                           mode="bisect", iters=w.iters, seed=w.seed, processes=procs)
-        for r in range(b.shape[0]):
-            ocodes.dequantize_block(out["codes"][r], out["chosen"][r])
-        return time.perf_counter() - t0
-
     pilot_n = min(layer_blocks, 16 * procs)
-    t_pilot = run(sample(pilot_n))
+    t_pilot = sum(oracle_stages(w, sample(pilot_n), procs).values())
     nb = int(min(layer_blocks, max(pilot_n, pilot_n * target_s / max(t_pilot, 1e-3))))
     b = sample(nb)
-    t = run(b)
+    stages = oracle_stages(w, b, procs)
+    t = sum(stages.values())
     in_bytes = b.size * (2 if w.dtype == "f16" else 4)
     return {"value": in_bytes / t / 1e9, "unit": "GB/s", "cores": procs, "kind": "oracle",
-            "sample": f"first {nb} blocks ({b.size} entries) of layer 0 of K: eval, bisection "
-                      f"(B={w.B}), quantize+pack, decode; {t:.2f} s wall"}
+            "sample": f"first {nb} blocks ({b.size} entries) of layer 0 of K: eval on {procs} "
+                      f"processes, then bisection (B={w.B}), quantize+pack and decode on one core; "
+                      f"{t:.2f} s wall",
+            "stage_s": stages, "stage_cores": {"eval": procs, "solve": 1, "quantize_pack": 1, "dequantize": 1},
+            "elements_per_s": b.size / t, "cpu_model": cpu_model(), "numpy": np.__version__}
+
+
+def per_workload(torch, kvq, W, reps=20):
+    """Every other configuration: eval + quantize_pack (HIP events, median of
+    ``reps`` after 3 warm-up calls) as KV GB/s and elements/s, the solve,
+    and the oracle on one core over a bounded sample of the same blocks."""
+    from oracle import blocks as oblocks
+    out = {}
+    for w in (W.TINY_K_FP32, W.PREFILL_KV_FP16, W.DECODE_ADMIT_FP16, W.FEATURE_GROUP_EXACT_FP32):
+        host = W.generate(w)
+        dev = [torch.from_numpy(np.ascontiguousarray(h)).cuda() for h in host]
+        search = {"grids": kvq.KVQ_GRIDS, "exact_dp": kvq.KVQ_EXACT_DP}[w.search]
+        plan = kvq.kvq_plan_blocks(dev, w.tokens_per_block, w.dims_per_block, w.s, search,
+                                   w.alphabet_m if search else 0)
+        buf = kvq.allocate(plan)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        tq, ts = [], []
+        mode = kvq.KVQ_BISECT if w.mode == "bisect" else kvq.KVQ_SUBGRAD
+        lam0 = 0.0 if mode == kvq.KVQ_BISECT else 0.5
+        for i in range(reps + 3):
+            ev[0].record()
+            kvq.kvq_eval_candidates(plan, dev, buf["D"], buf["H"], buf["stats"], buf["workspace"])
+            ev[1].record()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            kvq.kvq_solve_lambda(plan, buf["D"], buf["H"], buf["stats"], w.B, mode, w.iters, w.eta, lam0,
+                                 buf["choice"], buf["codebook"], buf["m"], buf["off"], buf["workspace"])
+            t1 = time.perf_counter()
+            ev[1].record()
+            kvq.kvq_quantize_pack(plan, dev, buf["codebook"], buf["m"], buf["off"], w.seed, buf["codes"])
+            ev[2].record()
+            torch.cuda.synchronize()
+            if i >= 3:
+                tq.append(ev[1].elapsed_time(ev[2]))
+                ts.append(1e3 * (t1 - t0))
+        # eval alone, timed separately (the solve's host wait sits between)
+        te = []
+        for i in range(reps + 3):
+            ev[0].record()
+            kvq.kvq_eval_candidates(plan, dev, buf["D"], buf["H"], buf["stats"], buf["workspace"])
+            ev[1].record()
+            torch.cuda.synchronize()
+            if i >= 3:
+                te.append(ev[0].elapsed_time(ev[1]))
+        ms = float(np.median(te)) + float(np.median(tq))
+        words = int(buf["off"][-1].item())
+        alg = algorithmic_bytes(plan, words, 2 if w.dtype == "f16" else 4)
+        b = oblocks.partition(host[:1], w.tokens_per_block, w.dims_per_block)
+        nb = min(b.shape[0], 64 if w.search == "grids" else 16)
+        stages = oracle_stages(w, b[:nb], 1)
+        tc = sum(stages.values())
+        out[w.name] = {"blocks": plan.n_blocks, "entries": plan.n_entries,
+                       "eval_ms": float(np.median(te)), "quantize_pack_ms": float(np.median(tq)),
+                       "solve_ms_incl_sync": float(np.median(ts)),
+                       "kv_GBps": w.input_bytes / (ms * 1e-3) / 1e9,
+                       "elements_per_s": plan.n_entries / (ms * 1e-3),
+                       "frac_of_hbm": (alg["eval"] + alg["quantize_pack"]) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                       "oracle_1core": {"blocks": nb, "stage_s": stages,
+                                        "elements_per_s": nb * plan.d_block / tc,
+                                        "kv_GBps": nb * plan.d_block * (2 if w.dtype == "f16" else 4) / tc / 1e9}}
+        del buf, dev
+    return out
 
 
 def main():
@@ -419,7 +530,8 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / max(1, a.steps)
-    per = {k: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(a.steps)]))
+    # per-call times: median over the timed steps
+    per = {k: float(np.median([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(a.steps)]))
            for j, k in enumerate(names)}
     words_total = int(buf["off"][-1].item())
     alg = algorithmic_bytes(plan, words_total, 2 if w.dtype == "f16" else 4)
@@ -439,6 +551,8 @@ def main():
         extras["extensions"] = extensions(torch, kvq, W, w, plan, dev, buf, stream)
         extras["extensions"]["decode_stream"] = decode_stream(torch, kvq, W)
         extras["extensions"]["exact_search"] = exact_search(torch, kvq, W)
+        log("measuring the other workloads")
+        extras["per_workload"] = per_workload(torch, kvq, W)
     rec = {
         "metric": "KV GB/s quantized (fp16 in) and % of HBM roofline at 32-token blocks",
         "value": value, "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
@@ -452,7 +566,9 @@ def main():
                    "step": "plan+eval+solve+quantize_pack+dequantize"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes": alg[dom]},
+                     "algorithmic_bytes": alg[dom],
+                     "table_fp64_excess_bytes": table_fp64_excess_bytes(plan) if dom in ("eval", "solve")
+                     else 0},
         "kernels_ms": per,
         "valu_issue": None,
         "eval_plus_quantize": {"ms": admit_ms,
@@ -480,6 +596,7 @@ def main():
         rec["roofline"]["frac_of_copy"] = achieved / extras["copy_GBps"]
         rec["decode_admission_latency"] = extras["decode_admission_latency"]
         rec["extensions"] = extras["extensions"]
+        rec["per_workload"] = extras["per_workload"]
     if not a.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(w, host)

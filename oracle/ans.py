@@ -128,15 +128,6 @@ def decode_block(data, m, n):
     return out
 
 
-def encode(code_blocks, ms):
-    """Encode every block.  Returns ``(stream uint8, byte offsets int64[R+1])``."""
-    parts = [encode_block(c, m) for c, m in zip(code_blocks, ms)]
-    off = np.zeros(len(parts) + 1, dtype=np.int64)
-    off[1:] = np.cumsum([p.size for p in parts])
-    stream = np.concatenate(parts) if parts else np.zeros(0, dtype=np.uint8)
-    return stream, off
-
-
 def model_bits(codes, m):
     """sum_t log2(M / f_{s_t}): the ideal code length of the block's symbols
     under its model (bits)."""

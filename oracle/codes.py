@@ -32,33 +32,36 @@ def code_width(m):
     return 0 if m <= 1 else (m - 1).bit_length()
 
 
+def _draws(x, Q, seed, r):
+    """Interval index i, interpolation probability p (fp64, from the fp32
+    codepoints) and Philox uniform u of every entry of block r."""
+    x = np.asarray(x, dtype=np.float64)
+    Q = np.asarray(Q, dtype=np.float64)
+    i = interval_index(Q, x)
+    p = (x - Q[i]) / (Q[i + 1] - Q[i])
+    u = block_uniforms(seed, r, x.size)
+    return i, p, u
+
+
 def quantize_block(x, Q, seed, r):
     """Codes of one block.  Returns ``(codes uint32[n], near)`` where
     ``near`` counts draws with |u - p| < 1e-6 (where an fp32 computation of
     p may legitimately decide the other way)."""
-    x = np.asarray(x, dtype=np.float64)
-    Q = np.asarray(Q, dtype=np.float64)
-    n = x.size
-    m = Q.size
-    if m == 1:
+    n = np.asarray(x).size
+    if np.asarray(Q).size == 1:
         return np.zeros(n, dtype=np.uint32), 0
-    i = interval_index(Q, x)
-    p = (x - Q[i]) / (Q[i + 1] - Q[i])
-    u = block_uniforms(seed, r, n)
+    i, p, u = _draws(x, Q, seed, r)
     codes = (i + (u < p)).astype(np.uint32)
     near = int(np.count_nonzero(np.abs(u - p) < NEAR))
     return codes, near
 
 
 def near_mask(x, Q, seed, r):
-    """Boolean mask of the entries whose draw is within 1e-6 of p."""
-    x = np.asarray(x, dtype=np.float64)
-    Q = np.asarray(Q, dtype=np.float64)
-    if Q.size == 1:
-        return np.zeros(x.size, dtype=bool)
-    i = interval_index(Q, x)
-    p = (x - Q[i]) / (Q[i + 1] - Q[i])
-    u = block_uniforms(seed, r, x.size)
+    """Boolean mask of the entries whose draw is within 1e-6 of p (the
+    entries :func:`quantize_block` counts as near)."""
+    if np.asarray(Q).size == 1:
+        return np.zeros(np.asarray(x).size, dtype=bool)
+    _, p, u = _draws(x, Q, seed, r)
     return np.abs(u - p) < NEAR
 
 

@@ -225,10 +225,3 @@ def default_processes():
     except AttributeError:  # pragma: no cover
         return os.cpu_count() or 1
 
-
-def everett_check(D, H, d, lam, choice):
-    """Lagrangian sufficiency: the choice at lam minimises sum D + lam d H
-    block by block; returns the total objective (for brute-force tests)."""
-    obj = D + (lam * d) * H
-    R = D.shape[0]
-    return math.fsum(obj[np.arange(R), choice].tolist())

@@ -248,4 +248,6 @@ def full_compare(g, o, search, seed, B=None, mode="bisect", lam_used_gpu=None, w
         assert np.array_equal(g["off"], o["offsets"]), "offsets differ"
     rep["code_mismatch_near"] = compare_codes(g, o, agree, seed)
     rep["oracle_near"] = o["near"]
+    # every differing code is one of the oracle's near draws
+    assert rep["code_mismatch_near"] <= o["near"], rep
     return rep

@@ -106,11 +106,12 @@ def test_full_size_sampled():
         seg = g["codes"][int(g["off"][r]):int(g["off"][r + 1])]
         cg = ocodes.unpack_block(seg, n, w)
         Q = g["codebook"][r, :int(g["m"][r])].astype(np.float64)
-        co, _ = ocodes.quantize_block(blocks[k], Q, WL.seed, r)
+        co, nnear = ocodes.quantize_block(blocks[k], Q, WL.seed, r)
         diff = cg != co
         if diff.any():
             near = ocodes.near_mask(blocks[k], Q, WL.seed, r)
             assert np.all(near[diff]), f"block {r}: code differs away from |u-p|<1e-6"
+            assert int(diff.sum()) <= nnear
             near_diff += int(diff.sum())
     _say(f"full size: lambda {g['lam']} rate {g['rate_per_entry']:.6f} sampled {len(sample)} "
          f"ties {ties} (max gap {gap:.2e}) near-draw code differences {near_diff}")

@@ -93,3 +93,29 @@ def test_monte_carlo_unbiased_and_mse():
     mse = sq.sum() / (M * x.size)
     # MSE estimate sd ~ sqrt(Var[(xh-x)^2]) / sqrt(M n); generous 6 sigma band
     assert mse == pytest.approx(var, rel=6 / np.sqrt(M * x.size) * 3)
+
+
+def test_near_draws_are_exactly_the_band_around_p():
+    """The exclusion set of code parity (draws with |u - p| < 1e-6; page
+    "Rate-adaptive KV-cache quantizer", Key formulas (3): round up iff u < p).
+    Entries are built at known distances from their Philox draws, so the band
+    edges, the block index of the draws and the rounding rule are all fixed:
+    distances 5e-7 and 9.9e-7 are near, 1.01e-6 and 2e-6 are not, and every
+    entry rounds up exactly when it lies above its draw."""
+    from oracle.philox import block_uniforms
+    seed, r, n = 0x1234ABCD5678, 7, 256
+    Q = np.array([-3.0, -0.5, 0.25, 4.0])
+    u = block_uniforms(seed, r, n)
+    assert np.all((u > 1e-5) & (u < 1 - 1e-5))
+    deltas = np.array([5e-7, -5e-7, 9.9e-7, -9.9e-7, 1.01e-6, -1.01e-6, 2e-6, -2e-6])
+    d = deltas[np.arange(n) % deltas.size]
+    i = np.arange(n) % (Q.size - 1)
+    x = Q[i] + (u + d) * (Q[i + 1] - Q[i])
+    mask = codes.near_mask(x, Q, seed, r)
+    want = np.abs(d) < 1e-6
+    assert np.array_equal(mask, want)
+    c, near = codes.quantize_block(x, Q, seed, r)
+    assert near == int(want.sum()) == n // 2
+    assert np.array_equal(c, (i + (d > 0)).astype(np.uint32))
+    # the draws of another block do not produce this band
+    assert not np.array_equal(codes.near_mask(x, Q, seed, r + 1), want)
