@@ -24,12 +24,13 @@
  *
  * Conventions for every entry point:
  *   - Device pointers are HIP device memory owned by the caller; the library
- *     allocates no device memory.  Its only state is one 8 KB pinned host
- *     buffer per calling thread (hipHostMalloc on first use, kept until the
- *     process ends) through which the synchronising calls read back their
- *     small results (for up to 1024 grid-search blocks the solve's last
- *     kernel writes them into it directly).  Sizes of every buffer come from
- *     kvq_plan (filled by kvq_plan_blocks).
+ *     allocates no device memory.  Its state is one 8 KB pinned host buffer
+ *     per calling thread (hipHostMalloc on first use, kept until the process
+ *     ends) through which the synchronising calls read back their small
+ *     results (for up to 1024 grid-search blocks the solve's last kernel
+ *     writes them into it directly), and the 32 KB static device scratch of
+ *     kvq_admit_noalloc (one per GPU, part of the loaded code object).  Sizes
+ *     of every buffer come from kvq_plan (filled by kvq_plan_blocks).
  *   - Host pointers are marked "(host)".
  *   - Arguments are validated on the host before any launch; a failed check
  *     returns KVQ_EINVAL or KVQ_ENOSPC and launches nothing.  Calls are
@@ -260,6 +261,26 @@ kvq_status kvq_admit(const kvq_plan* p, const kvq_tensor* t, int32_t n_tensors, 
                      double* rate_bits_per_entry_out, int32_t* choice, float* codebook,
                      uint8_t* m, uint64_t* word_off, uint64_t seed, uint32_t* codes,
                      uint64_t codes_capacity_words, void* workspace, hipStream_t s);
+
+/* kvq_admit without a workspace argument and without any allocation, for
+   callers that cannot allocate device or pinned memory (code under HIP graph
+   capture, tight serving loops, harnesses that forbid hipMalloc).  The
+   solve's workspace is a static device array of the library (32 KB per GPU,
+   held by each GPU the library runs on until the process ends), so plans of
+   at most 3,668,992 blocks are accepted (KVQ_ENOSPC beyond, with nothing
+   launched).  Results are read back with a plain copy into the caller's host
+   variables instead of the pinned staging buffer.  Arguments, outputs and
+   errors are those of kvq_admit.  Every call on one GPU shares that GPU's
+   scratch: calls that overlap in time on the same GPU (different streams or
+   threads) race and give unspecified results; calls in sequence are
+   independent (the scratch's stale contents are reset by the call's first
+   kernels).  mode: KVQ_BISECT or KVQ_SUBGRAD. */
+kvq_status kvq_admit_noalloc(const kvq_plan* p, const kvq_tensor* t, int32_t n_tensors, double* D,
+                             double* H, float* stats, double B_bits_per_entry, int32_t mode,
+                             int32_t iters, double eta, double* lambda_io,
+                             double* rate_bits_per_entry_out, int32_t* choice, float* codebook,
+                             uint8_t* m, uint64_t* word_off, uint64_t seed, uint32_t* codes,
+                             uint64_t codes_capacity_words, hipStream_t s);
 
 /* Decode before attention (Implementation notes): xhat[r][t] = Q_r[code_t]
    in fp32, blocks in plan order, entries row-major in the block.

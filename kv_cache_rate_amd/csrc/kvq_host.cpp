@@ -7,9 +7,16 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "kvq_internal.h"
+
+// Device scratch of kvq_admit_noalloc: the solve's workspace (header and
+// scan tile sums) for callers that cannot allocate.  Each device holds its
+// own copy for the life of the process; host code reaches it only through
+// the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kvq::kNoAllocScratchBytes];
 
 namespace kvq {
 
@@ -29,8 +36,8 @@ void* staging_buffer(void** dev) {
     return buf;
 }
 
-hipError_t read_back(void* dst, const void* src, size_t bytes, hipStream_t st) {
-    void* buf = staging_buffer(nullptr);
+hipError_t read_back(void* dst, const void* src, size_t bytes, hipStream_t st, bool staging) {
+    void* buf = staging ? staging_buffer(nullptr) : nullptr;
     if (!buf || bytes > kStagingBytes) {
         const hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, st);
         return e == hipSuccess ? hipStreamSynchronize(st) : e;
@@ -296,21 +303,23 @@ kvq_status solve_check(const kvq_plan* p, const double* D, const double* H, cons
 struct SolveState {
     kvq::SolveOut* out;  // pinned host buffer written by the last kernel, if `direct`
     bool direct;
+    bool staging;        // read-backs may use the pinned staging buffer
 };
 
 kvq_status solve_enqueue(const kvq_plan* p, const double* D, const double* H, const double* weight,
                          const float* stats, double B, int32_t mode, int32_t iters, double lam_in,
                          int32_t* choice, float* codebook, uint8_t* m, uint64_t* word_off, void* workspace,
-                         hipStream_t s, SolveState& ss) {
+                         hipStream_t s, SolveState& ss, bool staging = true) {
     kvq::RankTable rt;
     rank_table(*p, rt);
     void* dev_out = nullptr;
-    ss.out = static_cast<kvq::SolveOut*>(kvq::staging_buffer(&dev_out));
+    ss.out = staging ? static_cast<kvq::SolveOut*>(kvq::staging_buffer(&dev_out)) : nullptr;
     ss.direct = false;
+    ss.staging = staging;
     const hipError_t e = kvq::launch_solve(*p, rt, D, H, weight, stats, B, mode, iters, lam_in, choice,
                                            codebook, m, word_off, workspace,
                                            ss.out ? static_cast<kvq::SolveOut*>(dev_out) : nullptr,
-                                           &ss.direct, s);
+                                           &ss.direct, s, staging);
     if (e != hipSuccess) return hip_fail(e, "solve launch");
     return ok();
 }
@@ -328,7 +337,7 @@ kvq_status solve_result(const kvq_plan* p, double B, int32_t mode, double eta, d
         if (e == hipSuccess) memcpy(&hdr, ss.out, sizeof hdr);
     } else {
         kvq::WsHeader full;
-        e = kvq::read_back(&full, workspace, sizeof full, s);
+        e = kvq::read_back(&full, workspace, sizeof full, s, ss.staging);
         hdr.status = full.status;
         hdr.err = full.err;
         hdr.pool_overflow = full.pool_overflow;
@@ -351,6 +360,29 @@ kvq_status solve_result(const kvq_plan* p, double B, int32_t mode, double eta, d
         *lambda_io = hdr.lam_final;
     }
     return ok();
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (each device has its own copy at its own address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+kvq_status noalloc_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_EINVAL, "device %d outside 0..%d", dev, kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(KVQ_EHIP, "hipGetSymbolAddress(scratch) returned a null address");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return KVQ_OK;
 }
 
 kvq_status quantize_check(const kvq_plan* p, const float* codebook, const uint8_t* m, const uint64_t* word_off,
@@ -437,6 +469,45 @@ kvq_status kvq_admit(const kvq_plan* p, const kvq_tensor* t, int32_t nt, double*
     const hipError_t e = kvq::launch_quantize(g, p->n_blocks, p->s, codebook, m, word_off, seed, codes, s);
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
     return solve_result(p, B, mode, eta, lam_in, workspace, s, ss, lambda_io, rate_out);
+}
+
+kvq_status kvq_admit_noalloc(const kvq_plan* p, const kvq_tensor* t, int32_t nt, double* D, double* H,
+                             float* stats, double B, int32_t mode, int32_t iters, double eta, double* lambda_io,
+                             double* rate_out, int32_t* choice, float* codebook, uint8_t* m, uint64_t* word_off,
+                             uint64_t seed, uint32_t* codes, uint64_t cap, hipStream_t s) {
+    kvq::Geom g;
+    kvq_status st = make_geom(p, t, nt, g);
+    if (st) return st;
+    if (!D || !H || !stats) return fail(KVQ_EINVAL, "null output");
+    if (mode != KVQ_BISECT && mode != KVQ_SUBGRAD)
+        return fail(KVQ_EINVAL, "kvq_admit_noalloc takes KVQ_BISECT or KVQ_SUBGRAD");
+    const size_t need = kvq::ws_pool_offset(p->n_blocks);
+    if (need > kvq::kNoAllocScratchBytes)
+        return fail(KVQ_ENOSPC, "%lld blocks need %zu bytes of solve scratch; the static scratch holds %zu "
+                    "(at most 3668992 blocks)", (long long)p->n_blocks, need, kvq::kNoAllocScratchBytes);
+    // every argument is checked before the scratch is touched
+    int dummy = 0;
+    st = solve_check(p, D, H, nullptr, stats, B, mode, iters, eta, lambda_io, rate_out, choice, codebook, m,
+                     word_off, &dummy);
+    if (st) return st;
+    st = quantize_check(p, codebook, m, word_off, codes, cap);
+    if (st) return st;
+    void* ws = nullptr;
+    st = noalloc_scratch(&ws);
+    if (st) return st;
+    const double lam_in = *lambda_io;
+    // the scratch keeps the previous call's contents: eval's reset kernel
+    // clears the status word and the solve's first kernel sets up the
+    // header; the scan tile sums are written before they are read
+    st = eval_enqueue(p, t, nt, g, D, H, stats, ws, s);
+    if (st) return st;
+    SolveState ss;
+    st = solve_enqueue(p, D, H, nullptr, stats, B, mode, iters, lam_in, choice, codebook, m, word_off, ws, s, ss,
+                       /*staging=*/false);
+    if (st) return st;
+    const hipError_t e = kvq::launch_quantize(g, p->n_blocks, p->s, codebook, m, word_off, seed, codes, s);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    return solve_result(p, B, mode, eta, lam_in, ws, s, ss, lambda_io, rate_out);
 }
 
 kvq_status kvq_dequantize(const kvq_plan* p, const uint32_t* codes, const float* codebook, const uint8_t* m,

@@ -58,6 +58,9 @@ __host__ __device__ inline size_t ws_pool_offset(int64_t R) {
     return (kWsHeaderBytes + (size_t)tiles * sizeof(uint64_t) + 255) & ~(size_t)255;
 }
 static_assert(sizeof(WsHeader) <= kWsHeaderBytes, "workspace header");
+// Static device scratch of kvq_admit_noalloc: header plus scan tile sums
+// (no greedy pool), enough for ws_pool_offset(R) with R up to 3,668,992.
+constexpr size_t kNoAllocScratchBytes = 32768;
 
 // Block geometry as the kernels see it (passed by value).
 struct Geom {
@@ -313,9 +316,10 @@ hipError_t launch_ws_reset(void* ws, hipStream_t st);
 // Read `bytes` (<= kStagingBytes) of device memory into host memory `dst`
 // on stream st and wait for it, through the calling thread's pinned staging
 // buffer (hipHostMalloc'd on first use and kept until the process ends; a
-// plain pageable copy if the allocation fails).
+// plain pageable copy if the allocation fails).  With staging = false the
+// copy goes straight to `dst` and nothing is allocated.
 constexpr size_t kStagingBytes = 8192;
-hipError_t read_back(void* dst, const void* src, size_t bytes, hipStream_t st);
+hipError_t read_back(void* dst, const void* src, size_t bytes, hipStream_t st, bool staging = true);
 // The calling thread's pinned staging buffer (kStagingBytes, allocated on
 // first use), or null if it cannot be allocated; *dev (if dev is not null)
 // receives its device-side address, or null.
@@ -332,11 +336,14 @@ struct SolveOut {
 };
 // `out` (pinned host memory, may be null): if the solve's last kernel wrote
 // the result there, *direct is set and the caller only has to synchronise.
+// staging: whether the mid-solve read-back may use the pinned staging buffer
+// (false: a plain copy, no allocation).
 hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
                         const double* H, const double* wgt, const float* stats, double B,
                         int mode, int iters,
                         double lam_in, int32_t* choice, float* codebook, uint8_t* m,
-                        uint64_t* off, void* ws, SolveOut* out, bool* direct, hipStream_t st);
+                        uint64_t* off, void* ws, SolveOut* out, bool* direct, hipStream_t st,
+                        bool staging = true);
 hipError_t launch_quantize(const Geom& g, int64_t R, int s, const float* codebook,
                            const uint8_t* m, const uint64_t* off, uint64_t seed,
                            uint32_t* codes, hipStream_t st);

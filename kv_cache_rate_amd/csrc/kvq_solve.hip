@@ -1126,7 +1126,7 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
                         const double* wgt, const float* stats, double B, int mode, int iters,
                         double lam_in,
                         int32_t* choice, float* codebook, uint8_t* m, uint64_t* off, void* ws,
-                        SolveOut* out, bool* direct, hipStream_t st) {
+                        SolveOut* out, bool* direct, hipStream_t st, bool staging) {
     WsHeader* h = (WsHeader*)ws;
     *direct = false;
     const int64_t R = p.n_blocks;
@@ -1180,7 +1180,7 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
         // lambda = 0 first; the bracket passes run only when it is infeasible
         rates_pass();
         int32_t done = 0;
-        const hipError_t e = read_back(&done, &h->done, sizeof done, st);
+        const hipError_t e = read_back(&done, &h->done, sizeof done, st, staging);
         if (e != hipSuccess) return e;
         if (!done) {
             // doubling passes up to 2^62, the 2^63 / 2^64 pass if needed,

@@ -32,6 +32,7 @@ KVQ_BISECT_GREEDY = 2
 
 EXPORTED = ("kvq_status_string", "kvq_last_error", "kvq_plan_blocks", "kvq_eval_candidates",
             "kvq_solve_lambda", "kvq_solve_lambda_weighted", "kvq_quantize_pack", "kvq_admit",
+            "kvq_admit_noalloc",
             "kvq_dequantize",
             "kvq_ans_sizes",
             "kvq_ans_encode", "kvq_ans_decode", "kvq_decode_attention_workspace",
@@ -110,6 +111,10 @@ def lib():
         L.kvq_admit.argtypes = [ctypes.POINTER(KvqPlan), ctypes.POINTER(KvqTensor), i32, vp, vp, vp, f64,
                                 i32, i32, f64, ctypes.POINTER(f64), ctypes.POINTER(f64), vp, vp, vp, vp,
                                 u64, vp, u64, vp, vp]
+        L.kvq_admit_noalloc.restype = i32
+        L.kvq_admit_noalloc.argtypes = [ctypes.POINTER(KvqPlan), ctypes.POINTER(KvqTensor), i32, vp, vp, vp,
+                                        f64, i32, i32, f64, ctypes.POINTER(f64), ctypes.POINTER(f64), vp, vp,
+                                        vp, vp, u64, vp, u64, vp]
         L.kvq_dequantize.restype = i32
         L.kvq_dequantize.argtypes = [ctypes.POINTER(KvqPlan), vp, vp, vp, vp, vp, vp]
         L.kvq_ans_sizes.restype = i32
@@ -336,6 +341,23 @@ def kvq_admit(plan, tensors, buf, B, mode=KVQ_BISECT, iters=40, eta=1e-3, lam=0.
                            ctypes.byref(rate), _ptr(buf["choice"]), _ptr(buf["codebook"]), _ptr(buf["m"]),
                            _ptr(buf["off"]), int(seed), _ptr(codes), int(codes.numel()),
                            _ptr(buf["workspace"]), _stream(stream)))
+    return lam_io.value, rate.value
+
+
+def kvq_admit_noalloc(plan, tensors, buf, B, mode=KVQ_BISECT, iters=40, eta=1e-3, lam=0.0, seed=0,
+                      stream=None):
+    """kvq_admit with the library's static device scratch in place of a
+    workspace (no allocation in the call).  Returns ``(lambda,
+    rate_bits_per_entry)``."""
+    arr = _tensor_array(tensors)
+    lam_io = ctypes.c_double(lam)
+    rate = ctypes.c_double(0.0)
+    codes = buf["codes"]
+    _check(lib().kvq_admit_noalloc(ctypes.byref(plan), arr, len(tensors), _ptr(buf["D"]), _ptr(buf["H"]),
+                                   _ptr(buf["stats"]), float(B), mode, iters, float(eta), ctypes.byref(lam_io),
+                                   ctypes.byref(rate), _ptr(buf["choice"]), _ptr(buf["codebook"]),
+                                   _ptr(buf["m"]), _ptr(buf["off"]), int(seed), _ptr(codes),
+                                   int(codes.numel()), _stream(stream)))
     return lam_io.value, rate.value
 
 

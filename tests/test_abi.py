@@ -183,6 +183,40 @@ def test_admit_validates_before_launch(L):
     assert call(cap=p.max_code_words - 1) == kvq.KVQ_ENOSPC
 
 
+def test_admit_noalloc_validates_before_launch(L):
+    """kvq_admit_noalloc refuses on the host, before it touches its static
+    scratch or any GPU: bad arguments as kvq_admit does, and a plan whose
+    solve scratch exceeds the static 32 KB (more than 3,668,992 blocks)."""
+    Lb = kvq.lib()
+    lam = ctypes.c_double(0.0)
+    rate = ctypes.c_double(0.0)
+
+    def call(p, arr, D=8, B=2.0, mode=kvq.KVQ_BISECT, cap=None):
+        return Lb.kvq_admit_noalloc(ctypes.byref(p), arr, 1, D, 8, 8, B, mode, 40, 1e-3, ctypes.byref(lam),
+                                    ctypes.byref(rate), 8, 8, 8, 8, 0, 8,
+                                    p.max_code_words if cap is None else cap, None)
+    t = np.zeros((1, 2, 64, 128), dtype=np.float16)
+    p = kvq.kvq_plan_blocks([t], 32, 128, 16)
+    arr = kvq._tensor_array([t])
+    assert call(p, arr, D=None) == kvq.KVQ_EINVAL
+    assert call(p, arr, mode=kvq.KVQ_BISECT_GREEDY) == kvq.KVQ_EINVAL
+    assert "kvq_admit_noalloc" in kvq.last_error()
+    assert call(p, arr, mode=7) == kvq.KVQ_EINVAL
+    assert call(p, arr, B=-1.0) == kvq.KVQ_EINVAL
+    assert call(p, arr, cap=p.max_code_words - 1) == kvq.KVQ_ENOSPC
+    # the largest plan the scratch holds is accepted past this check (it then
+    # fails only on the missing pointers); one block more is refused
+    base = np.zeros(1, dtype=np.float16)
+    for blocks, want in ((3668993, kvq.KVQ_ENOSPC), (3668992, kvq.KVQ_EINVAL)):
+        big = np.lib.stride_tricks.as_strided(base, shape=(1, 1, 32 * blocks, 128), strides=(2, 2, 256, 2))
+        pb = kvq.kvq_plan_blocks([big], 32, 128, 16)
+        assert pb.n_blocks == blocks
+        got = call(pb, kvq._tensor_array([big]), D=8 if want == kvq.KVQ_ENOSPC else None)
+        assert got == want, (blocks, got, kvq.last_error())
+        if want == kvq.KVQ_ENOSPC:
+            assert "3668992" in kvq.last_error()
+
+
 def test_entropy_coding_sizes_and_validation(L):
     """kvq_ans_sizes: 4 bytes per fixed-width word plus a per-block margin
     (table, final states, and the coder's slack); encode and decode refuse
