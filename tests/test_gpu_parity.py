@@ -91,6 +91,26 @@ def test_feature_group_exact_dp():
     assert np.array_equal(g["choice"][:64].astype(np.int64), o["mask"][:64]) or rep["ties"] > 0
 
 
+def test_tiny_k_fp32_scaled_to_1e33(kernel_path):
+    """The tiny fp32 workload times 1e-33: codepoints ~1e-33 apart, so 2^24
+    over an interval width overflows fp32 and the specialised quantizer must
+    divide instead (codes bit-exact away from |u - p| < 1e-6)."""
+    w = W.TINY_K_FP32
+    x = [(a * np.float32(1e-33)).astype(np.float32) for a in W.generate(w)]
+    assert np.all(np.isfinite(x[0])) and np.abs(x[0]).max() < 1e-31
+    g, o, rep = _check(w, x, B=3.0)
+    assert g["lam"] == 0.0
+
+
+def test_long_context_one_layer_binding_budget(kernel_path):
+    """One layer of the long-context workload at B = 1.5, where the budget
+    binds: the whole bisection, the final choice and the codes against the
+    whole oracle."""
+    w = W.reduced(W.LONG_CONTEXT_KV_FP16, 1)
+    g, o, rep = _check(w, W.generate(w), B=1.5)
+    assert g["lam"] > 0.0
+
+
 def test_long_context_one_layer(kernel_path):
     """The long-context workload reduced to one layer of K and V (16384
     blocks), same per-layer streams as the full tensors."""
