@@ -65,6 +65,44 @@ def build(jobs=None, verbose=False):
     return LIB
 
 
+SANITIZED_LIB = os.path.join(BUILD, "asan", "libkvq_asan.so")
+
+
+def build_host_sanitized():
+    """Build of the library with AddressSanitizer and
+    UndefinedBehaviorSanitizer on the host code only (argument validation,
+    planning, launch sequencing; device code is built as usual, without
+    them).  For the CPU validation tests; returns its path."""
+    out = os.path.dirname(SANITIZED_LIB)
+    os.makedirs(out, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(out, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc(), "-O1", "-g", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+               "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined",
+               "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC,
+               "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        objs.append((obj, cmd))
+
+    def run(job):
+        obj, cmd = job
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"sanitized build failed on {obj}:\n{res.stderr}")
+        return obj
+    with ThreadPoolExecutor(min(len(objs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(run, objs))
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-shared-libsan",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-o", SANITIZED_LIB] + objs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{res.stderr}")
+    return SANITIZED_LIB
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)

@@ -35,7 +35,9 @@
 #include <math.h>
 #include <string.h>
 
+#include "kvq_grid_choice.h"
 #include "kvq_internal.h"
+#include "kvq_quant_block.h"
 
 namespace kvq {
 
@@ -83,6 +85,8 @@ struct PhaseC {                    // candidate intervals, written only by a wav
     double mr[kCL];                //   that holds a zero-width interval:
     double ma[kCL];                // mass at the interval's right point, mass it
     float bv[kCL];                 // sends to its left point, right point
+    double cd[kMaxCand];           // one-launch admission: the block's D and H
+    double chh[kMaxCand];
 };
 
 template <int kSlots>
@@ -91,7 +95,16 @@ struct Shared {
         PhaseA a;
         PhaseB<kSlots> b;
         PhaseC c;
+        QuantLds q;                // one-launch admission: the block's quantization
     } u;
+    alignas(16) float book[kMaxS]; // one-launch admission: the chosen codebook
+    int32_t fz_m;
+    uint64_t fz_ob;                // this block's word count
+    uint64_t fz_rate;              // this block's fixed-point rate
+    uint32_t fz_nf;                // this block holds NaN or Inf
+    uint64_t fz_part[kW];          // per wave: words of the preceding blocks
+    uint64_t fz_rpart[kW];         // per wave: their rates (last block only)
+    uint32_t fz_flags[kW];         // per wave: their status bits (last block only)
     alignas(16) uint32_t slot[kNC];  // bin -> byte offset of its slot, or kNoSlot
     alignas(16) Point P[kNP];
     uint16_t tbin[kNQ];
@@ -285,20 +298,174 @@ struct Eval16Tables {
     double lg_inv[64];              // 1 / (1 + (2i+1)/128)
 };
 
+// Words a block publishes for the blocks after it (relaxed device-scope
+// atomics: each word carries its own flag, so no fence orders one against
+// another).
+constexpr uint64_t kPub = 1ull << 63;      // the word is published
+constexpr uint64_t kPubNF = 1ull << 62;    // count word: the block holds NaN or Inf
+constexpr uint32_t kDescSpins = 1u << 22;  // polls before a missing predecessor is reported
+
+// The rest of the admission step at a known multiplier, run by the same
+// workgroup after scoring its block (one-launch admission).
+struct FusedArgs {
+    double lam;                    // multiplier the blocks are chosen at
+    int shift;                     // fixed-point scale of the rate sums
+    uint32_t k0, k1;               // Philox key (seed lo, seed hi)
+    int32_t* choice;
+    float* codebook;               // [R][16]
+    uint8_t* m;
+    uint64_t* off;                 // [R + 1]
+    uint64_t* desc;                // [R] published word counts, zeroed by fused_reset_kernel
+    uint64_t* rates;               // [R] published fixed-point rates, zeroed likewise
+    uint32_t* codes;
+    SolveOut* out;                 // pinned host memory, or null
+};
+
+// After scoring: choose the block's candidate at fa.lam (lowest index among
+// equal objectives, as the solve does), write its codebook, level count and
+// choice, add its fixed-point rate, publish its word count and sum those of
+// the preceding blocks for its word offset, then quantize and pack it (page
+// "Rate-adaptive KV-cache quantizer", Key formulas (2)-(4); Implementation
+// notes).  The last block's workgroup also writes the rate and the status
+// for the host.
+template <int kSlots>
+__device__ __forceinline__ void fused_tail(Shared<kSlots>& sh, const Eval16Tables& tb, const FusedArgs& fa,
+                                           WsHeader* ws, int64_t r, int64_t R, const __half* x0,
+                                           const __half* x1, int64_t nb0) {
+    const int tid = threadIdx.x;
+    __syncthreads();  // every candidate's D and H are in LDS
+    if (tid == 0) {
+        const PhaseC& pc = sh.u.c;
+        const double lamd = fa.lam * 4096.0;
+        double best = 0.0, bestH = 0.0;
+        int bc = -1;
+        for (int c = 0; c < kMaxCand; ++c) {
+            const double o = objective(pc.cd[c], pc.chh[c], lamd);
+            if (bc < 0 || o < best) {
+                best = o;
+                bestH = pc.chh[c];
+                bc = c;
+            }
+        }
+        const float mn = sh.P[kPQ].v, mx = sh.P[kPQ + kNQ - 1].v;
+        const int m = write_grid_codebook(bc, mn, mx, &sh.P[kPQ].v, (int64_t)(sizeof(Point) / sizeof(float)),
+                                          &tb.rt.col[0][0], kMaxS, sh.book);
+        fa.choice[r] = bc;
+        fa.m[r] = (uint8_t)m;
+        const uint64_t words = (4096u * (uint32_t)code_width(m) + 31u) / 32u;
+        const uint64_t rate = rate_fx(4096.0, bestH, fa.shift);
+        __hip_atomic_store(&fa.desc[r], kPub | (sh.fz_nf ? kPubNF : 0ull) | words, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&fa.rates[r], kPub | rate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (r == 0) fa.off[0] = 0;
+        sh.fz_m = m;
+        sh.fz_ob = words;
+        sh.fz_rate = rate;
+    }
+    __syncthreads();
+    if (tid < kMaxS) fa.codebook[r * kMaxS + tid] = sh.book[tid];
+    const int m = sh.fz_m;
+    const float cbv = tid < m ? sh.book[tid] : __builtin_huge_valf();
+    __syncthreads();  // the quantizer's tables reuse the phase memory
+    // the block's codes (kept in registers until the block's word offset is
+    // known), from its data read again (just read: from the cache) in the
+    // quantizer's 256-thread layout, chunks tid and 256 + tid
+    const __half* src = r < nb0 ? x0 : x1;
+    const int64_t e_base = (r < nb0 ? r : r - nb0) * 4096;
+    uint4 all[2][2] = {};
+    load_raw8<KVQ_F16>(src, e_base + 8 * tid, all[0]);
+    load_raw8<KVQ_F16>(src, e_base + 8 * (tid + kT), all[1]);
+    uint32_t bits[2] = {0u, 0u};
+    const int w = quantize_block4096<kT, KVQ_F16, true>(sh.u.q, r, kMaxS, cbv, m, 0, all, nullptr, 0, fa.k0,
+                                                        fa.k1, nullptr, bits);
+    // word offset: every thread sums the published counts of its share of
+    // the blocks before this one (published soon after each is scored;
+    // blocks with lower indices were dispatched first); the last block also
+    // sums their rates and status bits for the host
+    const bool last = r == R - 1;
+    uint64_t part = 0, rpart = 0;
+    uint32_t flags = 0;
+    for (int64_t j = tid; j < r; j += kT) {
+        uint32_t spins = 0;
+        uint64_t v, q = kPub;
+        for (;;) {
+            v = __hip_atomic_load(&fa.desc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (last) q = __hip_atomic_load(&fa.rates[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((v & kPub) && (q & kPub)) break;
+            if (++spins > kDescSpins) {  // never expected: report, do not hang
+                flags |= kStatusFusedStall;
+                v = kPub;
+                q = kPub;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        part += v & 0xffffffffull;
+        rpart += q & ~kPub;
+        if (v & kPubNF) flags |= kStatusNonFinite;
+    }
+    part = wave_scan_add_u64(part);  // lane 63: the wave's total
+    if (last) {
+        rpart = wave_scan_add_u64(rpart);
+        flags = (__any((flags & kStatusNonFinite) != 0u) ? kStatusNonFinite : 0u) |
+                (__any((flags & kStatusFusedStall) != 0u) ? kStatusFusedStall : 0u);
+    }
+    if ((tid & 63) == 63) {
+        sh.fz_part[tid >> 6] = part;
+        sh.fz_rpart[tid >> 6] = rpart;
+        sh.fz_flags[tid >> 6] = flags;
+    }
+    __syncthreads();
+    const uint64_t ob = (sh.fz_part[0] + sh.fz_part[1]) + (sh.fz_part[2] + sh.fz_part[3]);
+    if (w) {
+        uint8_t* out = reinterpret_cast<uint8_t*>(fa.codes + ob);
+        store_bytes(out + w * tid, bits[0], w);
+        store_bytes(out + w * (tid + kT), bits[1], w);
+    }
+    if (tid == 0) {
+        fa.off[r + 1] = ob + sh.fz_ob;
+        if (last) {
+            const unsigned long long t = (sh.fz_rpart[0] + sh.fz_rpart[1]) + (sh.fz_rpart[2] + sh.fz_rpart[3]) +
+                                         sh.fz_rate;
+            const uint32_t status = (sh.fz_flags[0] | sh.fz_flags[1] | sh.fz_flags[2] | sh.fz_flags[3]) |
+                                    (sh.fz_nf ? kStatusNonFinite : 0u);
+            if (status & kStatusFusedStall) atomicOr(&ws->status, kStatusFusedStall);
+            ws->err = 0;
+            ws->done = 1;
+            ws->pool_overflow = 0;
+            ws->lam_final = fa.lam;
+            ws->rate_final = t;
+            if (fa.out) {
+                SolveOut o;
+                o.status = status;
+                o.err = 0;
+                o.pool_overflow = 0u;
+                o.pad = 0u;
+                o.lam_final = fa.lam;
+                o.rate_final = t;
+                *fa.out = o;
+                __threadfence_system();
+            }
+        }
+    }
+}
+
 // kSlots = kSlotsAll (one round, 5 workgroups per CU) for small launches,
 // where a block's latency matters; kSlotsLarge (6 workgroups per CU) for
-// large ones, where throughput does.
-template <int kSlots>
-__global__ void __launch_bounds__(kT, kSlots == kSlotsAll ? 5 : 6)
+// large ones, where throughput does.  kFused: the one-launch admission (the
+// block is blockIdx.x, so that every block whose word count a workgroup
+// waits for was dispatched before it).
+template <int kSlots, bool kFused = false>
+__global__ void __launch_bounds__(kT, kFused ? 2 : (kSlots == kSlotsAll ? 5 : 6))
 eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int64_t nb0,
               Eval16Tables tb, double* __restrict__ Dout, double* __restrict__ Hout,
-              float* __restrict__ stats, WsHeader* ws) {
+              float* __restrict__ stats, WsHeader* ws, FusedArgs fa) {
     __shared__ Shared<kSlots> sh;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int64_t R = gridDim.x;
-    const int64_t r = xcd_block(blockIdx.x, R);
+    const int64_t r = kFused ? (int64_t)blockIdx.x : xcd_block(blockIdx.x, R);
     const __half* src = r < nb0 ? x0 + r * 4096 : x1 + (r - nb0) * 4096;
 
     // ---- load: thread owns entries [8 tid, 8 tid + 8) and [2048 + 8 tid, ...)
@@ -314,7 +481,10 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         sh.lg_c[tid] = tb.lg_c[tid];
         sh.lg_inv[tid] = tb.lg_inv[tid];
     }
-    if (tid == 0) sh.nslots = 0u;
+    if (tid == 0) {
+        sh.nslots = 0u;
+        if (kFused) sh.fz_nf = 0u;
+    }
     const uint32_t d = tid < kCL ? tb.desc[tid] : kNoLane;  // this lane's candidate interval
     // and its run (read here, with the other table words, so the candidate
     // phase does not wait on a memory load)
@@ -384,7 +554,10 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
                                  128u * c[2] + (pw.z & kLowF), 192u * c[3] + (pw.w & kLowF)};
         const uint32_t ct = (c[0] + c[1]) + (c[2] + c[3]);
         const uint32_t at = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        if ((tid < 4 || tid >= kT - 4) && ct != 0u) atomicOr(&ws->status, kStatusNonFinite);
+        if ((tid < 4 || tid >= kT - 4) && ct != 0u) {
+            atomicOr(&ws->status, kStatusNonFinite);
+            if (kFused) sh.fz_nf = 1u;
+        }
         const double st = (double)ct * (double)B0 + U * (double)at;
         const uint32_t ic = wave_scan_add_u32(ct);
         const double is = wave_scan_add_f64(st);
@@ -691,7 +864,9 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
     }
     if (live && (sg >> 9) != 0u) {
         const uint32_t c = sg & 31u;
-        Dout[c * R + r] = mx > mn ? fmax(dsum - sumsq, 0.0) : 0.0;
+        const double dout = mx > mn ? fmax(dsum - sumsq, 0.0) : 0.0;
+        Dout[c * R + r] = dout;
+        if (kFused) pc.cd[c] = dout;
         double h = hsum;
         if (zw != 0u) {
             const uint32_t first = (uint32_t)tid - off;
@@ -711,14 +886,16 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
             }
             h += point_entropy(acc, sh.lg_c, sh.lg_inv);
         }
-        Hout[c * R + r] = mx > mn ? fmax(h, 0.0) : 0.0;
+        const double hout = mx > mn ? fmax(h, 0.0) : 0.0;
+        Hout[c * R + r] = hout;
+        if (kFused) pc.chh[c] = hout;
     }
+    if constexpr (kFused) fused_tail(sh, tb, fa, ws, r, R, x0, x1, nb0);
 }
 
-hipError_t launch_eval16(const void* x0, const void* x1, int64_t nb0, int64_t R, const RankTable& rt,
-                         double* D, double* H, float* stats, void* ws, hipStream_t st) {
-    if (R == 0) return hipSuccess;
-    Eval16Tables tb;
+// The kernel's tables: distinct uniform fractions, lane layout of the
+// candidate intervals, log2 cells.
+static hipError_t build_tables(const RankTable& rt, Eval16Tables& tb) {
     memset(&tb, 0, sizeof tb);
     tb.rt = rt;
     // distinct interior fractions j/(k-1), k = 3..16, in order of first appearance
@@ -793,12 +970,86 @@ hipError_t launch_eval16(const void* x0, const void* x1, int64_t nb0, int64_t R,
         tb.lg_c[i] = log2(c);
         tb.lg_inv[i] = 1.0 / c;
     }
+    return hipSuccess;
+}
+
+// The tables for rt, built once per thread and rank table (they are the
+// same for every call of a given block size and s).
+static hipError_t make_tables(const RankTable& rt, Eval16Tables& tb) {
+    thread_local RankTable last_rt;
+    thread_local Eval16Tables last_tb;
+    thread_local bool have = false;
+    if (!have || memcmp(&last_rt, &rt, sizeof rt) != 0) {
+        const hipError_t e = build_tables(rt, last_tb);
+        if (e != hipSuccess) return e;
+        last_rt = rt;
+        have = true;
+    }
+    tb = last_tb;
+    return hipSuccess;
+}
+
+hipError_t launch_eval16(const void* x0, const void* x1, int64_t nb0, int64_t R, const RankTable& rt,
+                         double* D, double* H, float* stats, void* ws, hipStream_t st) {
+    if (R == 0) return hipSuccess;
+    Eval16Tables tb;
+    const hipError_t te = make_tables(rt, tb);
+    if (te != hipSuccess) return te;
     if (R < kEvalSmallLaunch)
         hipLaunchKernelGGL(eval16_kernel<kSlotsAll>, dim3((unsigned)R), dim3(kT), 0, st, (const __half*)x0,
-                       (const __half*)x1, nb0, tb, D, H, stats, (WsHeader*)ws);
+                       (const __half*)x1, nb0, tb, D, H, stats, (WsHeader*)ws, FusedArgs{});
     else
         hipLaunchKernelGGL(eval16_kernel<kSlotsLarge>, dim3((unsigned)R), dim3(kT), 0, st, (const __half*)x0,
-                       (const __half*)x1, nb0, tb, D, H, stats, (WsHeader*)ws);
+                       (const __half*)x1, nb0, tb, D, H, stats, (WsHeader*)ws, FusedArgs{});
+    return hipGetLastError();
+}
+
+// Workspace set-up of the one-launch admission: status, rate, ticket and
+// the R published word counts.
+__global__ void __launch_bounds__(1024) fused_reset_kernel(WsHeader* h, uint64_t* desc, uint64_t* rates,
+                                                           int64_t R) {
+    const int tid = threadIdx.x;
+    if (tid < R) {
+        desc[tid] = 0u;
+        rates[tid] = 0u;
+    }
+    if (tid == 0) {
+        h->status = 0;
+        h->phase = 0;
+        h->done = 0;
+        h->err = 0;
+        h->nlam = 0;
+    }
+}
+
+hipError_t launch_admit_fused(const void* x0, const void* x1, int64_t nb0, int64_t R, const RankTable& rt,
+                              double lam_in, int shift, uint64_t seed, double* D, double* H, float* stats,
+                              int32_t* choice, float* codebook, uint8_t* m, uint64_t* off, uint32_t* codes,
+                              void* ws, SolveOut* out, hipStream_t st) {
+    if (R < 1 || R > kFusedMaxBlocks) return hipErrorInvalidValue;
+    Eval16Tables tb;
+    const hipError_t te = make_tables(rt, tb);
+    if (te != hipSuccess) return te;
+    WsHeader* h = (WsHeader*)ws;
+    // published words after the header (the offsets scan's area, unused here)
+    uint64_t* desc = (uint64_t*)((char*)ws + kWsHeaderBytes);
+    uint64_t* rates = desc + kFusedMaxBlocks;
+    hipLaunchKernelGGL(fused_reset_kernel, dim3(1), dim3(1024), 0, st, h, desc, rates, R);
+    FusedArgs fa;
+    fa.lam = lam_in;
+    fa.shift = shift;
+    fa.k0 = (uint32_t)seed;
+    fa.k1 = (uint32_t)(seed >> 32);
+    fa.choice = choice;
+    fa.codebook = codebook;
+    fa.m = m;
+    fa.off = off;
+    fa.desc = desc;
+    fa.rates = rates;
+    fa.codes = codes;
+    fa.out = out;
+    hipLaunchKernelGGL((eval16_kernel<kSlotsAll, true>), dim3((unsigned)R), dim3(kT), 0, st, (const __half*)x0,
+                       (const __half*)x1, nb0, tb, D, H, stats, h, fa);
     return hipGetLastError();
 }
 

@@ -93,7 +93,7 @@ int distinct_quantile_ranks(int n, int s, int32_t* out) {
     return u;
 }
 
-void rank_table(const kvq_plan& p, kvq::RankTable& rt) {
+void build_rank_table(const kvq_plan& p, kvq::RankTable& rt) {
     memset(&rt, 0, sizeof rt);
     if (p.search != KVQ_GRIDS) return;
     rt.n_stats = distinct_quantile_ranks(p.d_block, p.s, rt.rank);
@@ -103,6 +103,20 @@ void rank_table(const kvq_plan& p, kvq::RankTable& rt) {
             for (int c = 0; c < rt.n_stats; ++c)
                 if (rt.rank[c] == q) rt.col[k][j] = (uint8_t)c;
         }
+}
+
+// The rank table of a plan, rebuilt only when the block size, s or the
+// search differ from the calling thread's previous call.
+void rank_table(const kvq_plan& p, kvq::RankTable& rt) {
+    thread_local int key_n = -1, key_s = -1, key_search = -1;
+    thread_local kvq::RankTable cached;
+    if (p.d_block != key_n || p.s != key_s || p.search != key_search) {
+        build_rank_table(p, cached);
+        key_n = p.d_block;
+        key_s = p.s;
+        key_search = p.search;
+    }
+    rt = cached;
 }
 
 bool valid_plan(const kvq_plan* p) {
@@ -346,6 +360,8 @@ kvq_status solve_result(const kvq_plan* p, double B, int32_t mode, double eta, d
     }
     if (e != hipSuccess) return hip_fail(e, "status read-back");
     if (hdr.status & kvq::kStatusNonFinite) return fail(KVQ_ENONFINITE, "NaN or Inf among the KV entries");
+    if (hdr.status & kvq::kStatusFusedStall)
+        return fail(KVQ_EHIP, "one-launch admission: a block's offset look-back did not complete");
     if (hdr.err == KVQ_EINFEASIBLE)
         return fail(KVQ_EINFEASIBLE, "no lambda <= 2^64 brings the rate under %g bits/entry", B);
     if (hdr.err) return fail(KVQ_EINVAL, "solver state error %d", hdr.err);
@@ -383,6 +399,36 @@ kvq_status noalloc_scratch(void** out) {
     }
     *out = g_scratch_ptr[dev];
     return KVQ_OK;
+}
+
+// The admission step at a known multiplier (subgradient mode) on up to
+// kFusedMaxBlocks fp16 blocks of 4096 contiguous entries with s = 16: one
+// kernel scores, chooses, quantizes and packs (after a reset launch), and
+// the call waits once for its result.  Outputs are those of the three
+// calls.
+bool fused_admission(const kvq_plan* p, const kvq_tensor* t, int32_t nt, int32_t mode) {
+    return mode == KVQ_SUBGRAD && p->n_blocks >= 1 && p->n_blocks <= kvq::kFusedMaxBlocks &&
+           fast_fp16_path(p, t, nt);
+}
+
+kvq_status admit_fused(const kvq_plan* p, const kvq_tensor* t, int32_t nt, double* D, double* H, float* stats,
+                       double B, double eta, double* lambda_io, double* rate_out, int32_t* choice,
+                       float* codebook, uint8_t* m, uint64_t* word_off, uint64_t seed, uint32_t* codes,
+                       void* ws, hipStream_t s, bool staging) {
+    kvq::RankTable rt;
+    rank_table(*p, rt);
+    const double lam_in = *lambda_io;
+    void* dev_out = nullptr;
+    SolveState ss;
+    ss.out = staging ? static_cast<kvq::SolveOut*>(kvq::staging_buffer(&dev_out)) : nullptr;
+    ss.direct = ss.out != nullptr && dev_out != nullptr;
+    ss.staging = staging;
+    const hipError_t e = kvq::launch_admit_fused(t[0].data, nt > 1 ? t[1].data : t[0].data, p->tensor_blocks[0],
+                                                 p->n_blocks, rt, lam_in, p->rate_shift, seed, D, H, stats,
+                                                 choice, codebook, m, word_off, codes, ws,
+                                                 ss.direct ? static_cast<kvq::SolveOut*>(dev_out) : nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "one-launch admission");
+    return solve_result(p, B, KVQ_SUBGRAD, eta, lam_in, ws, s, ss, lambda_io, rate_out);
 }
 
 kvq_status quantize_check(const kvq_plan* p, const float* codebook, const uint8_t* m, const uint64_t* word_off,
@@ -457,6 +503,9 @@ kvq_status kvq_admit(const kvq_plan* p, const kvq_tensor* t, int32_t nt, double*
     if (st) return st;
     st = quantize_check(p, codebook, m, word_off, codes, cap);
     if (st) return st;
+    if (fused_admission(p, t, nt, mode))
+        return admit_fused(p, t, nt, D, H, stats, B, eta, lambda_io, rate_out, choice, codebook, m, word_off, seed,
+                           codes, workspace, s, /*staging=*/true);
     const double lam_in = *lambda_io;
     st = eval_enqueue(p, t, nt, g, D, H, stats, workspace, s);
     if (st) return st;
@@ -495,6 +544,9 @@ kvq_status kvq_admit_noalloc(const kvq_plan* p, const kvq_tensor* t, int32_t nt,
     void* ws = nullptr;
     st = noalloc_scratch(&ws);
     if (st) return st;
+    if (fused_admission(p, t, nt, mode))
+        return admit_fused(p, t, nt, D, H, stats, B, eta, lambda_io, rate_out, choice, codebook, m, word_off, seed,
+                           codes, ws, s, /*staging=*/false);
     const double lam_in = *lambda_io;
     // the scratch keeps the previous call's contents: eval's reset kernel
     // clears the status word and the solve's first kernel sets up the

@@ -24,6 +24,7 @@ constexpr int kMaxLam = 64;                       // multipliers per solve pass
 constexpr uint32_t kStatusNonFinite = 1u;
 constexpr uint32_t kStatusAnsOverflow = 2u;  // an entropy-coded block outgrew its region
 constexpr uint32_t kStatusAnsCorrupt = 4u;   // a decoded block's states did not return to 2^16
+constexpr uint32_t kStatusFusedStall = 8u;   // one-launch admission: a predecessor's offset never came
 
 // Fixed header at the start of the caller's workspace.  All solve state lives
 // here so the whole bracket search runs on the device without host syncs.
@@ -313,6 +314,17 @@ hipError_t launch_eval16(const void* x0, const void* x1, int64_t nb0, int64_t R,
 hipError_t launch_eval_alphabet(const Geom& g, int64_t R, int alpha_m, double* D, double* H,
                                 float* stats, void* ws, hipStream_t st);
 hipError_t launch_ws_reset(void* ws, hipStream_t st);
+// One launch of the admission step at a known multiplier for up to
+// kFusedMaxBlocks fp16 blocks of 4096 contiguous entries with s = 16 (grid
+// search): scoring, the choice at lam_in, the codebook, the offsets, the
+// stochastic rounding and packing, the rate sum, preceded by a reset of the
+// workspace header.  `out` (pinned host memory, may be null) receives the
+// solve's result fields.
+constexpr int64_t kFusedMaxBlocks = 1024;
+hipError_t launch_admit_fused(const void* x0, const void* x1, int64_t nb0, int64_t R, const RankTable& rt,
+                              double lam_in, int shift, uint64_t seed, double* D, double* H, float* stats,
+                              int32_t* choice, float* codebook, uint8_t* m, uint64_t* off, uint32_t* codes,
+                              void* ws, struct SolveOut* out, hipStream_t st);
 // Read `bytes` (<= kStagingBytes) of device memory into host memory `dst`
 // on stream st and wait for it, through the calling thread's pinned staging
 // buffer (hipHostMalloc'd on first use and kept until the process ends; a

@@ -26,6 +26,7 @@
 #include <type_traits>
 
 #include "kvq_internal.h"
+#include "kvq_grid_choice.h"
 
 namespace kvq {
 
@@ -36,17 +37,6 @@ constexpr int kScanTile = kSolveThreads * kScanPer;
 enum Phase : int32_t {
     kPhaseDouble = 0, kPhaseDouble2 = 1, kPhaseMulti = 2, kPhaseZero = 3, kPhaseSubgrad = 10
 };
-
-// Objective D + (lambda * d) * H, evaluated without contraction.
-__device__ __forceinline__ double objective(double Dv, double Hv, double lamd) {
-#pragma clang fp contract(off)
-    const double t = lamd * Hv;
-    return Dv + t;
-}
-
-__device__ __forceinline__ unsigned long long rate_fx(double d, double Hv, int shift) {
-    return __double2ull_rn(ldexp(d * Hv, shift));
-}
 
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
 #pragma unroll
@@ -224,58 +214,6 @@ rates_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
         for (int w = 0; w < kSolveThreads / 64; ++w) t += part[w][j];
         atomicAdd(&h->sums[j], t);
     }
-}
-
-// Codepoints of grid candidate c of a block from its minimum, maximum and
-// order statistics (st: the block's first statistic, `stride` apart; col:
-// RankTable::col as a (kMaxS + 1) x kMaxS table, in LDS where it matters),
-// written as the block's codebook row (s entries, zero after the m distinct
-// points); returns m.  The k points are gathered unrolled to kMaxS with
-// unconditional loads (statistic 0 where a point needs none), so the loads
-// are in flight together.  The points are non-decreasing, so equal ones are
-// adjacent: each distinct point is stored at a running position, straight
-// to memory (a register array indexed by a per-lane position compiles into
-// long select chains).
-__device__ int write_grid_codebook(int c, float mn, float mx, const float* st, int64_t stride,
-                                   const uint8_t* col, int s, float* row) {
-    if ((s & 3) == 0 && ((uintptr_t)row & 15u) == 0) {
-#pragma unroll
-        for (int j4 = 0; j4 < kMaxS / 4; ++j4)
-            if (4 * j4 < s) reinterpret_cast<float4*>(row)[j4] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    } else {
-        for (int j = 0; j < s; ++j) row[j] = 0.0f;
-    }
-    if (mn == mx) {
-        row[0] = mn;
-        return 1;
-    }
-    int k;
-    bool uni = false;
-    if (c == 0) {
-        k = 2;
-    } else {
-        k = 3 + (c - 1) / 2;
-        uni = ((c - 1) & 1) == 0;
-    }
-    const bool quant = c != 0 && !uni;
-    int idx[kMaxS];
-#pragma unroll
-    for (int j = 0; j < kMaxS; ++j) idx[j] = quant && j < k ? (int)col[k * kMaxS + j] : 0;
-    float g[kMaxS];
-#pragma unroll
-    for (int j = 0; j < kMaxS; ++j) g[j] = st[idx[j] * stride];
-    int m = 0;
-    float prev = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kMaxS; ++j) {
-        float v = c == 0 ? (j == 0 ? mn : mx) : g[j];
-        if (uni && j < k) v = uniform_point(mn, mx, j, k);  // fp64 division: only where needed
-        const bool keep = j < k && (j == 0 || v != prev);
-        if (keep) row[m] = v;
-        m += keep ? 1 : 0;
-        prev = v;
-    }
-    return m;
 }
 
 // One block's choice at multiplier lam (grid search) from its table row
@@ -913,6 +851,9 @@ greedy_pool_kernel(const double* __restrict__ D, const double* __restrict__ H,
     }
 }
 
+// Pools of up to this many upgrades take greedy_apply_fast_kernel.
+constexpr int kGreedyFast = 1024;
+
 // One workgroup applies upgrades one at a time: the best efficiency
 // (D_cur - D_c) / (d H_c - d H_cur) among pool entries that still improve
 // their block and fit; ties to the lowest block, then candidate.  The chosen
@@ -930,7 +871,7 @@ greedy_apply_kernel(const double* __restrict__ D, const double* __restrict__ H,
     const int tid = threadIdx.x;
     if (h->err || h->pool_overflow) return;
     const uint32_t np = min(h->pool_n, kGreedyPool);
-    if (np == 0) return;
+    if (np <= (uint32_t)kGreedyFast) return;  // greedy_apply_fast_kernel's
     const double d = (double)n;
     if (tid == 0) slack = h->Btot_fx - h->rate_final;
     __syncthreads();
@@ -1002,6 +943,171 @@ greedy_apply_kernel(const double* __restrict__ D, const double* __restrict__ H,
         __threadfence();
         __syncthreads();
         if (!found) break;
+    }
+}
+
+// The same greedy fill for pools of up to kGreedyFast upgrades by one wave
+// with the pool in registers: lane l holds entries l, l + 64, ... of the
+// pool ordered by (block, candidate).  Each step every lane scores its
+// entries against their blocks' current choices and the remaining slack,
+// the wave takes the best by (efficiency, lower entry index, i.e. lower
+// block, then candidate), and the entries of the upgraded block take the
+// winner's values as their block's current ones.  No barrier is needed, and
+// the choices, rates and steps are those of greedy_apply_kernel (which took
+// 2.6 ms for the 444 upgrades of the long-context cache at 1.5 bits per
+// entry, scanning the pool in memory once per step).  Codebooks, levels and
+// word counts of the upgraded blocks are written once at the end.
+constexpr int kGreedyPer = kGreedyFast / 64;
+
+// Wave maximum of v (every lane gets it): DPP steps within rows, then
+// across rows, the result read from lane 63.
+__device__ __forceinline__ unsigned long long wave_max_u64_dpp(unsigned long long v) {
+#define KVQ_MAX64_STEP(CTRL, MASK)                                   \
+    {                                                                \
+        const unsigned long long t = dpp_u64<CTRL, MASK>(0ull, v);   \
+        v = t > v ? t : v;                                           \
+    }
+    KVQ_MAX64_STEP(kDppRowShr1, 0xF)
+    KVQ_MAX64_STEP(kDppRowShr2, 0xF)
+    KVQ_MAX64_STEP(kDppRowShr4, 0xF)
+    KVQ_MAX64_STEP(kDppRowShr8, 0xF)
+    KVQ_MAX64_STEP(kDppBcast15, 0xA)
+    KVQ_MAX64_STEP(kDppBcast31, 0xC)
+#undef KVQ_MAX64_STEP
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+__global__ void __launch_bounds__(64)
+greedy_apply_fast_kernel(const double* __restrict__ D, const double* __restrict__ H,
+                         const double* __restrict__ wgt, const float* __restrict__ stats, int64_t R,
+                         int s, int n, int shift, RankTable rt, WsHeader* h, int32_t* choice,
+                         float* __restrict__ codebook, uint8_t* __restrict__ m_out,
+                         uint64_t* __restrict__ off, const uint2* __restrict__ pool) {
+    __shared__ uint64_t sorted[kGreedyFast];
+    __shared__ double ent_h[kGreedyFast];   // each entry's H and weighted D, read when it wins
+    __shared__ double ent_d[kGreedyFast];
+    const int lane = threadIdx.x;
+    if (h->err || h->pool_overflow) return;
+    const uint32_t np = h->pool_n;
+    if (np == 0 || np > (uint32_t)kGreedyFast) return;  // larger pools: greedy_apply_kernel
+    const double d = (double)n;
+    // the pool ordered by (block, candidate)
+    for (int i = lane; i < kGreedyFast; i += 64)
+        sorted[i] = i < (int)np ? ((uint64_t)pool[i].x << 8 | pool[i].y) : ~0ull;
+    __syncthreads();
+    for (int k = 2; k <= kGreedyFast; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int t = lane; t < kGreedyFast; t += 64) {
+                const int p = t ^ j;
+                if (p > t) {
+                    const uint64_t a = sorted[t], b = sorted[p];
+                    if ((a > b) == ((t & k) == 0)) {
+                        sorted[t] = b;
+                        sorted[p] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    int64_t r[kGreedyPer];
+    int c[kGreedyPer], cur[kGreedyPer];
+    double hc[kGreedyPer], dcv[kGreedyPer], hu[kGreedyPer], du[kGreedyPer];
+    unsigned long long rc[kGreedyPer], ru[kGreedyPer];
+#pragma unroll
+    for (int k = 0; k < kGreedyPer; ++k) {
+        const int i = lane + 64 * k;
+        const bool live = i < (int)np;
+        r[k] = live ? (int64_t)(sorted[i] >> 8) : -1;
+        c[k] = live ? (int)(sorted[i] & 0xffu) : 0;
+        cur[k] = live ? choice[r[k]] : 0;
+        hc[k] = live ? H[c[k] * R + r[k]] : 0.0;
+        dcv[k] = live ? wdist(D, wgt, R, r[k], c[k]) : 0.0;
+        hu[k] = live ? H[cur[k] * R + r[k]] : 0.0;
+        du[k] = live ? wdist(D, wgt, R, r[k], cur[k]) : 0.0;
+        rc[k] = rate_fx(d, hc[k], shift);
+        ru[k] = rate_fx(d, hu[k], shift);
+        ent_h[i] = hc[k];
+        ent_d[i] = dcv[k];
+    }
+    int cur0[kGreedyPer];
+#pragma unroll
+    for (int k = 0; k < kGreedyPer; ++k) cur0[k] = cur[k];
+    __syncthreads();
+    // each entry's efficiency against its block's current choice (0 where it
+    // is no upgrade); it changes only when its block is upgraded.  Positive
+    // doubles order as their bit patterns, so the best entry is the maximum
+    // of (efficiency bits), then the lowest index among equal ones.
+    unsigned long long ekey[kGreedyPer];
+#pragma unroll
+    for (int k = 0; k < kGreedyPer; ++k) {
+        const bool up = r[k] >= 0 && rc[k] > ru[k] && du[k] - dcv[k] > 0.0;
+        ekey[k] = up ? (unsigned long long)__double_as_longlong((du[k] - dcv[k]) / (d * hc[k] - d * hu[k])) : 0ull;
+    }
+    unsigned long long slack = h->Btot_fx - h->rate_final;
+    unsigned long long added = 0;
+    uint32_t swaps = 0;
+    for (uint32_t step = 0; step < np * (uint32_t)kMaxCand; ++step) {
+        unsigned long long best = 0;
+        uint32_t bidx = 0xffffffffu;
+#pragma unroll
+        for (int k = 0; k < kGreedyPer; ++k) {
+            const unsigned long long key = rc[k] - ru[k] <= slack ? ekey[k] : 0ull;
+            if (key > best) {  // entries of a lane rise in index with k: the first of equals stays
+                best = key;
+                bidx = (uint32_t)(lane + 64 * k);
+            }
+        }
+        const unsigned long long top = wave_max_u64_dpp(best);
+        if (top == 0ull) break;
+        const uint32_t idx = wave_min_u32_dpp(best == top ? bidx : 0xffffffffu);
+        const int wl = (int)(idx & 63u), wk_slot = (int)(idx >> 6);
+        const uint64_t wk = sorted[idx];
+        const int64_t wr = (int64_t)(wk >> 8);
+        const int wc = (int)(wk & 0xffu);
+        const double wh = ent_h[idx], wd = ent_d[idx];
+        const unsigned long long wrt = rate_fx(d, wh, shift);
+        // the step's bits: the winner's rate over its block's current one
+        unsigned long long wru = 0;
+#pragma unroll
+        for (int k = 0; k < kGreedyPer; ++k)
+            if (k == wk_slot) wru = ru[k];
+        const uint32_t wru_lo = __builtin_amdgcn_readlane((uint32_t)wru, wl);
+        const uint32_t wru_hi = __builtin_amdgcn_readlane((uint32_t)(wru >> 32), wl);
+        const unsigned long long bits = wrt - (((unsigned long long)wru_hi << 32) | wru_lo);
+        slack -= bits;
+        added += bits;
+        ++swaps;
+#pragma unroll
+        for (int k = 0; k < kGreedyPer; ++k) {
+            if (r[k] == wr) {  // the upgraded block's entries take the winner's values
+                cur[k] = wc;
+                hu[k] = wh;
+                du[k] = wd;
+                ru[k] = wrt;
+                const bool up = rc[k] > ru[k] && du[k] - dcv[k] > 0.0;
+                ekey[k] = up ? (unsigned long long)__double_as_longlong((du[k] - dcv[k]) / (d * hc[k] - d * hu[k]))
+                             : 0ull;
+            }
+        }
+    }
+    // the upgraded blocks: the entry of the final choice writes its block's
+    // choice, codebook, levels and word count
+#pragma unroll
+    for (int k = 0; k < kGreedyPer; ++k) {
+        if (r[k] >= 0 && cur[k] != cur0[k] && c[k] == cur[k]) {
+            choice[r[k]] = cur[k];
+            const int m = write_grid_codebook(cur[k], stats[r[k]], stats[(int64_t)(rt.n_stats - 1) * R + r[k]],
+                                              stats + r[k], R, &rt.col[0][0], s, codebook + r[k] * s);
+            m_out[r[k]] = (uint8_t)m;
+            off[r[k] + 1] = ((uint64_t)n * (uint64_t)code_width(m) + 31u) / 32u;
+        }
+    }
+    if (lane == 0) {
+        h->rate_final += added;
+        h->swaps += swaps;
     }
 }
 
@@ -1206,6 +1312,11 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
         uint2* pool = (uint2*)((char*)ws + ws_pool_offset(R));
         hipLaunchKernelGGL(greedy_pool_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, wgt, R,
                            p.n_cand, (double)n, shift, h, choice, pool);
+        // pools of up to kGreedyFast upgrades take the register-resident
+        // kernel; larger ones the one-entry-scan kernel (each returns at
+        // once when the pool is the other's)
+        hipLaunchKernelGGL(greedy_apply_fast_kernel, dim3(1), dim3(64), 0, st, D, H, wgt, stats, R,
+                           p.s, n, shift, rt, h, choice, codebook, m, off, pool);
         hipLaunchKernelGGL(greedy_apply_kernel, dim3(1), dim3(kSolveThreads), 0, st, D, H, wgt, stats, R,
                            p.s, n, shift, rt, h, choice, codebook, m, off, pool);
     }

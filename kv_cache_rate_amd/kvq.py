@@ -12,7 +12,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libkvq.so")
+# KVQ_LIB names another build of the same library (the host-sanitizer build
+# of the CPU validation tests); by default the in-tree libkvq.so.
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(PKG, "libkvq.so")
 
 KVQ_OK = 0
 KVQ_EINVAL = -1

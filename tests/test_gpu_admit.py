@@ -51,3 +51,38 @@ def test_admit_reports_nonfinite_input():
     with pytest.raises(kvq.KvqError) as ei:
         kvq.kvq_admit(plan, dev, buf, 2.0, kvq.KVQ_SUBGRAD, 40, 1e-3, 0.3, 0)
     assert ei.value.status == kvq.KVQ_ENONFINITE
+
+
+@pytest.mark.parametrize("outer,heads,tensors", [(1, 1, 1), (64, 8, 1), (32, 8, 2), (128, 8, 1), (5, 205, 1)])
+def test_one_launch_admission_matches_the_three_calls(outer, heads, tensors):
+    """Subgradient admission of fp16 head x 32-token blocks: up to 1024
+    blocks take the one-launch kernel (score, choose at lambda, offsets by
+    look-back, quantize, pack); 1025 blocks (5 x 205) take the three-step
+    path.  Every output equals the three calls', bit for bit, from 1 block
+    to 1024 and with K and V."""
+    import torch
+    from kv_cache_rate_amd import kvq
+    rng = np.random.default_rng(1000 + outer * heads * tensors)
+    xs = [(rng.standard_t(5.0, size=(outer, heads, 32, 128))).astype(np.float16) for _ in range(tensors)]
+    dev = [torch.from_numpy(x).cuda() for x in xs]
+    plan = kvq.kvq_plan_blocks(dev, 32, 128, 16)
+    a = kvq.allocate(plan)
+    b = kvq.allocate(plan)
+    for k in ("choice", "codebook", "off", "codes"):
+        b[k].fill_(-1)
+    lam0 = 0.37
+    lam_a, rate_a = kvq.admit(plan, dev, a, 2.0, kvq.KVQ_SUBGRAD, 40, 1e-3, lam0, 11)
+    lam_b, rate_b = kvq.kvq_admit(plan, dev, b, 2.0, kvq.KVQ_SUBGRAD, 40, 1e-3, lam0, 11)
+    torch.cuda.synchronize()
+    assert lam_a == lam_b and rate_a == rate_b, (lam_a, lam_b, rate_a, rate_b)
+    for k in ("D", "H", "stats", "choice", "codebook", "m", "off"):
+        assert torch.equal(a[k], b[k]), k
+    words = int(a["off"][-1].item())
+    assert torch.equal(a["codes"][:words], b["codes"][:words])
+    # and the next step from the returned multiplier agrees as well
+    lam_a2, _ = kvq.admit(plan, dev, a, 2.0, kvq.KVQ_SUBGRAD, 40, 1e-3, lam_a, 12)
+    lam_b2, _ = kvq.kvq_admit(plan, dev, b, 2.0, kvq.KVQ_SUBGRAD, 40, 1e-3, lam_b, 12)
+    torch.cuda.synchronize()
+    assert lam_a2 == lam_b2
+    words = int(a["off"][-1].item())
+    assert torch.equal(a["codes"][:words], b["codes"][:words])

@@ -49,3 +49,43 @@ def test_lambda_trace_matches_the_oracle():
               flush=True)
     # the multiplier moves against the rate error: lambda_t - lambda_{t-1} = eta (Rbar - B)
     assert len(trace) == 7
+
+
+def _stream(kvq, torch, plan, dev_batches, lam, first_step, steps):
+    """Admit steps first_step .. first_step + steps - 1 (batch t % 8, Philox
+    seed t) from multiplier lam; returns (lam, per-step codes and lambdas)."""
+    w = W.DECODE_ADMIT_FP16
+    buf = kvq.allocate(plan)
+    out = []
+    for t in range(first_step, first_step + steps):
+        lam, rate = kvq.kvq_admit(plan, dev_batches[t % len(dev_batches)], buf, w.B, kvq.KVQ_SUBGRAD,
+                                  w.iters, w.eta, lam, t)
+        torch.cuda.synchronize()
+        words = int(buf["off"][-1].item())
+        out.append((lam, rate, buf["codes"][:words].clone(), buf["codebook"].clone(), buf["off"].clone()))
+    return lam, out
+
+
+def test_resume_from_saved_multiplier_and_step(tmp_path):
+    """The decode stream's only state across calls is the multiplier and the
+    step counter (the Philox seed of a step).  Saving both after step k,
+    restoring them into fresh buffers and continuing gives the same codes,
+    codebooks, offsets, rates and multipliers, bit for bit, as the stream
+    that never stopped."""
+    import json
+    import torch
+    from kv_cache_rate_amd import kvq
+    batches = [[torch.from_numpy(x).cuda() for x in _batch(b)] for b in range(8)]
+    plan = kvq.kvq_plan_blocks(batches[0], 32, 128, 16)
+    lam0 = 0.5
+    _, whole = _stream(kvq, torch, plan, batches, lam0, 1, 10)
+    k = 4
+    lam_k, head = _stream(kvq, torch, plan, batches, lam0, 1, k)
+    path = tmp_path / "stream_state.json"
+    path.write_text(json.dumps({"lambda": lam_k.hex(), "next_step": k + 1}))
+    state = json.loads(path.read_text())
+    _, tail = _stream(kvq, torch, plan, batches, float.fromhex(state["lambda"]), state["next_step"], 10 - k)
+    for t, (a, b) in enumerate(zip(whole, head + tail), start=1):
+        assert a[0] == b[0] and a[1] == b[1], (t, a[0], b[0])
+        for i in (2, 3, 4):
+            assert torch.equal(a[i], b[i]), (t, i)
