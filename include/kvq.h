@@ -334,7 +334,7 @@ kvq_status kvq_ans_decode(const kvq_plan* p, const void* stream, const uint64_t*
    the stored codepoints.  The plan must hold K (tensor 0) and V (tensor 1)
    [outer, heads, tokens, 128] cut into head x 32-token blocks; query head g
    reads KV head g / G, G = q_heads / heads any whole number >= 1 (run as
-   passes over 4, 2 and 1 query heads, each reading the codes once); K and V
+   passes over up to 4 query heads, each reading the codes once); K and V
    of equal shape, outer and heads at most 65535.  fp32 arithmetic. */
 
 /* Bytes of the split-partials workspace for q_heads query heads (host). */
