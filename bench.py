@@ -38,10 +38,10 @@ def log(*a):
 # Source files each timed call's kernels are built from (the recorded HBM
 # traffic of a kernel is used only while these files are unchanged).
 KERNEL_SOURCES = {
-    "eval": ("kvq_eval16.hip", "kvq_internal.h"),
-    "solve": ("kvq_solve.hip", "kvq_internal.h"),
-    "quantize_pack": ("kvq_quant.hip", "kvq_internal.h"),
-    "dequantize": ("kvq_quant.hip", "kvq_internal.h"),
+    "eval": ("kvq_eval16.hip", "kvq_internal.h", "kvq_grid_choice.h", "kvq_quant_block.h"),
+    "solve": ("kvq_solve.hip", "kvq_internal.h", "kvq_grid_choice.h"),
+    "quantize_pack": ("kvq_quant.hip", "kvq_internal.h", "kvq_quant_block.h"),
+    "dequantize": ("kvq_quant.hip", "kvq_internal.h", "kvq_quant_block.h"),
 }
 
 
@@ -463,6 +463,9 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a device-to-device copy of BYTES (reference for HBM "
                          "byte counters) and exit")
+    ap.add_argument("--read-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a sum over BYTES of device memory (a read-only kernel of "
+                         "known size, to cross-check the HBM read counter's scale) and exit")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path; "
@@ -480,6 +483,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": src.numel() * 4, "copies": 3}), flush=True)
+        return
+    if a.read_probe:
+        src = torch.ones(a.read_probe // 4, dtype=torch.float32, device="cuda")
+        tot = 0.0
+        for _ in range(3):
+            tot += float(src.sum().item())
+        print(json.dumps({"read_probe_bytes": src.numel() * 4, "sums": 3, "total": tot}), flush=True)
         return
 
     w = W.BY_NAME[a.workload]
