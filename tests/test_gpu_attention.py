@@ -194,10 +194,11 @@ def test_narrow_and_constant_blocks():
     _run(w, [x, v], 8)
 
 
-@pytest.mark.parametrize("group", [3, 8])
+@pytest.mark.parametrize("group", [3, 5, 8])
 def test_larger_and_odd_groups(group):
-    """8 query heads per KV head (run as two passes of 4) and 3 (a pass of
-    2 and one of 1): query head g reads KV head g // G."""
+    """8 query heads per KV head (run as two passes of 4), 5 (a pass of 4
+    and one of 1) and 3 (one pass with a row unused): query head g reads KV
+    head g // G."""
     rng = np.random.default_rng(23)
     x = rng.standard_normal((2, 2, 40 * 32, 128)).astype(np.float16)
     v = rng.laplace(size=(2, 2, 40 * 32, 128)).astype(np.float16)

@@ -19,7 +19,11 @@ The oracle cannot score all 524288 blocks in a test's time, so:
   block's choice is also the argmin of the oracle's own row;
 * the greedy fill is replayed by the oracle on the GPU's table (page "Joint
   Tucker-rank and residual-bit KV allocator", Implementation notes): same
-  upgrades, same final choice.
+  upgrades, same final choice;
+* decode attention over the whole quantized stack (32 query heads, 4 per KV
+  head, the configuration bench.py times) is checked on 16 sampled KV heads,
+  all 4 of their query heads, against the oracle on the decoded cache, each
+  output within the fp32 bound of tests/test_gpu_attention.py.
 """
 
 import math
@@ -223,3 +227,44 @@ def test_fp32_large_launch_sampled():
     assert np.array_equal(g["choice"], c_lam)
     sample = sorted(set([0, 1, 8191, 8192, 16383] + np.random.default_rng(5).integers(0, 16384, 59).tolist()))
     _check_sampled(w, plan, g, lam, sample)
+
+
+def test_long_context_full_size_decode_attention_sampled(long_context):
+    import torch
+    from kv_cache_rate_amd import kvq
+    from oracle import attention
+    from .test_gpu_attention import _fp32_bound
+    w, dev = long_context
+    plan, g, lam, rate = _run(long_context, 2.0, "bisect")
+    L, Hk, T, Dm = dev[0].shape
+    G = 4
+    Hq = G * Hk
+    q = np.random.default_rng(9).standard_normal((L, Hq, Dm)).astype(np.float32)
+    qd = torch.from_numpy(q).cuda()
+    out = torch.empty_like(qd)
+    work = torch.empty(kvq.kvq_decode_attention_workspace(plan, Hq), dtype=torch.uint8, device="cuda")
+    scale = 1.0 / np.sqrt(Dm)
+    _say("decode attention over the full stack")
+    kvq.kvq_decode_attention(plan, g["codes"], torch.from_numpy(g["codebook"]).cuda(),
+                             torch.from_numpy(g["m"]).cuda(), torch.from_numpy(g["off"].view(np.int64)).cuda(),
+                             qd, Hq, scale, out, work)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    nbK = plan.tensor_blocks[0]
+    C = T // 32
+    rng = np.random.default_rng(10)
+    heads = {(0, 0), (L - 1, Hk - 1)}
+    while len(heads) < 16:
+        heads.add((int(rng.integers(L)), int(rng.integers(Hk))))
+    worst = 0.0
+    for o, h in sorted(heads):
+        r0 = (o * Hk + h) * C
+        K = g["xhat"][r0:r0 + C].cpu().numpy().astype(np.float64).reshape(1, 1, T, Dm)
+        V = g["xhat"][nbK + r0:nbK + r0 + C].cpu().numpy().astype(np.float64).reshape(1, 1, T, Dm)
+        qs = q[o:o + 1, G * h:G * h + G]
+        ref = attention.decode_attention(K, V, qs, scale)
+        bound, _ = _fp32_bound(K, V, qs, scale, ref)
+        err = np.abs(got[o:o + 1, G * h:G * h + G] - ref)
+        worst = max(worst, float((err / bound).max()))
+        assert np.all(err <= bound), (o, h, float((err / bound).max()))
+    _say(f"16 KV heads x 4 query heads: largest error / bound {worst:.3g}")
