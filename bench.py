@@ -164,10 +164,22 @@ def decode_latency(torch, kvq, W, steps=1000, warmup=20):
         t1 = time.perf_counter()
         if i >= warmup:
             fused_us.append((t1 - t0) * 1e6)
+    # and through a prepared kvq_admit (arguments marshalled once, as a
+    # decode loop over fixed buffers would call it)
+    admit = kvq.prepare_admit(plan, cur, buf, w.B, kvq.KVQ_SUBGRAD, w.iters, w.eta, w.seed, st)
+    lam_p = lam0
+    prep_us = []
+    for i in range(warmup + steps):
+        t0 = time.perf_counter()
+        lam_p, _ = admit(lam_p)
+        t1 = time.perf_counter()
+        if i >= warmup:
+            prep_us.append((t1 - t0) * 1e6)
     q = lambda v: {"p50": float(np.percentile(v, 50)), "p90": float(np.percentile(v, 90))}
     return {"workload": w.name, "steps": steps, "step_us": q(step_us),
             "calls_us": {k: q(v) for k, v in per.items()}, "lambda_final": lam,
-            "kvq_admit_step_us": q(fused_us), "kvq_admit_lambda_final": lam_f}
+            "kvq_admit_step_us": q(fused_us), "kvq_admit_lambda_final": lam_f,
+            "kvq_admit_prepared_step_us": q(prep_us), "kvq_admit_prepared_lambda_final": lam_p}
 
 
 def extensions(torch, kvq, W, w, plan, dev, buf, stream):

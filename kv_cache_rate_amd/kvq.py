@@ -346,6 +346,41 @@ def kvq_admit(plan, tensors, buf, B, mode=KVQ_BISECT, iters=40, eta=1e-3, lam=0.
     return lam_io.value, rate.value
 
 
+def prepare_admit(plan, tensors, buf, B, mode=KVQ_SUBGRAD, iters=40, eta=1e-3, seed=0, stream=None,
+                  noalloc=False):
+    """kvq_admit (or, with ``noalloc``, kvq_admit_noalloc) for a loop over one
+    set of buffers, such as a decode loop: the arguments are marshalled once
+    and each call only sets the incoming multiplier.  The tensors' contents
+    may change between calls; their storage and shapes, the buffers and the
+    stream may not.  Returns a function ``lam -> (lambda,
+    rate_bits_per_entry)`` with kvq_admit's results."""
+    L = lib()
+    fn = L.kvq_admit_noalloc if noalloc else L.kvq_admit
+    vp = ctypes.c_void_p
+    arr = _tensor_array(tensors)
+    lam_io = ctypes.c_double(0.0)
+    rate = ctypes.c_double(0.0)
+    codes = buf["codes"]
+    args = [ctypes.byref(plan), arr, ctypes.c_int32(len(tensors)), vp(_ptr(buf["D"])), vp(_ptr(buf["H"])),
+            vp(_ptr(buf["stats"])), ctypes.c_double(B), ctypes.c_int32(mode), ctypes.c_int32(iters),
+            ctypes.c_double(eta), ctypes.byref(lam_io), ctypes.byref(rate), vp(_ptr(buf["choice"])),
+            vp(_ptr(buf["codebook"])), vp(_ptr(buf["m"])), vp(_ptr(buf["off"])), ctypes.c_uint64(int(seed)),
+            vp(_ptr(codes)), ctypes.c_uint64(int(codes.numel()))]
+    if not noalloc:
+        args.append(vp(_ptr(buf["workspace"])))
+    args.append(vp(_stream(stream)))
+    keep = (plan, tensors, buf, arr)
+
+    def call(lam):
+        lam_io.value = lam
+        st = fn(*args)
+        if st:
+            raise KvqError(st, last_error())
+        return lam_io.value, rate.value
+    call.keep = keep  # the marshalled pointers stay valid while the call lives
+    return call
+
+
 def kvq_admit_noalloc(plan, tensors, buf, B, mode=KVQ_BISECT, iters=40, eta=1e-3, lam=0.0, seed=0,
                       stream=None):
     """kvq_admit with the library's static device scratch in place of a

@@ -86,3 +86,28 @@ def test_one_launch_admission_matches_the_three_calls(outer, heads, tensors):
     assert lam_a2 == lam_b2
     words = int(a["off"][-1].item())
     assert torch.equal(a["codes"][:words], b["codes"][:words])
+
+
+def test_prepared_admit_matches_kvq_admit(noalloc=False):
+    """prepare_admit (arguments marshalled once, the multiplier carried from
+    step to step) gives kvq_admit's multipliers, rates and codes bit for bit
+    over a short decode loop whose input changes every step."""
+    import torch
+    from kv_cache_rate_amd import kvq
+    w = W.DECODE_ADMIT_FP16
+    batches = [[torch.from_numpy(x).cuda() for x in W.generate(w, which=b)] for b in range(2)]
+    cur = [torch.empty_like(t) for t in batches[0]]
+    plan = kvq.kvq_plan_blocks(cur, w.tokens_per_block, w.dims_per_block, w.s)
+    a, b = kvq.allocate(plan), kvq.allocate(plan)
+    call = kvq.prepare_admit(plan, cur, b, w.B, kvq.KVQ_SUBGRAD, w.iters, w.eta, w.seed, noalloc=noalloc)
+    la = lb = 0.52
+    for step in range(4):
+        for t, src in zip(cur, batches[step % 2]):
+            t.copy_(src)
+        la, ra = kvq.kvq_admit(plan, cur, a, w.B, kvq.KVQ_SUBGRAD, w.iters, w.eta, la, w.seed)
+        lb, rb = call(lb)
+        torch.cuda.synchronize()
+        assert la == lb and ra == rb, (step, la, lb, ra, rb)
+        for k in ("choice", "m", "off", "codebook"):
+            assert torch.equal(a[k], b[k]), (step, k)
+        assert torch.equal(a["codes"][:int(a["off"][-1])], b["codes"][:int(b["off"][-1])]), step

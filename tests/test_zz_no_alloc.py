@@ -61,3 +61,24 @@ def test_noalloc_matches_admit_on_two_calls_in_a_row():
     _say(f"call 3: {w2.name}[:16], bisect")
     R3, _ = _compare(torch, kvq, _inputs(torch, w2, outer=16), w2, kvq.KVQ_BISECT, 0.0, 1.5)
     assert R3 == 128
+
+
+def test_prepared_noalloc_matches_admit():
+    """The binding's prepared form of kvq_admit_noalloc (arguments
+    marshalled once) over three decode steps from one multiplier: the same
+    multipliers, rates and codes as kvq_admit."""
+    import torch
+    from kv_cache_rate_amd import kvq
+    w = W.DECODE_ADMIT_FP16
+    dev = _inputs(torch, w, outer=16)
+    plan = kvq.kvq_plan_blocks(dev, w.tokens_per_block, w.dims_per_block, w.s)
+    a, b = kvq.allocate(plan), kvq.allocate(plan)
+    call = kvq.prepare_admit(plan, dev, b, w.B, kvq.KVQ_SUBGRAD, w.iters, w.eta, w.seed, noalloc=True)
+    la = lb = 0.52
+    for step in range(3):
+        la, ra = kvq.kvq_admit(plan, dev, a, w.B, kvq.KVQ_SUBGRAD, w.iters, w.eta, la, w.seed)
+        lb, rb = call(lb)
+        torch.cuda.synchronize()
+        assert la == lb and ra == rb, (step, la, lb)
+        words = int(a["off"][-1].item())
+        assert torch.equal(a["codes"][:words], b["codes"][:words]), step
