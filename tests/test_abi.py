@@ -257,3 +257,20 @@ def test_decode_attention_validation(L):
     assert Lb.kvq_decode_attention(ctypes.byref(p), 8, 8, 8, 8, 8, 32, ctypes.c_float(0.1), 8, 8,
                                    10, None) == kvq.KVQ_ENOSPC
 
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without the HIP library every call raises: there is no CPU fallback."""
+    import sys
+    code = ("from kv_cache_rate_amd import kvq\n"
+            "try:\n"
+            "    kvq.lib()\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    print('loaded')\n")
+    env = dict(os.environ, KVQ_LIB=str(tmp_path / "libkvq_absent.so"))
+    res = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                         timeout=120)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.startswith("raised:") and "is missing" in res.stdout, res.stdout
