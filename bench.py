@@ -94,8 +94,11 @@ def load_profile(kernel, sha):
 
 
 # VALU issue peak: 256 CUs x 4 SIMDs, one wave64 VALU instruction per SIMD
-# every 4 cycles (16 lanes per cycle), at 2.4 GHz
-VALU_PEAK_WAVE_INSTR_PER_S = 256 * 4 * 2.4e9 / 4
+# every 4 cycles (16 lanes per cycle), at 2.4 GHz; some pairs of simple
+# instructions issue together in one quad-cycle (counted by the profile)
+VALU_SIMDS = 256 * 4
+VALU_CLOCK_HZ = 2.4e9
+VALU_PEAK_WAVE_INSTR_PER_S = VALU_SIMDS * VALU_CLOCK_HZ / 4
 
 
 def copy_bandwidth(torch, nbytes=1 << 30, reps=5):
@@ -611,6 +614,13 @@ def main():
         rec["valu_issue"] = {"kernel": dom, "wave_instructions_per_launch": ins,
                              "achieved_per_s": rate, "peak_per_s": VALU_PEAK_WAVE_INSTR_PER_S,
                              "frac": rate / VALU_PEAK_WAVE_INSTR_PER_S}
+        dual = prof.get("valu_dual_issue_quads_per_launch")
+        if dual is not None:
+            # quad-cycles the SIMDs' VALUs are busy (a dual-issued pair takes
+            # one) over this run's kernel time
+            rec["valu_issue"]["dual_issue_quads_per_launch"] = dual
+            rec["valu_issue"]["busy_frac"] = 4.0 * (ins - dual) / (
+                VALU_SIMDS * VALU_CLOCK_HZ * per[dom] * 1e-3)
     if extras:
         rec["copy_GBps"] = extras["copy_GBps"]
         rec["eval_plus_quantize"]["frac_of_copy"] = (alg["eval"] + alg["quantize_pack"]) / \
