@@ -208,6 +208,10 @@ kvq_status kvq_eval_candidates(const kvq_plan* p, const kvq_tensor* t, int32_t n
    rate sum_r d_r H_r / sum_r d_r of the choice.  Synchronises stream s at
    the end; KVQ_BISECT also waits once after the lambda = 0 probe, which
    decides whether the bracket passes are launched.
+   workspace: the one kvq_eval_candidates wrote these tables with (its
+   status word, the first 4 bytes, carries eval's NaN/Inf report and is
+   read here); for tables from elsewhere, plan.workspace_bytes whose first
+   4 bytes are zero (a zero-filled buffer will do).
    Errors: KVQ_ENONFINITE (from eval), KVQ_EINFEASIBLE, KVQ_EINVAL. */
 kvq_status kvq_solve_lambda(const kvq_plan* p, const double* D, const double* H,
                             const float* stats, double B_bits_per_entry, int32_t mode,

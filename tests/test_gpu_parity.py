@@ -401,3 +401,59 @@ def test_greedy_fill(name, B, iters):
     assert np.array_equal(g["off"], o["offsets"])
     agree = np.ones(o["R"], dtype=bool)
     assert parity.compare_codes(g, o, agree, w.seed) <= o["near"]
+
+
+def _monotone_tables(R, seed, C=29):
+    """Seeded score tables [R][C]: in every block H rises and D falls with
+    the candidate index, D convex in H (distinct random steps, so no two
+    objectives tie)."""
+    rng = np.random.default_rng(seed)
+    steps_h = rng.uniform(0.001, 0.05, size=(R, C - 1)) * rng.uniform(0.05, 1.0, size=(R, 1))
+    H = np.concatenate([rng.uniform(0.2, 0.5, (R, 1)), steps_h], axis=1).cumsum(axis=1)
+    slopes = np.sort(rng.uniform(0.5, 5.0, size=(R, C - 1)), axis=1)[:, ::-1]
+    D = 100.0 - np.concatenate([np.zeros((R, 1)), (slopes * steps_h).cumsum(axis=1)], axis=1)
+    return D, H
+
+
+@pytest.mark.parametrize("R,iters,lo,hi", [(16, 40, 1, 128), (8, 4, 129, 256), (16, 4, 257, 512),
+                                           (32, 4, 513, 1024), (40, 4, 1025, 16384)])
+def test_greedy_fill_pool_sizes(R, iters, lo, hi):
+    """The greedy post-pass on score tables given directly to
+    kvq_solve_lambda, sized so that the upgrades fitting the slack left by
+    the bisection (its pool) fall in each of the apply kernel's ranges: the
+    register pool scanning 2, 4, 8 or 16 slots per lane, and the in-memory
+    pool above 1024 entries.  Multiplier, choices and rate equal the
+    oracle's bisection and greedy fill (page "Joint Tucker-rank and
+    residual-bit KV allocator", Implementation notes)."""
+    import torch
+    from kv_cache_rate_amd import kvq
+    D, H = _monotone_tables(R, seed=R)
+    d = 4096.0
+    B = float(np.mean(H[:, 14]))
+    lam_o, ch_o, rate_o, Btot, _ = ecasq.solve_bisect(D, H, d, B, iters, None)
+    rows = np.arange(R)
+    rates = d * H
+    slack = float(Btot) - float(rate_o)
+    pool = int(((rates - rates[rows, ch_o][:, None] > 0) & (D[rows, ch_o][:, None] - D > 0) &
+                (rates - rates[rows, ch_o][:, None] <= slack)).sum())
+    assert lo <= pool <= hi, pool
+    ch_g, rate_g, swaps = ecasq.greedy_fill(D, H, d, Btot, ch_o)
+    # a plan of R fp16 head x 32 x 128 blocks (its data is never read here)
+    x = torch.zeros((1, 1, 32 * R, 128), dtype=torch.float16, device="cuda")
+    plan = kvq.kvq_plan_blocks([x], 32, 128, 16, kvq.KVQ_GRIDS, 0)
+    assert plan.n_blocks == R and plan.n_cand == D.shape[1]
+    buf = kvq.allocate(plan, dequant=False)
+    buf["workspace"].zero_()  # no eval ran: its status word must start clear
+    buf["D"].copy_(torch.from_numpy(np.ascontiguousarray(D.T)))
+    buf["H"].copy_(torch.from_numpy(np.ascontiguousarray(H.T)))
+    st = np.repeat(np.linspace(-1.0, 1.0, plan.n_stats, dtype=np.float32)[:, None], R, axis=1)
+    buf["stats"].copy_(torch.from_numpy(st))
+    lam, rate = kvq.kvq_solve_lambda(plan, buf["D"], buf["H"], buf["stats"], B, kvq.KVQ_BISECT_GREEDY, iters,
+                                     1e-3, 0.0, buf["choice"], buf["codebook"], buf["m"], buf["off"],
+                                     buf["workspace"])
+    torch.cuda.synchronize()
+    _say(f"greedy pool {pool} (R={R}, iters={iters}): swaps {len(swaps)} lambda {lam!r}")
+    assert lam == lam_o
+    assert np.array_equal(buf["choice"].cpu().numpy().astype(np.int64), ch_g)
+    assert rate == pytest.approx(rate_g / (d * R), rel=1e-12)
+    assert rate <= B + 1e-12
