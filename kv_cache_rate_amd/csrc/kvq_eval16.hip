@@ -112,6 +112,7 @@ struct Shared {
     uint16_t ukey[kNU];
     double lg_c[64];
     double lg_inv[64];
+    uint32_t rcol[(kMaxS + 1) * kMaxS / 4];  // one-launch admission: the rank table's columns
     uint32_t wmin[kW], wmax[kW], wtot[kW];
     double wsq[kW], wts1[kW];
     uint32_t nslots;
@@ -334,33 +335,55 @@ __device__ __forceinline__ void fused_tail(Shared<kSlots>& sh, const Eval16Table
                                            const __half* x1, int64_t nb0) {
     const int tid = threadIdx.x;
     __syncthreads();  // every candidate's D and H are in LDS
-    if (tid == 0) {
+    if (tid < 64) {
+        // the choice: lane c scores candidate c, and the lowest index among
+        // equal minimal objectives wins (as in the solve's final pass).  The
+        // objectives are >= 0 (+ 0.0 turns a -0 into +0), so their bit
+        // patterns order as their values.
         const PhaseC& pc = sh.u.c;
         const double lamd = fa.lam * 4096.0;
-        double best = 0.0, bestH = 0.0;
-        int bc = -1;
-        for (int c = 0; c < kMaxCand; ++c) {
-            const double o = objective(pc.cd[c], pc.chh[c], lamd);
-            if (bc < 0 || o < best) {
-                best = o;
-                bestH = pc.chh[c];
-                bc = c;
-            }
-        }
+        const double o = tid < kMaxCand ? objective(pc.cd[tid], pc.chh[tid], lamd) + 0.0 : __builtin_huge_val();
+        const uint64_t key = (uint64_t)__double_as_longlong(o);
+        const uint32_t khi = (uint32_t)(key >> 32), klo = (uint32_t)key;
+        const uint32_t mhi = wave_min_u32_dpp(khi);
+        const uint32_t mlo = wave_min_u32_dpp(khi == mhi ? klo : 0xffffffffu);
+        const int bc = __builtin_amdgcn_readfirstlane(__builtin_ctzll(__ballot(khi == mhi && klo == mlo)));
+        // its codebook, the points of write_grid_codebook one per lane:
+        // lane j computes point j, keeps it unless it equals point j - 1,
+        // and stores it at the count of kept points before it
         const float mn = sh.P[kPQ].v, mx = sh.P[kPQ + kNQ - 1].v;
-        const int m = write_grid_codebook(bc, mn, mx, &sh.P[kPQ].v, (int64_t)(sizeof(Point) / sizeof(float)),
-                                          &tb.rt.col[0][0], kMaxS, sh.book);
-        fa.choice[r] = bc;
-        fa.m[r] = (uint8_t)m;
-        const uint64_t words = (4096u * (uint32_t)code_width(m) + 31u) / 32u;
-        const uint64_t rate = rate_fx(4096.0, bestH, fa.shift);
-        __hip_atomic_store(&fa.desc[r], kPub | (sh.fz_nf ? kPubNF : 0ull) | words, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&fa.rates[r], kPub | rate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (r == 0) fa.off[0] = 0;
-        sh.fz_m = m;
-        sh.fz_ob = words;
-        sh.fz_rate = rate;
+        const int k = bc == 0 ? 2 : 3 + (bc - 1) / 2;
+        const bool uni = bc != 0 && ((bc - 1) & 1) == 0;
+        const int j = tid;
+        float v = 0.0f;
+        if (j < k) {
+            if (bc == 0)
+                v = j == 0 ? mn : mx;
+            else if (uni)
+                v = uniform_point(mn, mx, j, k);
+            else
+                v = sh.P[kPQ + reinterpret_cast<const uint8_t*>(sh.rcol)[k * kMaxS + j]].v;
+        }
+        const float prev = __shfl_up(v, 1, 64);
+        const bool keep = mn == mx ? j == 0 : (j < k && (j == 0 || v != prev));
+        const uint64_t kb = __ballot(keep);
+        const int m = __popcll(kb);
+        if (j < kMaxS) sh.book[j] = 0.0f;
+        if (keep) sh.book[__popcll(kb & ((1ull << j) - 1ull))] = mn == mx ? mn : v;
+        if (tid == 0) {
+            const double bestH = pc.chh[bc];
+            fa.choice[r] = bc;
+            fa.m[r] = (uint8_t)m;
+            const uint64_t words = (4096u * (uint32_t)code_width(m) + 31u) / 32u;
+            const uint64_t rate = rate_fx(4096.0, bestH, fa.shift);
+            __hip_atomic_store(&fa.desc[r], kPub | (sh.fz_nf ? kPubNF : 0ull) | words, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&fa.rates[r], kPub | rate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (r == 0) fa.off[0] = 0;
+            sh.fz_m = m;
+            sh.fz_ob = words;
+            sh.fz_rate = rate;
+        }
     }
     __syncthreads();
     if (tid < kMaxS) fa.codebook[r * kMaxS + tid] = sh.book[tid];
@@ -481,6 +504,8 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         sh.lg_c[tid] = tb.lg_c[tid];
         sh.lg_inv[tid] = tb.lg_inv[tid];
     }
+    if (kFused && tid < (kMaxS + 1) * kMaxS / 4)
+        sh.rcol[tid] = reinterpret_cast<const uint32_t*>(&tb.rt.col[0][0])[tid];
     if (tid == 0) {
         sh.nslots = 0u;
         if (kFused) sh.fz_nf = 0u;

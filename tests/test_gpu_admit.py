@@ -88,6 +88,37 @@ def test_one_launch_admission_matches_the_three_calls(outer, heads, tensors):
     assert torch.equal(a["codes"][:words], b["codes"][:words])
 
 
+def test_one_launch_admission_ties_and_constant_blocks():
+    """The one-launch admission on blocks whose candidates tie (a constant
+    block, an all-zero block, blocks of two and three distinct values: many
+    candidates then share their codebook, D and H, and the lowest index must
+    win) and whose codebooks merge equal points: every output equals the
+    three calls', bit for bit."""
+    import torch
+    from kv_cache_rate_amd import kvq
+    rng = np.random.default_rng(77)
+    x = rng.standard_t(5.0, size=(2, 8, 32, 128)).astype(np.float16)
+    x[0, 0] = np.float16(0.5)
+    x[0, 1] = np.float16(0.0)
+    x[0, 2] = rng.choice(np.array([-1.0, 1.0], dtype=np.float16), size=(32, 128))
+    x[0, 3] = rng.choice(np.array([-2.0, 0.25, 3.0], dtype=np.float16), size=(32, 128))
+    x[1, 5, :16] = np.float16(-0.75)  # half the block on one value
+    dev = [torch.from_numpy(x).cuda()]
+    plan = kvq.kvq_plan_blocks(dev, 32, 128, 16)
+    a = kvq.allocate(plan)
+    b = kvq.allocate(plan)
+    for lam0 in (0.0, 0.37, 5.0):
+        lam_a, rate_a = kvq.admit(plan, dev, a, 2.0, kvq.KVQ_SUBGRAD, 40, 1e-3, lam0, 5)
+        lam_b, rate_b = kvq.kvq_admit(plan, dev, b, 2.0, kvq.KVQ_SUBGRAD, 40, 1e-3, lam0, 5)
+        torch.cuda.synchronize()
+        assert lam_a == lam_b and rate_a == rate_b, (lam0, lam_a, lam_b, rate_a, rate_b)
+        for k in ("D", "H", "stats", "choice", "codebook", "m", "off"):
+            assert torch.equal(a[k], b[k]), (lam0, k)
+        words = int(a["off"][-1].item())
+        assert torch.equal(a["codes"][:words], b["codes"][:words]), lam0
+    assert int(a["m"][0].item()) == 1 and int(a["m"][1].item()) == 1
+
+
 def test_prepared_admit_matches_kvq_admit(noalloc=False):
     """prepare_admit (arguments marshalled once, the multiplier carried from
     step to step) gives kvq_admit's multipliers, rates and codes bit for bit
