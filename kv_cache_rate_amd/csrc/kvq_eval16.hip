@@ -331,8 +331,7 @@ struct FusedArgs {
 // for the host.
 template <int kSlots>
 __device__ __forceinline__ void fused_tail(Shared<kSlots>& sh, const Eval16Tables& tb, const FusedArgs& fa,
-                                           WsHeader* ws, int64_t r, int64_t R, const __half* x0,
-                                           const __half* x1, int64_t nb0) {
+                                           WsHeader* ws, int64_t r, int64_t R, const uint32_t (&hw)[kPer / 2]) {
     const int tid = threadIdx.x;
     __syncthreads();  // every candidate's D and H are in LDS
     if (tid < 64) {
@@ -391,13 +390,11 @@ __device__ __forceinline__ void fused_tail(Shared<kSlots>& sh, const Eval16Table
     const float cbv = tid < m ? sh.book[tid] : __builtin_huge_valf();
     __syncthreads();  // the quantizer's tables reuse the phase memory
     // the block's codes (kept in registers until the block's word offset is
-    // known), from its data read again (just read: from the cache) in the
-    // quantizer's 256-thread layout, chunks tid and 256 + tid
-    const __half* src = r < nb0 ? x0 : x1;
-    const int64_t e_base = (r < nb0 ? r : r - nb0) * 4096;
+    // known), from the data the thread loaded for scoring: its entries are
+    // the quantizer's 256-thread chunks tid and 256 + tid
     uint4 all[2][2] = {};
-    load_raw8<KVQ_F16>(src, e_base + 8 * tid, all[0]);
-    load_raw8<KVQ_F16>(src, e_base + 8 * (tid + kT), all[1]);
+    all[0][0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    all[1][0] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
     uint32_t bits[2] = {0u, 0u};
     const int w = quantize_block4096<kT, KVQ_F16, true>(sh.u.q, r, kMaxS, cbv, m, 0, all, nullptr, 0, fa.k0,
                                                         fa.k1, nullptr, bits);
@@ -915,7 +912,7 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         Hout[c * R + r] = hout;
         if (kFused) pc.chh[c] = hout;
     }
-    if constexpr (kFused) fused_tail(sh, tb, fa, ws, r, R, x0, x1, nb0);
+    if constexpr (kFused) fused_tail(sh, tb, fa, ws, r, R, hw);
 }
 
 // The kernel's tables: distinct uniform fractions, lane layout of the
