@@ -1,7 +1,8 @@
-// A block's choice among the grid candidates at a known multiplier, shared
-// by the solve (kvq_solve.hip) and the one-launch decode admission
-// (kvq_eval16.hip): the objective, the fixed-point rate and the chosen
-// codebook's points.
+// A block's choice among the grid candidates at a known multiplier: the
+// objective and the fixed-point rate (shared by the solve, kvq_solve.hip,
+// and the one-launch decode admission, kvq_eval16.hip) and the chosen
+// codebook's points (the solve; the one-launch admission computes the same
+// points one per lane).
 //
 // Page "Rate-adaptive KV-cache quantizer", Key formulas (2): at a fixed
 // multiplier each block minimises D_r + lambda d_r H_r on its own;
