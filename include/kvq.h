@@ -238,8 +238,12 @@ kvq_status kvq_solve_lambda_weighted(const kvq_plan* p, const double* D, const d
    and fixed-width packing (Key formulas (3); Implementation notes).  The
    draw of entry t of block r is Philox4x32-10 with key (seed lo, seed hi),
    counter (t >> 2, r lo, r hi, 0), word t & 3, u = (word >> 8) 2^-24; the
-   code is i+1 when u < p = (x - q_i)/(q_{i+1} - q_i), else i.  Codes are a
-   little-endian bit stream, block r starting at word word_off[r].
+   code is i+1 when u < p = (x - q_i)/(q_{i+1} - q_i), else i.  Every
+   entry must lie in [q_0, q_{m_r - 1}] of its block's codebook, as it does
+   for the codebooks kvq_solve_lambda writes (their end points are the
+   block's minimum and maximum); the codes of entries outside it are
+   unspecified.  Codes are a little-endian bit stream, block r starting at
+   word word_off[r].
    codes_capacity_words must be >= plan.max_code_words (KVQ_ENOSPC).
    Asynchronous. */
 kvq_status kvq_quantize_pack(const kvq_plan* p, const kvq_tensor* t, int32_t n_tensors,
