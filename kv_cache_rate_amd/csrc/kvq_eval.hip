@@ -36,46 +36,97 @@ hipError_t launch_ws_reset(void* ws, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Load block r into LDS as order-preserving keys (padding keys sort last),
-// flag non-finite entries, and sort ascending.
-__device__ void load_and_sort(const Geom& g, int64_t r, int NP, uint32_t* keys, WsHeader* ws) {
+// Bitonic sort of one block's NP keys (NP a power of two), thread t
+// holding positions [E t, E t + E) in registers.  A stage whose partner
+// distance j is below E stays inside the thread; one with j below 64 E
+// exchanges across the wave by lane shuffles; only the stages with j >= 64 E
+// (two or three per sort) pass through LDS and a barrier.
+template <int E>
+__device__ void bitonic_regs(uint32_t (&v)[E], int NP, uint32_t* buf) {
+    const int t = threadIdx.x;
+    for (int k = 2; k <= NP; k <<= 1) {
+        for (int j = k >> 1; j >= E; j >>= 1) {
+            // partner of position E t + e is E (t ^ tj) + e; the pair takes
+            // the direction of its lower position, (E t) & k (k > j >= E)
+            const int tj = j / E;
+            const bool take_min = ((t & tj) == 0) == (((E * t) & k) == 0);
+            uint32_t p[E];
+            if (tj < 64) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) p[e] = __shfl_xor(v[e], tj, 64);
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) buf[E * t + e] = v[e];
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < E; ++e) p[e] = buf[E * (t ^ tj) + e];
+                __syncthreads();
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[e] = take_min ? min(v[e], p[e]) : max(v[e], p[e]);
+        }
+#pragma unroll
+        for (int jj = E / 2; jj >= 1; jj >>= 1) {
+            if (jj < k) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    if ((e & jj) == 0) {
+                        const bool asc = ((E * t + e) & k) == 0;
+                        const uint32_t a = v[e], b = v[e | jj];
+                        const uint32_t lo = min(a, b), hi = max(a, b);
+                        v[e] = asc ? lo : hi;
+                        v[e | jj] = asc ? hi : lo;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Load block r as order-preserving keys (padding keys sort last), flag
+// non-finite entries, sort ascending, and leave the sorted values in LDS
+// as fp32 (position i at xs[i], i < NP).
+template <int E>
+__device__ void load_and_sort_e(const Geom& g, int64_t r, int NP, uint32_t* keys, WsHeader* ws) {
     int ti;
     const int64_t base = block_base(g, r, ti);
     const int n = g.n;
+    const int t0 = E * (int)threadIdx.x;
+    uint32_t v[E];
     bool bad = false;
-    for (int t = threadIdx.x; t < NP; t += blockDim.x) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
         uint32_t k = 0xffffffffu;
-        if (t < n) {
-            float v = load_entry(g, ti, base + entry_off(g, ti, t));
-            if (v == 0.0f) v = 0.0f;  // -0 -> +0
-            if (!isfinite(v)) bad = true;
-            k = f32_key(v);
+        if (t0 + e < n) {
+            float x = load_entry(g, ti, base + entry_off(g, ti, t0 + e));
+            if (x == 0.0f) x = 0.0f;  // -0 -> +0
+            if (!isfinite(x)) bad = true;
+            k = f32_key(x);
         }
-        keys[t] = k;
+        v[e] = k;
     }
     if (__syncthreads_or(bad)) {
         if (threadIdx.x == 0) atomicOr(&ws->status, kStatusNonFinite);
     }
-    for (int k = 2; k <= NP; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < NP; i += blockDim.x) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const uint32_t a = keys[i];
-                    const uint32_t b = keys[ixj];
-                    const bool up = (i & k) == 0;
-                    if ((a > b) == up) {
-                        keys[i] = b;
-                        keys[ixj] = a;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
+    bitonic_regs<E>(v, NP, keys);
     float* xs = reinterpret_cast<float*>(keys);
-    for (int t = threadIdx.x; t < NP; t += blockDim.x) xs[t] = key_f32(keys[t]);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (t0 + e < NP) xs[t0 + e] = key_f32(v[e]);
     __syncthreads();
+}
+
+// NP = next power of two of the block size, 2 .. kMaxBlock; each of the
+// kEvalThreads threads holds NP / kEvalThreads keys (at least one).
+__device__ void load_and_sort(const Geom& g, int64_t r, int NP, uint32_t* keys, WsHeader* ws) {
+    static_assert(kMaxBlock == 16 * kEvalThreads, "16 keys per thread at most");
+    switch (NP / kEvalThreads) {
+        case 16: load_and_sort_e<16>(g, r, NP, keys, ws); break;
+        case 8: load_and_sort_e<8>(g, r, NP, keys, ws); break;
+        case 4: load_and_sort_e<4>(g, r, NP, keys, ws); break;
+        case 2: load_and_sort_e<2>(g, r, NP, keys, ws); break;
+        default: load_and_sort_e<1>(g, r, NP, keys, ws); break;
+    }
 }
 
 __device__ __forceinline__ double wave_incl_scan(double v) {
