@@ -320,6 +320,16 @@ final_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
 
 __device__ __forceinline__ double hbits(double p) { return p > 0.0 ? -p * log2(p) : 0.0; }
 
+// Triples i < j < l of an M-point alphabet: those of pair (j, l) are
+// i = 0 .. j - 1 from tri_base(j, l), pairs in their triangle order, so
+// tri_base(j, l) = S(j) + j (l - j - 1) with S(j) = sum over j' < j of
+// j' (M - 1 - j').
+__host__ __device__ __forceinline__ int n_triples(int M) { return M * (M - 1) * (M - 2) / 6; }
+__device__ __forceinline__ int tri_first(int j, int M) {
+    return (M - 1) * j * (j - 1) / 2 - (j - 1) * j * (2 * j - 1) / 6;
+}
+__device__ __forceinline__ int tri_base(int j, int l, int M) { return tri_first(j, M) + j * (l - j - 1); }
+
 constexpr int kDpThreads = 256;
 // beam arrivals at one destination, (l - 1) width <= 30 x 8, over 64 lanes
 constexpr int kArrivalsPerLane = ((kAlpha - 2) * kMaxBeam + 63) / 64;
@@ -338,9 +348,14 @@ constexpr int kArrivalsPerLane = ((kAlpha - 2) * kMaxBeam + 63) / 64;
 // double-buffered in LDS; the chain's points ride along as a bitmask.
 // LDS of one alphabet-search workgroup, carved from dynamic shared memory
 // and sized by the alphabet (P pairs) and the beam width W (0: the DP):
-//   Dp, ML, MR [P] (fp64)  pair statistics
-//   DP:   f[2][P] (fp64), mk[2][P] (u32)       two layers of chain costs / masks
-//   beam: cand[P][W] (fp64), g[2][M][W], cnt[2][M]  arrivals and kept groups
+//   Dp [P] (fp64)  pair distortions
+//   DP:   hl, hr [P], h3 [T] (fp64)  entropy terms, independent of the
+//         multiplier: h(ML(j,l)/n), h(MR(j,l)/n) and, for every triple
+//         i < j < l, h((MR(i,j) + ML(j,l))/n) (T = M(M-1)(M-2)/6 triples,
+//         those of pair (j, l) consecutive from tri_base(j, l));
+//         f[2][P] (fp64), mk[2][P] (u32)       two layers of chain costs / masks
+//   beam: ML, MR [P] (fp64) pair masses; cand[P][W] (fp64), g[2][M][W],
+//         cnt[2][M]  arrivals and kept groups
 //   A[M] (fp32) distinct alphabet, m (its size)
 struct BeamEntry {
     double cost;
@@ -349,7 +364,7 @@ struct BeamEntry {
 };
 
 struct AlphaLds {
-    double *Dp, *ML, *MR, *f, *cand;
+    double *Dp, *ML, *MR, *hl, *hr, *h3, *f, *cand;
     uint32_t* mk;
     BeamEntry* g;
     int* cnt;
@@ -357,7 +372,13 @@ struct AlphaLds {
     int* m;
 };
 
-__host__ __device__ inline size_t alpha_lds_bytes(int M, int W, AlphaLds* v, unsigned char* base) {
+// The DP keeps its entropy terms in tables while its LDS stays within
+// kDpTableLds (at least five workgroups per CU); with larger alphabets
+// (32 points: a 39.7 KB triple table, two workgroups per CU) and in the
+// beam it evaluates them per transition.
+constexpr size_t kDpTableLds = 32768;
+
+__host__ __device__ inline size_t alpha_lds_layout(int M, int W, bool tab, AlphaLds* v, unsigned char* base) {
     const size_t P = (size_t)n_pairs(M);
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -367,8 +388,14 @@ __host__ __device__ inline size_t alpha_lds_bytes(int M, int W, AlphaLds* v, uns
     };
     AlphaLds t{};
     t.Dp = (double*)take(P * 8);
-    t.ML = (double*)take(P * 8);
-    t.MR = (double*)take(P * 8);
+    if (tab) {
+        t.hl = (double*)take(P * 8);
+        t.hr = (double*)take(P * 8);
+        t.h3 = (double*)take((size_t)n_triples(M) * 8 + 8);
+    } else {
+        t.ML = (double*)take(P * 8);
+        t.MR = (double*)take(P * 8);
+    }
     if (W == 0) {
         t.f = (double*)take(2 * P * 8);
         t.mk = (uint32_t*)take(2 * P * 4);
@@ -383,14 +410,54 @@ __host__ __device__ inline size_t alpha_lds_bytes(int M, int W, AlphaLds* v, uns
     return o;
 }
 
-// Load one block's pair statistics and distinct alphabet into LDS.
+__host__ __device__ inline bool alpha_dp_tables(int M, int W) {
+    return W == 0 && alpha_lds_layout(M, 0, true, nullptr, nullptr) <= kDpTableLds;
+}
+__host__ __device__ inline size_t alpha_lds_bytes(int M, int W, AlphaLds* v, unsigned char* base) {
+    return alpha_lds_layout(M, W, alpha_dp_tables(M, W), v, base);
+}
+
+// Alphabet searches, one kernel instance each (their register needs
+// differ): the beam, the DP evaluating its entropy terms per transition,
+// the DP reading them from tables.
+constexpr int kSearchBeam = 0, kSearchDp = 1, kSearchDpTables = 2;
+inline int alpha_search_kind(int M, int W) {
+    return W ? kSearchBeam : (alpha_dp_tables(M, W) ? kSearchDpTables : kSearchDp);
+}
+
+// Load one block's pair statistics and distinct alphabet into LDS.  The DP
+// takes its entropy terms from tables: each point frequency's term depends
+// on the point and its two neighbours only, not on the multiplier, so it is
+// evaluated once per triple here instead of once per transition and layer.
 __device__ void load_pairs(const AlphaLds& t, const double* __restrict__ Dg, const double* __restrict__ Mg,
-                           const float* __restrict__ st, int M) {
+                           const float* __restrict__ st, int M, int n) {
     const int P = n_pairs(M);
+    const double dn = (double)n;
     for (int p = threadIdx.x; p < P; p += blockDim.x) {
         t.Dp[p] = Dg[p];
-        t.ML[p] = Mg[2 * p];
-        t.MR[p] = Mg[2 * p + 1];
+        if (t.h3) {
+            t.hl[p] = hbits(Mg[2 * p] / dn);
+            t.hr[p] = hbits(Mg[2 * p + 1] / dn);
+        } else {
+            t.ML[p] = Mg[2 * p];
+            t.MR[p] = Mg[2 * p + 1];
+        }
+    }
+    if (t.h3) {
+        // triple x: find its middle point j (the S(j) it lies past), then
+        // l and i; points at or past the distinct count m carry zero masses
+        const int T = n_triples(M);
+        for (int x = threadIdx.x; x < T; x += blockDim.x) {
+            int j = 1, b = 0;
+            while (x >= b + j * (M - 1 - j)) {
+                b += j * (M - 1 - j);
+                ++j;
+            }
+            const int li = (x - b) / j;
+            const int i = x - b - li * j;
+            const int l = j + 1 + li;
+            t.h3[x] = hbits((Mg[2 * pair_index(i, j, M) + 1] + Mg[2 * pair_index(j, l, M)]) / dn);
+        }
     }
     if (threadIdx.x == 0) {
         int m = 0;
@@ -411,13 +478,16 @@ __device__ __forceinline__ void pair_of(int p, int M, int& j, int& l) {
     l = j + 1 + rem;
 }
 
+template <bool tab>  // entropy terms from the tables (t.h3 set) or evaluated per transition
 __device__ uint32_t dp_block(const AlphaLds& t, const double* __restrict__ Dg, const double* __restrict__ Mg,
                              const float* __restrict__ st, int M, int smax, int n, double w) {
+    // each cost is formed as written, (f + D) + w h, each step rounded
+#pragma clang fp contract(off)
     const int tid = threadIdx.x;
     const int P = n_pairs(M);
     const double dn = (double)n;
     const double INF = __builtin_huge_val();
-    load_pairs(t, Dg, Mg, st, M);
+    load_pairs(t, Dg, Mg, st, M, n);
     for (int p = tid; p < P; p += blockDim.x) {
         t.f[p] = INF;
         t.mk[p] = 0u;
@@ -427,7 +497,7 @@ __device__ uint32_t dp_block(const AlphaLds& t, const double* __restrict__ Dg, c
     if (m <= 1) return 1u;
     for (int l = 1 + tid; l < m; l += blockDim.x) {
         const int p = pair_index(0, l, M);
-        t.f[p] = t.Dp[p] + w * hbits(t.ML[p] / dn);
+        t.f[p] = t.Dp[p] + w * (tab ? t.hl[p] : hbits(t.ML[p] / dn));
         t.mk[p] = 1u | (1u << l);
     }
     double best = INF;  // wave 0's running completion
@@ -445,7 +515,7 @@ __device__ uint32_t dp_block(const AlphaLds& t, const double* __restrict__ Dg, c
             if (tid < m - 1) {
                 const int p = pair_index(tid, m - 1, M);
                 const double fv = fc[p];
-                if (fv < INF) tot = fv + w * hbits(t.MR[p] / dn);
+                if (fv < INF) tot = fv + w * (tab ? t.hr[p] : hbits(t.MR[p] / dn));
             }
             double mn = tot;
             for (int o = 32; o > 0; o >>= 1) mn = fmin(mn, __shfl_xor(mn, o, 64));
@@ -468,12 +538,15 @@ __device__ uint32_t dp_block(const AlphaLds& t, const double* __restrict__ Dg, c
             double bv = INF;
             uint32_t bm = 0u;
             if (j >= 1 && l < m) {
-                const double Djl = t.Dp[p], MLjl = t.ML[p];
+                const double Djl = t.Dp[p];
+                const double* h3 = tab ? t.h3 + tri_base(j, l, M) : nullptr;
+                const double MLjl = tab ? 0.0 : t.ML[p];
                 for (int i = 0; i < j; ++i) {
                     const int q = pair_index(i, j, M);
                     const double fv = fc[q];
                     if (fv < INF) {
-                        const double v = (fv + Djl) + w * hbits((t.MR[q] + MLjl) / dn);
+                        const double h = tab ? h3[i] : hbits((t.MR[q] + MLjl) / dn);
+                        const double v = (fv + Djl) + w * h;
                         if (v < bv) {
                             bv = v;
                             bm = mc[q];
@@ -513,7 +586,7 @@ __device__ uint32_t beam_block(const AlphaLds& t, const double* __restrict__ Dg,
     const int P = n_pairs(M);
     const double dn = (double)n;
     const double INF = __builtin_huge_val();
-    load_pairs(t, Dg, Mg, st, M);
+    load_pairs(t, Dg, Mg, st, M, n);
     __syncthreads();
     const int m = *t.m;
     if (m <= 1) return 1u;
@@ -665,6 +738,13 @@ __device__ double subset_entropy(const AlphaLds& t, int M, uint32_t mask, int n)
         if (mask & (1u << i)) pts[k++] = i;
     if (k <= 1) return 0.0;
     double Hs = 0.0;
+    if (t.h3) {  // the DP's tables hold exactly these terms
+        for (int q = 0; q < k; ++q)
+            Hs += q == 0       ? t.hl[pair_index(pts[0], pts[1], M)]
+                  : q == k - 1 ? t.hr[pair_index(pts[k - 2], pts[k - 1], M)]
+                               : t.h3[tri_base(pts[q], pts[q + 1], M) + pts[q - 1]];
+        return Hs;
+    }
     for (int q = 0; q < k; ++q) {
         double mass = 0.0;
         if (q > 0) mass += t.MR[pair_index(pts[q - 1], pts[q], M)];
@@ -674,14 +754,17 @@ __device__ double subset_entropy(const AlphaLds& t, int M, uint32_t mask, int n)
     return Hs;
 }
 
+template <int kSearch>
 __device__ __forceinline__ uint32_t alpha_search(const AlphaLds& t, const double* Dg, const double* Mg,
                                                  const float* st, int M, int smax, int width, int n,
                                                  double w) {
-    return width ? beam_block(t, Dg, Mg, st, M, smax, width, n, w) : dp_block(t, Dg, Mg, st, M, smax, n, w);
+    if constexpr (kSearch == kSearchBeam) return beam_block(t, Dg, Mg, st, M, smax, width, n, w);
+    else return dp_block<kSearch == kSearchDpTables>(t, Dg, Mg, st, M, smax, n, w);
 }
 
 // Rate of every multiplier of the pass: workgroup (block r, multiplier j);
 // width 0 runs the exact DP, else the beam.
+template <int kSearch>
 __global__ void __launch_bounds__(kDpThreads)
 rates_alpha_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr,
                    const float* __restrict__ stats, int64_t R, int alpha_m, int smax, int width, int n,
@@ -694,7 +777,7 @@ rates_alpha_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr
     const int64_t r = blockIdx.x;
     const int P = n_pairs(alpha_m);
     const double w = h->lam[j] * (double)n;
-    const uint32_t mask = alpha_search(t, Dp + r * P, Mlr + r * P * 2, stats + r * alpha_m, alpha_m, smax,
+    const uint32_t mask = alpha_search<kSearch>(t, Dp + r * P, Mlr + r * P * 2, stats + r * alpha_m, alpha_m, smax,
                                        width, n, w);
     if (threadIdx.x == 0) {
         const double Hs = subset_entropy(t, alpha_m, mask, n);
@@ -703,6 +786,7 @@ rates_alpha_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr
 }
 
 // The blocks' choice at the final multiplier: workgroup = block.
+template <int kSearch>
 __global__ void __launch_bounds__(kDpThreads)
 final_alpha_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr,
                    const float* __restrict__ stats, int64_t R, int alpha_m, int smax, int width, int s,
@@ -725,7 +809,7 @@ final_alpha_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr
     alpha_lds_bytes(alpha_m, width, &t, lds);
     const int P = n_pairs(alpha_m);
     const double w = h->lam_final * (double)n;
-    const uint32_t mask = alpha_search(t, Dp + r * P, Mlr + r * P * 2, stats + r * alpha_m, alpha_m, smax,
+    const uint32_t mask = alpha_search<kSearch>(t, Dp + r * P, Mlr + r * P * 2, stats + r * alpha_m, alpha_m, smax,
                                        width, n, w);
     if (tid == 0) {
         const double Hs = subset_entropy(t, alpha_m, mask, n);
@@ -1282,6 +1366,7 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
     const unsigned lam_slots = (unsigned)std::max(std::max(dbl_n, (1 << bits_max) - 1), 2);
     const int width = p.search == KVQ_BEAM ? p.beam_width : 0;
     const size_t alpha_lds = grids ? 0 : alpha_lds_bytes(p.alphabet_m, width, nullptr, nullptr);
+    const int kind = grids ? kSearchDp : alpha_search_kind(p.alphabet_m, width);
     const unsigned grid = (unsigned)((R + kSolveThreads - 1) / kSolveThreads);
     // exact DP: one thread per pair state, in whole waves
     const int dp_pairs = p.search != KVQ_GRIDS ? n_pairs(p.alphabet_m) : 0;
@@ -1293,7 +1378,10 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
             hipLaunchKernelGGL(rates_grids_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, wgt,
                                R, p.n_cand, (double)n, shift, h);
         } else {
-            hipLaunchKernelGGL(rates_alpha_kernel, dim3((unsigned)R, lam_slots), dim3(dp_threads), alpha_lds,
+            const auto k = kind == kSearchBeam ? rates_alpha_kernel<kSearchBeam>
+                         : kind == kSearchDp   ? rates_alpha_kernel<kSearchDp>
+                                               : rates_alpha_kernel<kSearchDpTables>;
+            hipLaunchKernelGGL(k, dim3((unsigned)R, lam_slots), dim3(dp_threads), alpha_lds,
                                st, D, H, stats, R, p.alphabet_m, p.s, width, n, shift, h);
         }
         hipLaunchKernelGGL(solve_select_kernel, dim3(1), dim3(64), 0, st, h);
@@ -1321,7 +1409,10 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
         hipLaunchKernelGGL(final_grids_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, wgt, stats,
                            R, p.n_cand, p.s, n, shift, rt, h, choice, codebook, m, off);
     } else {
-        hipLaunchKernelGGL(final_alpha_kernel, dim3((unsigned)R), dim3(dp_threads), alpha_lds, st, D, H,
+        const auto k = kind == kSearchBeam ? final_alpha_kernel<kSearchBeam>
+                     : kind == kSearchDp   ? final_alpha_kernel<kSearchDp>
+                                           : final_alpha_kernel<kSearchDpTables>;
+        hipLaunchKernelGGL(k, dim3((unsigned)R), dim3(dp_threads), alpha_lds, st, D, H,
                            stats, R, p.alphabet_m, p.s, width, p.s, n, shift, h, choice, codebook, m, off);
     }
     if (mode == KVQ_BISECT_GREEDY && p.search == KVQ_GRIDS) {
