@@ -53,6 +53,21 @@ def test_slice_full_oracle(B):
     assert g["lam"] > 0.0 and np.all(g["m"] <= WL.s) and np.all(g["m"] >= 2)
 
 
+@pytest.mark.parametrize("M", [24, 25])
+def test_slice_table_boundary(M):
+    """Alphabets of 24 points (the largest whose DP keeps its entropy terms
+    in LDS tables) and 25 (the smallest that evaluates them per
+    transition), on the 32-block slice against the whole oracle."""
+    x = np.ascontiguousarray(W.generate(WL)[0][:, :1, :1024, :])
+    kw = _kw(B=2.0, alphabet_m=M)
+    g = parity.run_gpu([x], **kw)
+    o = parity.run_oracle([x], **kw)
+    assert o["route"] == "dp"
+    rep = parity.full_compare(g, o, "exact_dp", kw["seed"], kw["B"], "bisect")
+    _say(f"slice M={M}: {rep}")
+    assert g["lam"] > 0.0
+
+
 def test_ties_and_constant_blocks():
     """Values on a 0.1 grid (fewer than 32 distinct quantiles per block) and
     one constant block (a single level, no codes)."""

@@ -142,6 +142,22 @@ def test_ragged_small_blocks(dtype):
     _check(w, [x])
 
 
+@pytest.mark.parametrize("T,D,dtype,kind", [(5, 40, np.float32, "normal"), (10, 30, np.float16, "ties"),
+                                              (8, 125, np.float32, "normal"), (12, 128, np.float16, "normal"),
+                                              (31, 128, np.float32, "ties")])
+def test_generic_sort_block_sizes(T, D, dtype, kind):
+    """The generic kernels' register sort at every keys-per-thread count:
+    blocks of 200, 300, 1000, 1536 and 3968 entries (padded to 256, 512,
+    1024, 2048 and 4096 keys: 1, 2, 4, 8 and 16 per thread), with tied data
+    in two of them, against the oracle."""
+    rng = np.random.default_rng(7 + T * D)
+    x = _small(dtype, (2, 3, 2 * T, 2 * D), rng, kind)
+    w = W.Workload(name=f"sort{T}x{D}", index=0, tensors=(("K", x.shape),),
+                   dtype="f16" if dtype == np.float16 else "f32",
+                   tokens_per_block=T, dims_per_block=D, s=16, search="grids", B=1.7, mode="bisect")
+    _check(w, [x])
+
+
 @pytest.mark.parametrize("mode", ["bisect", "subgrad"])
 @pytest.mark.parametrize("heads", [64, 65])
 def test_final_pass_block_count_edges(heads, mode):
