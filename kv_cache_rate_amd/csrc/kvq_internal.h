@@ -19,6 +19,11 @@ constexpr int kAlpha = KVQ_MAX_ALPHABET;             // 32
 constexpr int kMaxPairs = kAlpha * (kAlpha - 1) / 2; // 496
 constexpr int kMaxBeam = KVQ_MAX_BEAM;                // 8
 constexpr int kMaxLam = 64;                       // multipliers per solve pass
+constexpr int kStripedLam = 8;                     // multipliers per alphabet-search pass
+// Same-address atomics from every workgroup serialise (about 11 ns each
+// here: 2048 of them cost a 12-point alphabet-search pass 22 us of its 44),
+// so those passes spread their rate sums over this many addresses.
+constexpr int kRateStripes = 16;
 
 // Device status bits (workspace header).
 constexpr uint32_t kStatusNonFinite = 1u;
@@ -45,6 +50,10 @@ struct WsHeader {
     uint64_t Btot_fx;    // budget in the same fixed point
     double lam[kMaxLam + 8];
     unsigned long long sums[kMaxLam + 8];
+    // an alphabet-search pass (at most kStripedLam multipliers) adds its
+    // blocks' rates into kRateStripes accumulators per multiplier, chosen by
+    // workgroup; the pass's select folds them into sums
+    unsigned long long asums[kStripedLam][kRateStripes];
     uint32_t pool_n;          // greedy post-pass: upgrades collected
     uint32_t pool_overflow;   // 1 if they exceeded the pool
     uint32_t swaps;           // upgrades applied

@@ -46,6 +46,8 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
 
 __global__ void solve_init_kernel(WsHeader* h, int mode, double lam_in, unsigned long long Btot_fx,
                                   int iters, int bits_max, int dbl_n) {
+    for (int i = threadIdx.x; i < kStripedLam * kRateStripes; i += blockDim.x)
+        h->asums[i / kRateStripes][i % kRateStripes] = 0ull;
     if (threadIdx.x != 0) return;
     h->done = 0;
     h->err = 0;
@@ -87,8 +89,22 @@ __device__ void setup_multisection(WsHeader* h) {
     h->phase = kPhaseMulti;
 }
 
-__global__ void solve_select_kernel(WsHeader* h) {
-    if (threadIdx.x != 0 || h->done) return;
+// striped: the pass was an alphabet search, whose rates sit in asums.
+__global__ void solve_select_kernel(WsHeader* h, int striped) {
+    if (h->done) return;
+    if (striped) {
+        const int j = threadIdx.x;
+        if (j < kStripedLam) {
+            unsigned long long t = 0;
+            for (int k = 0; k < kRateStripes; ++k) {
+                t += h->asums[j][k];
+                h->asums[j][k] = 0ull;
+            }
+            h->sums[j] += t;
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x != 0) return;
     const unsigned long long B = h->Btot_fx;
     switch (h->phase) {
     case kPhaseZero:
@@ -459,11 +475,17 @@ __device__ void load_pairs(const AlphaLds& t, const double* __restrict__ Dg, con
             t.h3[x] = hbits((Mg[2 * pair_index(i, j, M) + 1] + Mg[2 * pair_index(j, l, M)]) / dn);
         }
     }
-    if (threadIdx.x == 0) {
-        int m = 0;
-        for (int j = 0; j < M; ++j)
-            if (m == 0 || st[j] != t.A[m - 1]) t.A[m++] = st[j];
-        *t.m = m;
+    // distinct alphabet: the M order statistics are non-decreasing, so a
+    // point is new unless it equals the one before; wave 0 keeps lane j's
+    // point at the count of kept lanes below it (M <= 32)
+    if (threadIdx.x < 64) {
+        const int j = threadIdx.x;
+        const float v = j < M ? st[j] : 0.0f;
+        const float prev = __shfl_up(v, 1, 64);
+        const bool keep = j < M && (j == 0 || v != prev);
+        const unsigned long long kb = __ballot(keep);
+        if (keep) t.A[__popcll(kb & ((1ull << j) - 1ull))] = v;
+        if (j == 0) *t.m = __popcll(kb);
     }
 }
 
@@ -478,16 +500,15 @@ __device__ __forceinline__ void pair_of(int p, int M, int& j, int& l) {
     l = j + 1 + rem;
 }
 
+// The block's tables are in LDS (load_pairs, then a barrier).
 template <bool tab>  // entropy terms from the tables (t.h3 set) or evaluated per transition
-__device__ uint32_t dp_block(const AlphaLds& t, const double* __restrict__ Dg, const double* __restrict__ Mg,
-                             const float* __restrict__ st, int M, int smax, int n, double w) {
+__device__ uint32_t dp_block(const AlphaLds& t, int M, int smax, int n, double w) {
     // each cost is formed as written, (f + D) + w h, each step rounded
 #pragma clang fp contract(off)
     const int tid = threadIdx.x;
     const int P = n_pairs(M);
     const double dn = (double)n;
     const double INF = __builtin_huge_val();
-    load_pairs(t, Dg, Mg, st, M, n);
     for (int p = tid; p < P; p += blockDim.x) {
         t.f[p] = INF;
         t.mk[p] = 0u;
@@ -580,14 +601,11 @@ __device__ __forceinline__ bool lex_before(uint32_t a, uint32_t b) {
 //   the arrivals at its destination that precede it and the `width` first
 //   take the next layer's group; wave 0 picks the best completion
 //   (destination m - 1).
-__device__ uint32_t beam_block(const AlphaLds& t, const double* __restrict__ Dg, const double* __restrict__ Mg,
-                               const float* __restrict__ st, int M, int smax, int width, int n, double w) {
+__device__ uint32_t beam_block(const AlphaLds& t, int M, int smax, int width, int n, double w) {
     const int tid = threadIdx.x;
     const int P = n_pairs(M);
     const double dn = (double)n;
     const double INF = __builtin_huge_val();
-    load_pairs(t, Dg, Mg, st, M, n);
-    __syncthreads();
     const int m = *t.m;
     if (m <= 1) return 1u;
     auto grp = [&](int layer, int l) { return t.g + ((size_t)layer * M + l) * width; };
@@ -754,34 +772,49 @@ __device__ double subset_entropy(const AlphaLds& t, int M, uint32_t mask, int n)
     return Hs;
 }
 
+// One search at multiplier w / n over the block whose tables load_pairs
+// put in LDS (a barrier between; the previous search, if any, finished).
 template <int kSearch>
-__device__ __forceinline__ uint32_t alpha_search(const AlphaLds& t, const double* Dg, const double* Mg,
-                                                 const float* st, int M, int smax, int width, int n,
-                                                 double w) {
-    if constexpr (kSearch == kSearchBeam) return beam_block(t, Dg, Mg, st, M, smax, width, n, w);
-    else return dp_block<kSearch == kSearchDpTables>(t, Dg, Mg, st, M, smax, n, w);
+__device__ __forceinline__ uint32_t alpha_search(const AlphaLds& t, int M, int smax, int width, int n, double w) {
+    if constexpr (kSearch == kSearchBeam) return beam_block(t, M, smax, width, n, w);
+    else return dp_block<kSearch == kSearchDpTables>(t, M, smax, n, w);
 }
 
-// Rate of every multiplier of the pass: workgroup (block r, multiplier j);
-// width 0 runs the exact DP, else the beam.
+// Rate of every multiplier of the pass (up to 8 per doubling pass, one per
+// bisection pass).  The DP with tables runs one workgroup per block, which
+// loads the tables once and searches at the multipliers in turn: its
+// searches are short and share the tables.  The others (each search costs
+// far more than the load) run one workgroup per block and multiplier y.
+// Width 0 runs the exact DP, else the beam.
 template <int kSearch>
 __global__ void __launch_bounds__(kDpThreads)
 rates_alpha_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr,
                    const float* __restrict__ stats, int64_t R, int alpha_m, int smax, int width, int n,
                    int shift, WsHeader* h) {
     extern __shared__ __align__(16) unsigned char lds[];
-    const int j = blockIdx.y;
-    if (h->done || j >= h->nlam) return;
+    const int nlam = h->nlam;
+    if (h->done || (int)blockIdx.y >= nlam) return;
     AlphaLds t;
     alpha_lds_bytes(alpha_m, width, &t, lds);
     const int64_t r = blockIdx.x;
     const int P = n_pairs(alpha_m);
-    const double w = h->lam[j] * (double)n;
-    const uint32_t mask = alpha_search<kSearch>(t, Dp + r * P, Mlr + r * P * 2, stats + r * alpha_m, alpha_m, smax,
-                                       width, n, w);
-    if (threadIdx.x == 0) {
-        const double Hs = subset_entropy(t, alpha_m, mask, n);
-        atomicAdd(&h->sums[j], rate_fx((double)n, Hs, shift));
+    load_pairs(t, Dp + r * P, Mlr + r * P * 2, stats + r * alpha_m, alpha_m, n);
+    auto search = [&](int j) {
+        const double w = h->lam[j] * (double)n;
+        const uint32_t mask = alpha_search<kSearch>(t, alpha_m, smax, width, n, w);
+        if (threadIdx.x == 0) {
+            const double Hs = subset_entropy(t, alpha_m, mask, n);
+            atomicAdd(&h->asums[j][blockIdx.x % kRateStripes], rate_fx((double)n, Hs, shift));
+        }
+    };
+    if constexpr (kSearch == kSearchDpTables) {
+        for (int j = 0; j < nlam; ++j) {
+            __syncthreads();  // tables loaded; the previous search done with its layers
+            search(j);
+        }
+    } else {  // one multiplier per workgroup (a loop here costs these kernels registers)
+        __syncthreads();
+        search(blockIdx.y);
     }
 }
 
@@ -809,8 +842,9 @@ final_alpha_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr
     alpha_lds_bytes(alpha_m, width, &t, lds);
     const int P = n_pairs(alpha_m);
     const double w = h->lam_final * (double)n;
-    const uint32_t mask = alpha_search<kSearch>(t, Dp + r * P, Mlr + r * P * 2, stats + r * alpha_m, alpha_m, smax,
-                                       width, n, w);
+    load_pairs(t, Dp + r * P, Mlr + r * P * 2, stats + r * alpha_m, alpha_m, n);
+    __syncthreads();
+    const uint32_t mask = alpha_search<kSearch>(t, alpha_m, smax, width, n, w);
     if (tid == 0) {
         const double Hs = subset_entropy(t, alpha_m, mask, n);
         atomicAdd(&h->rate_final, rate_fx((double)n, Hs, shift));
@@ -1349,7 +1383,7 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
     // probes) per pass: fewer evaluations, more passes.
     const bool grids = p.search == KVQ_GRIDS;
     const int bits_max = grids ? 6 : 1;
-    const int dbl_n = grids ? kMaxLam - 1 : 8;
+    const int dbl_n = grids ? kMaxLam - 1 : kStripedLam;  // alphabet passes: at most kStripedLam multipliers
     // few blocks (a decode step): choice, rate and offsets in two small
     // launches (launch_final_small), the result written to `out`
     const bool small = grids && R >= 1 && R <= kSmallR && mode != KVQ_BISECT_GREEDY;
@@ -1361,9 +1395,6 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
     }
     hipLaunchKernelGGL(solve_init_kernel, dim3(1), dim3(64), 0, st, h, mode, lam_in, Btot_fx, iters,
                        bits_max, dbl_n);
-    // workgroups per block in an alphabet-search pass: the most multipliers
-    // any pass probes
-    const unsigned lam_slots = (unsigned)std::max(std::max(dbl_n, (1 << bits_max) - 1), 2);
     const int width = p.search == KVQ_BEAM ? p.beam_width : 0;
     const size_t alpha_lds = grids ? 0 : alpha_lds_bytes(p.alphabet_m, width, nullptr, nullptr);
     const int kind = grids ? kSearchDp : alpha_search_kind(p.alphabet_m, width);
@@ -1381,10 +1412,11 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
             const auto k = kind == kSearchBeam ? rates_alpha_kernel<kSearchBeam>
                          : kind == kSearchDp   ? rates_alpha_kernel<kSearchDp>
                                                : rates_alpha_kernel<kSearchDpTables>;
-            hipLaunchKernelGGL(k, dim3((unsigned)R, lam_slots), dim3(dp_threads), alpha_lds,
+            const unsigned ys = kind == kSearchDpTables ? 1u : (unsigned)kStripedLam;
+            hipLaunchKernelGGL(k, dim3((unsigned)R, ys), dim3(dp_threads), alpha_lds,
                                st, D, H, stats, R, p.alphabet_m, p.s, width, n, shift, h);
         }
-        hipLaunchKernelGGL(solve_select_kernel, dim3(1), dim3(64), 0, st, h);
+        hipLaunchKernelGGL(solve_select_kernel, dim3(1), dim3(64), 0, st, h, grids ? 0 : 1);
     };
     if (mode == KVQ_BISECT || mode == KVQ_BISECT_GREEDY) {
         // lambda = 0 first; the bracket passes run only when it is infeasible
