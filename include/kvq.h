@@ -28,7 +28,7 @@
  *     per calling thread (hipHostMalloc on first use, kept until the process
  *     ends) through which the synchronising calls read back their small
  *     results (for up to 1024 grid-search blocks the solve's last kernel
- *     writes them into it directly), and the 32 KB static device scratch of
+ *     writes them into it directly), and the 44 KB static device scratch of
  *     kvq_admit_noalloc (one per GPU, part of the loaded code object).  Sizes
  *     of every buffer come from kvq_plan (filled by kvq_plan_blocks).
  *   - Host pointers are marked "(host)".
@@ -273,7 +273,7 @@ kvq_status kvq_admit(const kvq_plan* p, const kvq_tensor* t, int32_t n_tensors, 
 /* kvq_admit without a workspace argument and without any allocation, for
    callers that cannot allocate device or pinned memory (code under HIP graph
    capture, tight serving loops, harnesses that forbid hipMalloc).  The
-   solve's workspace is a static device array of the library (32 KB per GPU,
+   solve's workspace is a static device array of the library (44 KB per GPU,
    held by each GPU the library runs on until the process ends), so plans of
    at most 3,668,992 blocks are accepted (KVQ_ENOSPC beyond, with nothing
    launched).  Results are read back with a plain copy into the caller's host

@@ -351,7 +351,7 @@ kvq_status solve_result(const kvq_plan* p, double B, int32_t mode, double eta, d
         if (e == hipSuccess) memcpy(&hdr, ss.out, sizeof hdr);
     } else {
         kvq::WsHeader full;
-        e = kvq::read_back(&full, workspace, sizeof full, s, ss.staging);
+        e = kvq::read_back(&full, workspace, kvq::kWsHeaderReadBytes, s, ss.staging);
         hdr.status = full.status;
         hdr.err = full.err;
         hdr.pool_overflow = full.pool_overflow;
@@ -602,7 +602,7 @@ kvq_status kvq_ans_encode(const kvq_plan* p, const uint32_t* codes, const uint8_
     if (e != hipSuccess) return hip_fail(e, "entropy-coding launch");
     kvq::WsHeader hdr;
     uint64_t total = 0;
-    e = kvq::read_back(&hdr, workspace, sizeof hdr, s);
+    e = kvq::read_back(&hdr, workspace, kvq::kWsHeaderReadBytes, s);
     if (e == hipSuccess) e = kvq::read_back(&total, block_off + p->n_blocks, sizeof total, s);
     if (e != hipSuccess) return hip_fail(e, "entropy-coding read-back");
     if (hdr.status & kvq::kStatusAnsOverflow) return fail(KVQ_ENOSPC, "a coded block outgrew its scratch region");

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "kvq.h"
@@ -19,10 +20,10 @@ constexpr int kAlpha = KVQ_MAX_ALPHABET;             // 32
 constexpr int kMaxPairs = kAlpha * (kAlpha - 1) / 2; // 496
 constexpr int kMaxBeam = KVQ_MAX_BEAM;                // 8
 constexpr int kMaxLam = 64;                       // multipliers per solve pass
-constexpr int kStripedLam = 8;                     // multipliers per alphabet-search pass
+constexpr int kAlphaLam = 8;                       // multipliers per alphabet-search pass
 // Same-address atomics from every workgroup serialise (about 11 ns each
 // here: 2048 of them cost a 12-point alphabet-search pass 22 us of its 44),
-// so those passes spread their rate sums over this many addresses.
+// so the solve's rate sums are spread over this many addresses each.
 constexpr int kRateStripes = 16;
 
 // Device status bits (workspace header).
@@ -50,17 +51,23 @@ struct WsHeader {
     uint64_t Btot_fx;    // budget in the same fixed point
     double lam[kMaxLam + 8];
     unsigned long long sums[kMaxLam + 8];
-    // an alphabet-search pass (at most kStripedLam multipliers) adds its
-    // blocks' rates into kRateStripes accumulators per multiplier, chosen by
-    // workgroup; the pass's select folds them into sums
-    unsigned long long asums[kStripedLam][kRateStripes];
     uint32_t pool_n;          // greedy post-pass: upgrades collected
     uint32_t pool_overflow;   // 1 if they exceeded the pool
     uint32_t swaps;           // upgrades applied
     uint32_t pad1;
     uint64_t part_rate[16];   // few-block final pass: fixed-point rate per workgroup
+    // (the host reads the header up to here)
+    // a rates pass adds its blocks' rates into kRateStripes accumulators
+    // per multiplier, chosen by workgroup, and the pass's select folds them
+    // into sums; the final pass likewise into rate_part, folded into
+    // rate_final by fold_rate_kernel
+    unsigned long long rsum[kMaxLam][kRateStripes];
+    unsigned long long rate_part[kRateStripes];
 };
-constexpr size_t kWsHeaderBytes = 4096;
+// bytes of the header the host reads back after a solve
+constexpr size_t kWsHeaderReadBytes = offsetof(WsHeader, rsum);
+static_assert(kWsHeaderReadBytes <= 8192, "solve read-back fits the staging buffer");
+constexpr size_t kWsHeaderBytes = 16384;
 constexpr uint32_t kGreedyPool = 16384;  // (block, candidate) pairs in the workspace pool
 // workspace = header, scan tile sums, greedy pool (8 bytes per pair)
 __host__ __device__ inline size_t ws_pool_offset(int64_t R) {
@@ -70,7 +77,7 @@ __host__ __device__ inline size_t ws_pool_offset(int64_t R) {
 static_assert(sizeof(WsHeader) <= kWsHeaderBytes, "workspace header");
 // Static device scratch of kvq_admit_noalloc: header plus scan tile sums
 // (no greedy pool), enough for ws_pool_offset(R) with R up to 3,668,992.
-constexpr size_t kNoAllocScratchBytes = 32768;
+constexpr size_t kNoAllocScratchBytes = 45056;
 
 // Block geometry as the kernels see it (passed by value).
 struct Geom {

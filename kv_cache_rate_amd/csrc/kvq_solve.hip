@@ -46,8 +46,9 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
 
 __global__ void solve_init_kernel(WsHeader* h, int mode, double lam_in, unsigned long long Btot_fx,
                                   int iters, int bits_max, int dbl_n) {
-    for (int i = threadIdx.x; i < kStripedLam * kRateStripes; i += blockDim.x)
-        h->asums[i / kRateStripes][i % kRateStripes] = 0ull;
+    for (int i = threadIdx.x; i < kMaxLam * kRateStripes; i += blockDim.x)
+        h->rsum[i / kRateStripes][i % kRateStripes] = 0ull;
+    for (int i = threadIdx.x; i < kRateStripes; i += blockDim.x) h->rate_part[i] = 0ull;
     if (threadIdx.x != 0) return;
     h->done = 0;
     h->err = 0;
@@ -89,22 +90,32 @@ __device__ void setup_multisection(WsHeader* h) {
     h->phase = kPhaseMulti;
 }
 
-// striped: the pass was an alphabet search, whose rates sit in asums.
-__global__ void solve_select_kernel(WsHeader* h, int striped) {
-    if (h->done) return;
-    if (striped) {
-        const int j = threadIdx.x;
-        if (j < kStripedLam) {
-            unsigned long long t = 0;
-            for (int k = 0; k < kRateStripes; ++k) {
-                t += h->asums[j][k];
-                h->asums[j][k] = 0ull;
-            }
-            h->sums[j] += t;
-        }
-        __syncthreads();
+// rate_final += the final pass's striped rate sums (64 threads).
+__global__ void fold_rate_kernel(WsHeader* h) {
+    const int k = threadIdx.x;
+    unsigned long long v = 0;
+    if (k < kRateStripes) {
+        v = h->rate_part[k];
+        h->rate_part[k] = 0ull;
     }
-    if (threadIdx.x != 0) return;
+    v = wave_sum_u64(v);
+    if (k == 0) h->rate_final += v;
+}
+
+// 64 threads: lane j first folds multiplier j's rate stripes into sums[j]
+// (every lane, whether or not the pass probed j or ran at all: unused
+// stripes hold zeros, and the loads wait for nothing).
+__global__ void solve_select_kernel(WsHeader* h) {
+    static_assert(kMaxLam == 64, "one lane per multiplier");
+    const int j = threadIdx.x;
+    unsigned long long t = 0;
+    for (int k = 0; k < kRateStripes; ++k) {
+        t += h->rsum[j][k];
+        h->rsum[j][k] = 0ull;
+    }
+    h->sums[j] += t;
+    __syncthreads();
+    if (threadIdx.x != 0 || h->done) return;
     const unsigned long long B = h->Btot_fx;
     switch (h->phase) {
     case kPhaseZero:
@@ -228,7 +239,7 @@ rates_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
     for (int j = threadIdx.x; j < nlam; j += blockDim.x) {
         unsigned long long t = 0;
         for (int w = 0; w < kSolveThreads / 64; ++w) t += part[w][j];
-        atomicAdd(&h->sums[j], t);
+        atomicAdd(&h->rsum[j][blockIdx.x % kRateStripes], t);
     }
 }
 
@@ -328,7 +339,7 @@ final_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
     if (threadIdx.x == 0) {
         unsigned long long t = 0;
         for (int w = 0; w < kSolveThreads / 64; ++w) t += part[w];
-        atomicAdd(&h->rate_final, t);
+        atomicAdd(&h->rate_part[blockIdx.x % kRateStripes], t);
     }
 }
 
@@ -804,7 +815,7 @@ rates_alpha_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr
         const uint32_t mask = alpha_search<kSearch>(t, alpha_m, smax, width, n, w);
         if (threadIdx.x == 0) {
             const double Hs = subset_entropy(t, alpha_m, mask, n);
-            atomicAdd(&h->asums[j][blockIdx.x % kRateStripes], rate_fx((double)n, Hs, shift));
+            atomicAdd(&h->rsum[j][blockIdx.x % kRateStripes], rate_fx((double)n, Hs, shift));
         }
     };
     if constexpr (kSearch == kSearchDpTables) {
@@ -847,7 +858,7 @@ final_alpha_kernel(const double* __restrict__ Dp, const double* __restrict__ Mlr
     const uint32_t mask = alpha_search<kSearch>(t, alpha_m, smax, width, n, w);
     if (tid == 0) {
         const double Hs = subset_entropy(t, alpha_m, mask, n);
-        atomicAdd(&h->rate_final, rate_fx((double)n, Hs, shift));
+        atomicAdd(&h->rate_part[blockIdx.x % kRateStripes], rate_fx((double)n, Hs, shift));
         const int m = *t.m;
         int k = 0;
         for (int i = 0; i < m; ++i)
@@ -1383,7 +1394,7 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
     // probes) per pass: fewer evaluations, more passes.
     const bool grids = p.search == KVQ_GRIDS;
     const int bits_max = grids ? 6 : 1;
-    const int dbl_n = grids ? kMaxLam - 1 : kStripedLam;  // alphabet passes: at most kStripedLam multipliers
+    const int dbl_n = grids ? kMaxLam - 1 : kAlphaLam;
     // few blocks (a decode step): choice, rate and offsets in two small
     // launches (launch_final_small), the result written to `out`
     const bool small = grids && R >= 1 && R <= kSmallR && mode != KVQ_BISECT_GREEDY;
@@ -1412,11 +1423,11 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
             const auto k = kind == kSearchBeam ? rates_alpha_kernel<kSearchBeam>
                          : kind == kSearchDp   ? rates_alpha_kernel<kSearchDp>
                                                : rates_alpha_kernel<kSearchDpTables>;
-            const unsigned ys = kind == kSearchDpTables ? 1u : (unsigned)kStripedLam;
+            const unsigned ys = kind == kSearchDpTables ? 1u : (unsigned)kAlphaLam;
             hipLaunchKernelGGL(k, dim3((unsigned)R, ys), dim3(dp_threads), alpha_lds,
                                st, D, H, stats, R, p.alphabet_m, p.s, width, n, shift, h);
         }
-        hipLaunchKernelGGL(solve_select_kernel, dim3(1), dim3(64), 0, st, h, grids ? 0 : 1);
+        hipLaunchKernelGGL(solve_select_kernel, dim3(1), dim3(64), 0, st, h);
     };
     if (mode == KVQ_BISECT || mode == KVQ_BISECT_GREEDY) {
         // lambda = 0 first; the bracket passes run only when it is infeasible
@@ -1447,6 +1458,7 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
         hipLaunchKernelGGL(k, dim3((unsigned)R), dim3(dp_threads), alpha_lds, st, D, H,
                            stats, R, p.alphabet_m, p.s, width, p.s, n, shift, h, choice, codebook, m, off);
     }
+    hipLaunchKernelGGL(fold_rate_kernel, dim3(1), dim3(64), 0, st, h);
     if (mode == KVQ_BISECT_GREEDY && p.search == KVQ_GRIDS) {
         uint2* pool = (uint2*)((char*)ws + ws_pool_offset(R));
         hipLaunchKernelGGL(greedy_pool_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, wgt, R,

@@ -186,7 +186,7 @@ def test_admit_validates_before_launch(L):
 def test_admit_noalloc_validates_before_launch(L):
     """kvq_admit_noalloc refuses on the host, before it touches its static
     scratch or any GPU: bad arguments as kvq_admit does, and a plan whose
-    solve scratch exceeds the static 32 KB (more than 3,668,992 blocks)."""
+    solve scratch exceeds the static 44 KB (more than 3,668,992 blocks)."""
     Lb = kvq.lib()
     lam = ctypes.c_double(0.0)
     rate = ctypes.c_double(0.0)
