@@ -21,6 +21,8 @@ constexpr int kMaxPairs = kAlpha * (kAlpha - 1) / 2; // 496
 constexpr int kMaxBeam = KVQ_MAX_BEAM;                // 8
 constexpr int kMaxLam = 64;                       // multipliers per solve pass
 constexpr int kAlphaLam = 8;                       // multipliers per alphabet-search pass
+constexpr int64_t kManyBlocks = 65536;             // grid searches at least this large probe
+                                                   // fewer multipliers per pass
 // Same-address atomics from every workgroup serialise (about 11 ns each
 // here: 2048 of them cost a 12-point alphabet-search pass 22 us of its 44),
 // so the solve's rate sums are spread over this many addresses each.

@@ -1387,14 +1387,20 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
     const double Bfx = ldexp(Btot, shift);
     const unsigned long long Btot_fx =
         Bfx >= 18446744073709551615.0 ? ~0ull : (unsigned long long)floor(Bfx);
-    // Multipliers per pass: the grid search scores a block at 63 multipliers
-    // for little more than the cost of one, so it takes 6 halvings (and all
-    // 63 doubling probes) per pass; the alphabet searches cost a dynamic
-    // program per multiplier, so they take one halving (and 8 doubling
-    // probes) per pass: fewer evaluations, more passes.
+    // Multipliers per pass (every split gives the same bisection).  A grid
+    // search over fewer than kManyBlocks blocks pays about a launch per pass
+    // whatever it probes, so it takes 6 halvings (63 multipliers, and all 63
+    // doubling probes) per pass.  Over more, the objective evaluations
+    // dominate (on 524288 blocks a 63-multiplier pass took 230 us, a
+    // one-multiplier pass 68), so it takes 4 halvings (15 multipliers) and 7
+    // doubling probes per pass: 1.33 ms against 2.16 ms for the B = 1.5
+    // bisection there.  The alphabet searches cost a dynamic program per
+    // block and multiplier, so they take one halving (and 8 doubling
+    // probes) per pass.
     const bool grids = p.search == KVQ_GRIDS;
-    const int bits_max = grids ? 6 : 1;
-    const int dbl_n = grids ? kMaxLam - 1 : kAlphaLam;
+    const bool many = R >= kManyBlocks;
+    const int bits_max = grids ? (many ? 4 : 6) : 1;
+    const int dbl_n = grids ? (many ? 7 : kMaxLam - 1) : kAlphaLam;
     // few blocks (a decode step): choice, rate and offsets in two small
     // launches (launch_final_small), the result written to `out`
     const bool small = grids && R >= 1 && R <= kSmallR && mode != KVQ_BISECT_GREEDY;
