@@ -194,6 +194,9 @@ __global__ void solve_select_kernel(WsHeader* h) {
 
 // ---------------------------------------------------------------- grids ----
 
+// kZero: the bisection's first pass, lambda = 0 alone (the host launches
+// this instance for it and the general one for the others).
+template <bool kZero>
 __global__ void __launch_bounds__(kSolveThreads)
 rates_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
                    const double* __restrict__ wgt, int64_t R, int C, double d, int shift,
@@ -202,6 +205,41 @@ rates_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
     const int nlam = h->nlam;
     if (h->done || nlam == 0) return;
     const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int wave = threadIdx.x >> 6;
+    if constexpr (kZero) {
+        // lambda = 0: the objective is the weighted D plus (+0) (0 H = +0 for
+        // the finite, non-negative H), so only D is read for the choice and
+        // H only at the chosen candidate
+        unsigned long long v = 0;
+        if (r < R) {
+            const double wr = wgt ? wgt[r] : 1.0;
+            double Dr[kMaxCand];
+#pragma unroll
+            for (int c = 0; c < kMaxCand; ++c) Dr[c] = c < C ? wr * D[c * R + r] : 0.0;
+            double best = Dr[0] + 0.0;
+            int bc = 0;
+#pragma unroll
+            for (int c = 1; c < kMaxCand; ++c) {
+                if (c < C) {
+                    const double o = Dr[c] + 0.0;
+                    if (o < best) {
+                        best = o;
+                        bc = c;
+                    }
+                }
+            }
+            v = rate_fx(d, H[bc * R + r], shift);
+        }
+        v = wave_sum_u64(v);
+        if ((threadIdx.x & 63) == 0) part[wave][0] = v;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            unsigned long long t = 0;
+            for (int w = 0; w < kSolveThreads / 64; ++w) t += part[w][0];
+            atomicAdd(&h->rsum[0][blockIdx.x % kRateStripes], t);
+        }
+        return;
+    } else {
     double Dr[kMaxCand], Hr[kMaxCand];
     if (r < R) {
         const double wr = wgt ? wgt[r] : 1.0;  // distortion weight (1: exact identity)
@@ -213,7 +251,6 @@ rates_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
             }
         }
     }
-    const int wave = threadIdx.x >> 6;
     for (int j = 0; j < nlam; ++j) {
         unsigned long long v = 0;
         if (r < R) {
@@ -240,6 +277,7 @@ rates_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
         unsigned long long t = 0;
         for (int w = 0; w < kSolveThreads / 64; ++w) t += part[w][j];
         atomicAdd(&h->rsum[j][blockIdx.x % kRateStripes], t);
+    }
     }
 }
 
@@ -284,6 +322,7 @@ __device__ __forceinline__ void empty_grid_block(int64_t r, int s, int32_t* __re
 // The same, loading the table row in chunks of 15 candidates whose loads are
 // in flight together (a loop bounded by the run-time C waits out one load
 // latency per candidate).
+template <bool kZero>  // the multiplier is 0
 __device__ unsigned long long final_grid_block(int64_t r, const double* __restrict__ D,
                                                const double* __restrict__ H, const double* __restrict__ wgt,
                                                const float* __restrict__ stats, int64_t R, int C, int s,
@@ -299,6 +338,32 @@ __device__ unsigned long long final_grid_block(int64_t r, const double* __restri
     const double wr = wgt ? wgt[r] : 1.0;
     const float mn = stats[r];
     const float mx = stats[(int64_t)(n_stats - 1) * R + r];
+    if constexpr (kZero) {
+        // the objective is the weighted D plus (+0) (0 H = +0 for the
+        // finite, non-negative H): D is read for the choice, H only at the
+        // chosen candidate, and the choice is choose_grid_block's
+        double Dv[kMaxCand];
+#pragma unroll
+        for (int c = 0; c < kMaxCand; ++c) Dv[c] = c < C ? D[c * R + r] : 0.0;
+        double best = 0.0;
+        int bc = -1;
+#pragma unroll
+        for (int c = 0; c < kMaxCand; ++c) {
+            if (c < C) {
+                const double o = wr * Dv[c] + 0.0;
+                if (bc < 0 || o < best) {
+                    best = o;
+                    bc = c;
+                }
+            }
+        }
+        const double Hc = H[bc * R + r];
+        const int m = write_grid_codebook(bc, mn, mx, stats + r, R, col, s, codebook + r * s);
+        choice[r] = bc;
+        m_out[r] = (uint8_t)m;
+        words = ((uint64_t)n * (uint64_t)code_width(m) + 31u) / 32u;
+        return rate_fx((double)n, Hc, shift);
+    } else {
     double Dv[kMaxCand], Hv[kMaxCand];
     constexpr int kChunk = 15;
 #pragma unroll
@@ -311,8 +376,12 @@ __device__ unsigned long long final_grid_block(int64_t r, const double* __restri
     }
     return choose_grid_block(r, Dv, Hv, C, wr, lam * (double)n, mn, mx, stats, R, s, n, shift, col, choice,
                              codebook, m_out, words);
+    }
 }
 
+// kZero: the multiplier is 0 (the host knows it from the bisection's first
+// pass).
+template <bool kZero>
 __global__ void __launch_bounds__(kSolveThreads)
 final_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
                    const double* __restrict__ wgt, const float* __restrict__ stats, int64_t R,
@@ -329,7 +398,7 @@ final_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
     unsigned long long v = 0;
     if (r < R) {
         uint64_t words;
-        v = final_grid_block(r, D, H, wgt, stats, R, C, s, n, shift, col, rt.n_stats, h->err != 0,
+        v = final_grid_block<kZero>(r, D, H, wgt, stats, R, C, s, n, shift, col, rt.n_stats, h->err != 0,
                              h->lam_final, choice, codebook, m_out, words);
         off[r + 1] = words;
     }
@@ -1421,10 +1490,10 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
     const int dp_waves = (dp_pairs + 63) / 64;
     const unsigned dp_threads = dp_waves < 1 ? 64u : (dp_waves > kDpThreads / 64 ? (unsigned)kDpThreads
                                                                                 : 64u * dp_waves);
-    auto rates_pass = [&]() {
+    auto rates_pass = [&](bool zero) {
         if (p.search == KVQ_GRIDS) {
-            hipLaunchKernelGGL(rates_grids_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, wgt,
-                               R, p.n_cand, (double)n, shift, h);
+            hipLaunchKernelGGL(zero ? rates_grids_kernel<true> : rates_grids_kernel<false>, dim3(grid),
+                               dim3(kSolveThreads), 0, st, D, H, wgt, R, p.n_cand, (double)n, shift, h);
         } else {
             const auto k = kind == kSearchBeam ? rates_alpha_kernel<kSearchBeam>
                          : kind == kSearchDp   ? rates_alpha_kernel<kSearchDp>
@@ -1435,18 +1504,20 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
         }
         hipLaunchKernelGGL(solve_select_kernel, dim3(1), dim3(64), 0, st, h);
     };
+    bool lam_zero = false;  // the final multiplier is known to be 0
     if (mode == KVQ_BISECT || mode == KVQ_BISECT_GREEDY) {
         // lambda = 0 first; the bracket passes run only when it is infeasible
-        rates_pass();
+        rates_pass(true);
         int32_t done = 0;
         const hipError_t e = read_back(&done, &h->done, sizeof done, st, staging);
         if (e != hipSuccess) return e;
+        lam_zero = done != 0;
         if (!done) {
             // doubling passes up to 2^62, the 2^63 / 2^64 pass if needed,
             // then multisection passes of up to bits_max halvings each;
             // passes after the bracket is closed return at once
             const int passes = (kMaxLam - 1 + dbl_n - 1) / dbl_n + 1 + (iters + bits_max - 1) / bits_max;
-            for (int ps = 0; ps < passes; ++ps) rates_pass();
+            for (int ps = 0; ps < passes; ++ps) rates_pass(false);
         }
     }
     if (small) {
@@ -1455,8 +1526,9 @@ hipError_t launch_solve(const kvq_plan& p, const RankTable& rt, const double* D,
         return hipGetLastError();
     }
     if (p.search == KVQ_GRIDS) {
-        hipLaunchKernelGGL(final_grids_kernel, dim3(grid), dim3(kSolveThreads), 0, st, D, H, wgt, stats,
-                           R, p.n_cand, p.s, n, shift, rt, h, choice, codebook, m, off);
+        hipLaunchKernelGGL(lam_zero ? final_grids_kernel<true> : final_grids_kernel<false>, dim3(grid),
+                           dim3(kSolveThreads), 0, st, D, H, wgt, stats, R, p.n_cand, p.s, n, shift, rt, h,
+                           choice, codebook, m, off);
     } else {
         const auto k = kind == kSearchBeam ? final_alpha_kernel<kSearchBeam>
                      : kind == kSearchDp   ? final_alpha_kernel<kSearchDp>
