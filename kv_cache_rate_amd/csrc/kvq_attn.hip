@@ -249,31 +249,55 @@ attn_split_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ 
     const int sp = blockIdx.x, h = blockIdx.y, o = blockIdx.z;
     const int c0 = sp * kChunkSplit, c1 = min(c0 + kChunkSplit, chunks);
     const int64_t rbase = ((int64_t)o * heads + h) * chunks;
-    // codebooks, widths and word offsets of the split's K and V blocks
-    for (int e = tid; e < 2 * kChunkSplit * kMaxS; e += kAT) {
+    // codebooks, widths and word offsets of the split's K and V blocks, and
+    // the query registers (lane 32 hf + 4 k + i holds, in register g8, head
+    // i's q at feature 64 hf + 8 g8 + k, scaled into base-2 units; heads past
+    // gcount are zero).  Every load is issued first, unconditionally (block
+    // and entry indices clamped into their arrays), and selected afterwards:
+    // loads under conditions were each waited on in turn, a dozen memory
+    // round trips before the first chunk.
+    constexpr int kSetup = 2 * kChunkSplit * kMaxS / kAT;  // table entries per thread
+    static_assert(kSetup * kAT == 2 * kChunkSplit * kMaxS, "whole rounds");
+    uint8_t mv[kSetup];
+    float cv[kSetup];
+    uint64_t ov[kSetup];
+#pragma unroll
+    for (int u = 0; u < kSetup; ++u) {
+        const int e = tid + u * kAT;
         const int t = e / (kChunkSplit * kMaxS), rem = e % (kChunkSplit * kMaxS);
         const int c = rem / kMaxS, k = rem % kMaxS;
-        if (c0 + c < c1) {
-            const int64_t r = rbase + c0 + c + (t ? nbK : 0);
-            const int mm = min(max((int)m_in[r], 1), s);
-            cb[t][c][k] = k < mm ? codebook[r * s + k] : 0.0f;
-            if (k == 0) {
-                wdt[t][c] = code_width(mm);
-                wof[t][c] = word_off[r];
-            }
-        }
+        const int64_t r = rbase + min(c0 + c, c1 - 1) + (t ? nbK : 0);
+        mv[u] = m_in[r];
+        cv[u] = codebook[r * s + min(k, s - 1)];
+        ov[u] = word_off[r];
     }
-    // query registers: lane 32 hf + 4 k + i holds, in register g8, head i's
-    // q at feature 64 hf + 8 g8 + k (scaled into base-2 units); heads past
-    // gcount are zero
     const int hf = lane >> 5, hi = lane & 3, kq = (lane >> 2) & 7;
-    float qreg[8];
+    float qv[8];
     {
-        const float c = scale * kLog2e;
         const float* qp = q + ((int64_t)o * heads * gtot + (int64_t)h * gtot + goff + min(hi, gcount - 1)) * kHD +
                           64 * hf + kq;
 #pragma unroll
-        for (int g8 = 0; g8 < 8; ++g8) qreg[g8] = hi < gcount ? c * qp[8 * g8] : 0.0f;
+        for (int g8 = 0; g8 < 8; ++g8) qv[g8] = qp[8 * g8];
+    }
+#pragma unroll
+    for (int u = 0; u < kSetup; ++u) {
+        const int e = tid + u * kAT;
+        const int t = e / (kChunkSplit * kMaxS), rem = e % (kChunkSplit * kMaxS);
+        const int c = rem / kMaxS, k = rem % kMaxS;
+        if (c0 + c < c1) {
+            const int mm = min(max((int)mv[u], 1), s);
+            cb[t][c][k] = k < mm ? cv[u] : 0.0f;
+            if (k == 0) {
+                wdt[t][c] = code_width(mm);
+                wof[t][c] = ov[u];
+            }
+        }
+    }
+    float qreg[8];
+    {
+        const float c = scale * kLog2e;
+#pragma unroll
+        for (int g8 = 0; g8 < 8; ++g8) qreg[g8] = hi < gcount ? c * qv[g8] : 0.0f;
     }
     __syncthreads();
 
