@@ -215,7 +215,12 @@ rates_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
             const double wr = wgt ? wgt[r] : 1.0;
             double Dr[kMaxCand];
 #pragma unroll
-            for (int c = 0; c < kMaxCand; ++c) Dr[c] = c < C ? wr * D[c * R + r] : 0.0;
+            for (int c = 0; c < kMaxCand; ++c) {
+                // unconditional loads (candidate clamped into the table):
+                // a load under the c < C condition was waited on by itself
+                const double dv = D[(c < C ? c : C - 1) * R + r];
+                Dr[c] = c < C ? wr * dv : 0.0;
+            }
             double best = Dr[0] + 0.0;
             int bc = 0;
 #pragma unroll
@@ -243,12 +248,14 @@ rates_grids_kernel(const double* __restrict__ D, const double* __restrict__ H,
     double Dr[kMaxCand], Hr[kMaxCand];
     if (r < R) {
         const double wr = wgt ? wgt[r] : 1.0;  // distortion weight (1: exact identity)
+        // every load unconditional (candidate clamped into the table), so
+        // all are in flight together; under the c < C condition each was
+        // waited on by itself
 #pragma unroll
         for (int c = 0; c < kMaxCand; ++c) {
-            if (c < C) {
-                Dr[c] = wr * D[c * R + r];
-                Hr[c] = H[c * R + r];
-            }
+            const int cc = c < C ? c : C - 1;
+            Dr[c] = wr * D[cc * R + r];
+            Hr[c] = H[cc * R + r];
         }
     }
     for (int j = 0; j < nlam; ++j) {
