@@ -92,13 +92,29 @@ __device__ void load_and_sort_e(const Geom& g, int64_t r, int NP, uint32_t* keys
     const int64_t base = block_base(g, r, ti);
     const int n = g.n;
     const int t0 = E * (int)threadIdx.x;
+    // every load first, unconditionally (positions past the block read its
+    // last entry and are dropped): a load under the position test was
+    // waited on by itself, one memory round trip per key
+    int64_t ofs[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) ofs[e] = base + entry_off(g, ti, min(t0 + e, n - 1));
+    float xv[E];
+    if (g.dtype == KVQ_F16) {
+        const __half* src = reinterpret_cast<const __half*>(g.data[ti]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) xv[e] = __half2float(src[ofs[e]]);
+    } else {
+        const float* src = reinterpret_cast<const float*>(g.data[ti]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) xv[e] = src[ofs[e]];
+    }
     uint32_t v[E];
     bool bad = false;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         uint32_t k = 0xffffffffu;
         if (t0 + e < n) {
-            float x = load_entry(g, ti, base + entry_off(g, ti, t0 + e));
+            float x = xv[e];
             if (x == 0.0f) x = 0.0f;  // -0 -> +0
             if (!isfinite(x)) bad = true;
             k = f32_key(x);

@@ -42,9 +42,28 @@ quantize_kernel(Geom g, int s, const float* __restrict__ codebook, const uint8_t
     uint64_t acc = 0;
     int nb = 0;
     uint64_t wi = off[r] + (uint64_t)threadIdx.x * (uint64_t)w;
+    // the thread's entries, every load first and unconditional (positions
+    // past its last entry re-read that entry, unused): loads under the
+    // position test were waited on one by one
+    float xs[32];
+    {
+        int64_t ofs[32];
+#pragma unroll
+        for (int e = 0; e < 32; ++e) ofs[e] = base + entry_off(g, ti, t0 + min(e, cnt - 1));
+        if (g.dtype == KVQ_F16) {
+            const __half* src = reinterpret_cast<const __half*>(g.data[ti]);
+#pragma unroll
+            for (int e = 0; e < 32; ++e) xs[e] = __half2float(src[ofs[e]]);
+        } else {
+            const float* src = reinterpret_cast<const float*>(g.data[ti]);
+#pragma unroll
+            for (int e = 0; e < 32; ++e) xs[e] = src[ofs[e]];
+        }
+    }
+#pragma unroll
     for (int gq = 0; gq < 8; ++gq) {
         const int tg = t0 + 4 * gq;
-        if (tg >= t0 + cnt) break;
+        if (tg >= t0 + cnt) continue;
         uint32_t c0 = (uint32_t)(tg >> 2), c1 = rlo, c2 = rhi, c3 = 0u;
         philox4x32_10(c0, c1, c2, c3, k0, k1);
         const uint32_t wd[4] = {c0, c1, c2, c3};
@@ -52,7 +71,7 @@ quantize_kernel(Geom g, int s, const float* __restrict__ codebook, const uint8_t
         for (int e = 0; e < 4; ++e) {
             const int t = tg + e;
             if (t < t0 + cnt) {
-                const float x = load_entry(g, ti, base + entry_off(g, ti, t));
+                const float x = xs[4 * gq + e];
                 int i = 0;
                 for (int j = 1; j < m - 1; ++j) i += (q[j] <= x) ? 1 : 0;
                 const float a = q[i];
