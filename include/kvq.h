@@ -282,7 +282,9 @@ kvq_status kvq_admit(const kvq_plan* p, const kvq_tensor* t, int32_t n_tensors, 
    scratch: calls that overlap in time on the same GPU (different streams or
    threads) race and give unspecified results; calls in sequence are
    independent (the scratch's stale contents are reset by the call's first
-   kernels).  mode: KVQ_BISECT or KVQ_SUBGRAD. */
+   kernels; the one-launch decode admission instead tags the words it
+   publishes with a per-launch epoch and writes the header whole, so stale
+   words are never read as its own).  mode: KVQ_BISECT or KVQ_SUBGRAD. */
 kvq_status kvq_admit_noalloc(const kvq_plan* p, const kvq_tensor* t, int32_t n_tensors, double* D,
                              double* H, float* stats, double B_bits_per_entry, int32_t mode,
                              int32_t iters, double eta, double* lambda_io,

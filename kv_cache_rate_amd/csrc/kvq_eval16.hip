@@ -35,6 +35,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "kvq_grid_choice.h"
 #include "kvq_internal.h"
 #include "kvq_quant_block.h"
@@ -300,10 +302,17 @@ struct Eval16Tables {
 };
 
 // Words a block publishes for the blocks after it (relaxed device-scope
-// atomics: each word carries its own flag, so no fence orders one against
-// another).
+// atomics: each word carries its own flag and the launch's epoch, so no fence
+// orders one against another and nothing has to clear them between launches).
+//   count word: kPub | kPubNF | epoch << 34 | rate bits 35..56 << 12 | words
+//   rate word:  kPub | epoch << 35 | rate bits 0..34
+// A block's fixed-point rate is below 2^55 (4096 entries x 4 bits x 2^40).
 constexpr uint64_t kPub = 1ull << 63;      // the word is published
 constexpr uint64_t kPubNF = 1ull << 62;    // count word: the block holds NaN or Inf
+constexpr uint32_t kEpochMask = (1u << 28) - 1u;
+constexpr uint64_t kRateLoMask = (1ull << 35) - 1ull;
+__device__ __forceinline__ uint32_t count_epoch(uint64_t v) { return (uint32_t)(v >> 34) & kEpochMask; }
+__device__ __forceinline__ uint32_t rate_epoch(uint64_t v) { return (uint32_t)(v >> 35) & kEpochMask; }
 constexpr uint32_t kDescSpins = 1u << 22;  // polls before a missing predecessor is reported
 
 // The rest of the admission step at a known multiplier, run by the same
@@ -316,8 +325,9 @@ struct FusedArgs {
     float* codebook;               // [R][16]
     uint8_t* m;
     uint64_t* off;                 // [R + 1]
-    uint64_t* desc;                // [R] published word counts, zeroed by fused_reset_kernel
-    uint64_t* rates;               // [R] published fixed-point rates, zeroed likewise
+    uint32_t epoch;                // this launch's tag (1 .. kEpochMask), new for every launch
+    uint64_t* desc;                // [R] published count words (never cleared: see kPub)
+    uint64_t* rates;               // [R] published rate words
     uint32_t* codes;
     SolveOut* out;                 // pinned host memory, or null
 };
@@ -375,9 +385,12 @@ __device__ __forceinline__ void fused_tail(Shared<kSlots>& sh, const Eval16Table
             fa.m[r] = (uint8_t)m;
             const uint64_t words = (4096u * (uint32_t)code_width(m) + 31u) / 32u;
             const uint64_t rate = rate_fx(4096.0, bestH, fa.shift);
-            __hip_atomic_store(&fa.desc[r], kPub | (sh.fz_nf ? kPubNF : 0ull) | words, __ATOMIC_RELAXED,
+            const uint64_t ep = fa.epoch;
+            __hip_atomic_store(&fa.desc[r],
+                               kPub | (sh.fz_nf ? kPubNF : 0ull) | (ep << 34) | ((rate >> 35) << 12) | words,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&fa.rates[r], kPub | (ep << 35) | (rate & kRateLoMask), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&fa.rates[r], kPub | rate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (r == 0) fa.off[0] = 0;
             sh.fz_m = m;
             sh.fz_ob = words;
@@ -407,21 +420,23 @@ __device__ __forceinline__ void fused_tail(Shared<kSlots>& sh, const Eval16Table
     uint32_t flags = 0;
     for (int64_t j = tid; j < r; j += kT) {
         uint32_t spins = 0;
-        uint64_t v, q = kPub;
+        uint64_t v, q = 0;
         for (;;) {
             v = __hip_atomic_load(&fa.desc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (last) q = __hip_atomic_load(&fa.rates[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if ((v & kPub) && (q & kPub)) break;
+            const bool vok = (v & kPub) && count_epoch(v) == fa.epoch;
+            const bool qok = !last || ((q & kPub) && rate_epoch(q) == fa.epoch);
+            if (vok && qok) break;
             if (++spins > kDescSpins) {  // never expected: report, do not hang
                 flags |= kStatusFusedStall;
-                v = kPub;
-                q = kPub;
+                v = 0;
+                q = 0;
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
         }
-        part += v & 0xffffffffull;
-        rpart += q & ~kPub;
+        part += v & 0xfffull;
+        rpart += (((v >> 12) & 0x3fffffull) << 35) | (q & kRateLoMask);
         if (v & kPubNF) flags |= kStatusNonFinite;
     }
     part = wave_scan_add_u64(part);  // lane 63: the wave's total
@@ -449,7 +464,10 @@ __device__ __forceinline__ void fused_tail(Shared<kSlots>& sh, const Eval16Table
                                          sh.fz_rate;
             const uint32_t status = (sh.fz_flags[0] | sh.fz_flags[1] | sh.fz_flags[2] | sh.fz_flags[3]) |
                                     (sh.fz_nf ? kStatusNonFinite : 0u);
-            if (status & kStatusFusedStall) atomicOr(&ws->status, kStatusFusedStall);
+            // the header is written whole: nothing clears it before a launch
+            ws->status = status;
+            ws->phase = 0;
+            ws->nlam = 0;
             ws->err = 0;
             ws->done = 1;
             ws->pool_overflow = 0;
@@ -577,8 +595,10 @@ eval16_kernel(const __half* __restrict__ x0, const __half* __restrict__ x1, int6
         const uint32_t ct = (c[0] + c[1]) + (c[2] + c[3]);
         const uint32_t at = (acc[0] + acc[1]) + (acc[2] + acc[3]);
         if ((tid < 4 || tid >= kT - 4) && ct != 0u) {
-            atomicOr(&ws->status, kStatusNonFinite);
-            if (kFused) sh.fz_nf = 1u;
+            if (kFused)
+                sh.fz_nf = 1u;  // reported through the count word and the last block
+            else
+                atomicOr(&ws->status, kStatusNonFinite);
         }
         const double st = (double)ct * (double)B0 + U * (double)at;
         const uint32_t ic = wave_scan_add_u32(ct);
@@ -1026,21 +1046,14 @@ hipError_t launch_eval16(const void* x0, const void* x1, int64_t nb0, int64_t R,
     return hipGetLastError();
 }
 
-// Workspace set-up of the one-launch admission: status, rate, ticket and
-// the R published word counts.
-__global__ void __launch_bounds__(1024) fused_reset_kernel(WsHeader* h, uint64_t* desc, uint64_t* rates,
-                                                           int64_t R) {
-    const int tid = threadIdx.x;
-    if (tid < R) {
-        desc[tid] = 0u;
-        rates[tid] = 0u;
-    }
-    if (tid == 0) {
-        h->status = 0;
-        h->phase = 0;
-        h->done = 0;
-        h->err = 0;
-        h->nlam = 0;
+// Epoch of a one-launch admission: process-wide, new for every launch and
+// never 0, so words left by earlier launches (or a fresh workspace's zeros)
+// are not taken for this launch's.
+static uint32_t next_fused_epoch() {
+    static std::atomic<uint32_t> counter{0};
+    for (;;) {
+        const uint32_t e = (counter.fetch_add(1u, std::memory_order_relaxed) + 1u) & kEpochMask;
+        if (e != 0u) return e;
     }
 }
 
@@ -1056,8 +1069,8 @@ hipError_t launch_admit_fused(const void* x0, const void* x1, int64_t nb0, int64
     // published words after the header (the offsets scan's area, unused here)
     uint64_t* desc = (uint64_t*)((char*)ws + kWsHeaderBytes);
     uint64_t* rates = desc + kFusedMaxBlocks;
-    hipLaunchKernelGGL(fused_reset_kernel, dim3(1), dim3(1024), 0, st, h, desc, rates, R);
     FusedArgs fa;
+    fa.epoch = next_fused_epoch();
     fa.lam = lam_in;
     fa.shift = shift;
     fa.k0 = (uint32_t)seed;

@@ -119,6 +119,41 @@ def test_one_launch_admission_ties_and_constant_blocks():
     assert int(a["m"][0].item()) == 1 and int(a["m"][1].item()) == 1
 
 
+def test_one_launch_admission_ignores_stale_workspace_words():
+    """Nothing clears the one-launch admission's published words between
+    launches: each carries its launch's epoch.  A workspace filled with
+    words that look published (all bits set), and one left by a launch whose
+    input held an Inf (its status bit must not leak into the next launch),
+    must both give the three calls' outputs bit for bit."""
+    import torch
+    from kv_cache_rate_amd import kvq
+    rng = np.random.default_rng(31)
+    x = rng.standard_t(5.0, size=(16, 8, 32, 128)).astype(np.float16)
+    bad = x.copy()
+    bad[3, 2, 1, 0] = np.inf
+    dev, dev_bad = [torch.from_numpy(x).cuda()], [torch.from_numpy(bad).cuda()]
+    plan = kvq.kvq_plan_blocks(dev, 32, 128, 16)
+    a = kvq.allocate(plan)
+    b = kvq.allocate(plan)
+    lam_a, rate_a = kvq.admit(plan, dev, a, 2.0, kvq.KVQ_SUBGRAD, 40, 1e-3, 0.4, 3)
+    for prep in ("ones", "nonfinite"):
+        if prep == "ones":
+            b["workspace"].fill_(255)
+        else:
+            with pytest.raises(kvq.KvqError) as ei:
+                kvq.kvq_admit(plan, dev_bad, b, 2.0, kvq.KVQ_SUBGRAD, 40, 1e-3, 0.4, 3)
+            assert ei.value.status == kvq.KVQ_ENONFINITE
+        for k in ("choice", "codebook", "off", "codes"):
+            b[k].fill_(-1)
+        lam_b, rate_b = kvq.kvq_admit(plan, dev, b, 2.0, kvq.KVQ_SUBGRAD, 40, 1e-3, 0.4, 3)
+        torch.cuda.synchronize()
+        assert lam_a == lam_b and rate_a == rate_b, (prep, lam_a, lam_b, rate_a, rate_b)
+        for k in ("D", "H", "stats", "choice", "codebook", "m", "off"):
+            assert torch.equal(a[k], b[k]), (prep, k)
+        words = int(a["off"][-1].item())
+        assert torch.equal(a["codes"][:words], b["codes"][:words]), prep
+
+
 def test_prepared_admit_matches_kvq_admit(noalloc=False):
     """prepare_admit (arguments marshalled once, the multiplier carried from
     step to step) gives kvq_admit's multipliers, rates and codes bit for bit
