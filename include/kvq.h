@@ -23,13 +23,16 @@
  * multiplier finds a budget-feasible allocation).
  *
  * Conventions for every entry point:
- *   - Device pointers are HIP device memory owned by the caller; the library
- *     allocates no device memory.  Its state is one 8 KB pinned host buffer
- *     per calling thread (hipHostMalloc on first use, kept until the process
- *     ends) through which the synchronising calls read back their small
- *     results (for up to 1024 grid-search blocks the solve's last kernel
- *     writes them into it directly), and the 44 KB static device scratch of
- *     kvq_admit_noalloc (one per GPU, part of the loaded code object).  Sizes
+ *   - Device pointers are HIP device memory owned by the caller.  The
+ *     library's own state is one 8 KB pinned host buffer per calling thread
+ *     (hipHostMalloc on first use, kept until the process ends) through
+ *     which the synchronising calls read back their small results (for up to
+ *     1024 grid-search blocks the solve's last kernel writes them into it
+ *     directly); one 16 KB device buffer per calling thread and GPU for
+ *     kvq_admit's one-launch decode admission (hipMalloc on its first such
+ *     call, kept until the process ends); and the 60 KB static device
+ *     scratch of kvq_admit_noalloc (one per GPU, part of the loaded code
+ *     object).  No other device memory is allocated.  Sizes
  *     of every buffer come from kvq_plan (filled by kvq_plan_blocks).
  *   - Host pointers are marked "(host)".
  *   - Arguments are validated on the host before any launch; a failed check
@@ -273,7 +276,7 @@ kvq_status kvq_admit(const kvq_plan* p, const kvq_tensor* t, int32_t n_tensors, 
 /* kvq_admit without a workspace argument and without any allocation, for
    callers that cannot allocate device or pinned memory (code under HIP graph
    capture, tight serving loops, harnesses that forbid hipMalloc).  The
-   solve's workspace is a static device array of the library (44 KB per GPU,
+   solve's workspace is a static device array of the library (60 KB per GPU,
    held by each GPU the library runs on until the process ends), so plans of
    at most 3,668,992 blocks are accepted (KVQ_ENOSPC beyond, with nothing
    launched).  Results are read back with a plain copy into the caller's host
@@ -282,9 +285,9 @@ kvq_status kvq_admit(const kvq_plan* p, const kvq_tensor* t, int32_t n_tensors, 
    scratch: calls that overlap in time on the same GPU (different streams or
    threads) race and give unspecified results; calls in sequence are
    independent (the scratch's stale contents are reset by the call's first
-   kernels; the one-launch decode admission instead tags the words it
-   publishes with a per-launch epoch and writes the header whole, so stale
-   words are never read as its own).  mode: KVQ_BISECT or KVQ_SUBGRAD. */
+   kernels; the one-launch decode admission tags the words it publishes with
+   a per-launch epoch, clears them when the epochs start over, and writes the
+   header whole).  mode: KVQ_BISECT or KVQ_SUBGRAD. */
 kvq_status kvq_admit_noalloc(const kvq_plan* p, const kvq_tensor* t, int32_t n_tensors, double* D,
                              double* H, float* stats, double B_bits_per_entry, int32_t mode,
                              int32_t iters, double eta, double* lambda_io,

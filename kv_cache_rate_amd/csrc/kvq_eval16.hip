@@ -35,8 +35,6 @@
 #include <math.h>
 #include <string.h>
 
-#include <atomic>
-
 #include "kvq_grid_choice.h"
 #include "kvq_internal.h"
 #include "kvq_quant_block.h"
@@ -303,13 +301,13 @@ struct Eval16Tables {
 
 // Words a block publishes for the blocks after it (relaxed device-scope
 // atomics: each word carries its own flag and the launch's epoch, so no fence
-// orders one against another and nothing has to clear them between launches).
+// orders one against another and nothing clears them between launches).
 //   count word: kPub | kPubNF | epoch << 34 | rate bits 35..56 << 12 | words
 //   rate word:  kPub | epoch << 35 | rate bits 0..34
 // A block's fixed-point rate is below 2^55 (4096 entries x 4 bits x 2^40).
 constexpr uint64_t kPub = 1ull << 63;      // the word is published
 constexpr uint64_t kPubNF = 1ull << 62;    // count word: the block holds NaN or Inf
-constexpr uint32_t kEpochMask = (1u << 28) - 1u;
+constexpr uint32_t kEpochMask = kFusedEpochMax;
 constexpr uint64_t kRateLoMask = (1ull << 35) - 1ull;
 __device__ __forceinline__ uint32_t count_epoch(uint64_t v) { return (uint32_t)(v >> 34) & kEpochMask; }
 __device__ __forceinline__ uint32_t rate_epoch(uint64_t v) { return (uint32_t)(v >> 35) & kEpochMask; }
@@ -326,7 +324,7 @@ struct FusedArgs {
     uint8_t* m;
     uint64_t* off;                 // [R + 1]
     uint32_t epoch;                // this launch's tag (1 .. kEpochMask), new for every launch
-    uint64_t* desc;                // [R] published count words (never cleared: see kPub)
+    uint64_t* desc;                // [R] published count words (see kPub)
     uint64_t* rates;               // [R] published rate words
     uint32_t* codes;
     SolveOut* out;                 // pinned host memory, or null
@@ -1046,31 +1044,32 @@ hipError_t launch_eval16(const void* x0, const void* x1, int64_t nb0, int64_t R,
     return hipGetLastError();
 }
 
-// Epoch of a one-launch admission: process-wide, new for every launch and
-// never 0, so words left by earlier launches (or a fresh workspace's zeros)
-// are not taken for this launch's.
-static uint32_t next_fused_epoch() {
-    static std::atomic<uint32_t> counter{0};
-    for (;;) {
-        const uint32_t e = (counter.fetch_add(1u, std::memory_order_relaxed) + 1u) & kEpochMask;
-        if (e != 0u) return e;
-    }
+// Clears a one-launch admission's words buffer (both arrays).
+__global__ void __launch_bounds__(1024) fused_words_clear_kernel(uint64_t* words) {
+    const int tid = threadIdx.x;
+    words[tid] = 0u;
+    words[kFusedMaxBlocks + tid] = 0u;
+}
+static_assert(kFusedMaxBlocks == 1024, "one thread per block index");
+
+hipError_t launch_fused_words_clear(uint64_t* words, hipStream_t st) {
+    hipLaunchKernelGGL(fused_words_clear_kernel, dim3(1), dim3(1024), 0, st, words);
+    return hipGetLastError();
 }
 
 hipError_t launch_admit_fused(const void* x0, const void* x1, int64_t nb0, int64_t R, const RankTable& rt,
                               double lam_in, int shift, uint64_t seed, double* D, double* H, float* stats,
                               int32_t* choice, float* codebook, uint8_t* m, uint64_t* off, uint32_t* codes,
-                              void* ws, SolveOut* out, hipStream_t st) {
-    if (R < 1 || R > kFusedMaxBlocks) return hipErrorInvalidValue;
+                              void* ws, uint64_t* words, uint32_t epoch, SolveOut* out, hipStream_t st) {
+    if (R < 1 || R > kFusedMaxBlocks || epoch < 1u || epoch > kFusedEpochMax) return hipErrorInvalidValue;
     Eval16Tables tb;
     const hipError_t te = make_tables(rt, tb);
     if (te != hipSuccess) return te;
     WsHeader* h = (WsHeader*)ws;
-    // published words after the header (the offsets scan's area, unused here)
-    uint64_t* desc = (uint64_t*)((char*)ws + kWsHeaderBytes);
-    uint64_t* rates = desc + kFusedMaxBlocks;
+    uint64_t* desc = words;
+    uint64_t* rates = words + kFusedMaxBlocks;
     FusedArgs fa;
-    fa.epoch = next_fused_epoch();
+    fa.epoch = epoch;
     fa.lam = lam_in;
     fa.shift = shift;
     fa.k0 = (uint32_t)seed;

@@ -13,7 +13,8 @@
 #include "kvq_internal.h"
 
 // Device scratch of kvq_admit_noalloc: the solve's workspace (header and
-// scan tile sums) for callers that cannot allocate.  Each device holds its
+// scan tile sums), then the one-launch admission's published words, for
+// callers that cannot allocate.  Each device holds its
 // own copy for the life of the process; host code reaches it only through
 // the address hipGetSymbolAddress returns for the current device.
 static __device__ __align__(256) unsigned char scratch[kvq::kNoAllocScratchBytes];
@@ -401,10 +402,67 @@ kvq_status noalloc_scratch(void** out) {
     return KVQ_OK;
 }
 
+// A one-launch admission's words buffer and the epoch of its last launch.
+// Every launch on a buffer takes the next epoch; the buffer is cleared on
+// the stream before its first launch and whenever the epochs start over, so
+// no word of an earlier launch ever carries the current epoch.
+struct FusedWords {
+    uint64_t* words = nullptr;
+    uint32_t epoch = 0;
+};
+
+kvq_status next_fused_epoch(FusedWords& fw, hipStream_t s, uint32_t* epoch) {
+    if (fw.epoch == 0u || fw.epoch >= kvq::kFusedEpochMax) {
+        const hipError_t e = kvq::launch_fused_words_clear(fw.words, s);
+        if (e != hipSuccess) return hip_fail(e, "clearing the admission's published words");
+        fw.epoch = 0u;
+    }
+    *epoch = ++fw.epoch;
+    return KVQ_OK;
+}
+
+// kvq_admit: one words buffer per host thread and device, allocated on first
+// use and kept until the process ends (a thread's calls wait for their
+// result, so its launches never overlap).
+kvq_status thread_fused_words(hipStream_t s, uint64_t** words, uint32_t* epoch) {
+    thread_local FusedWords tl[kMaxDevices];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_EINVAL, "device %d outside 0..%d", dev, kMaxDevices - 1);
+    FusedWords& fw = tl[dev];
+    if (!fw.words) {
+        e = hipMalloc((void**)&fw.words, kvq::kFusedWordsBytes);
+        if (e != hipSuccess) {
+            fw.words = nullptr;
+            return hip_fail(e, "hipMalloc (admission words)");
+        }
+        fw.epoch = 0u;
+    }
+    *words = fw.words;
+    return next_fused_epoch(fw, s, epoch);
+}
+
+// kvq_admit_noalloc: the words at the end of the device's static scratch
+// (calls that overlap on one device race, as for the rest of the scratch).
+FusedWords g_scratch_words[kMaxDevices];
+
+kvq_status scratch_fused_words(void* scratch_ptr, hipStream_t s, uint64_t** words, uint32_t* epoch) {
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_EINVAL, "device %d outside 0..%d", dev, kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    FusedWords& fw = g_scratch_words[dev];
+    fw.words = reinterpret_cast<uint64_t*>(static_cast<char*>(scratch_ptr) + kvq::kNoAllocSolveBytes);
+    *words = fw.words;
+    return next_fused_epoch(fw, s, epoch);
+}
+
 // The admission step at a known multiplier (subgradient mode) on up to
 // kFusedMaxBlocks fp16 blocks of 4096 contiguous entries with s = 16: one
-// kernel scores, chooses, quantizes and packs (after a reset launch), and
-// the call waits once for its result.  Outputs are those of the three
+// kernel scores, chooses, quantizes and packs, and the call waits once for
+// its result.  Outputs are those of the three
 // calls.
 bool fused_admission(const kvq_plan* p, const kvq_tensor* t, int32_t nt, int32_t mode) {
     return mode == KVQ_SUBGRAD && p->n_blocks >= 1 && p->n_blocks <= kvq::kFusedMaxBlocks &&
@@ -415,6 +473,10 @@ kvq_status admit_fused(const kvq_plan* p, const kvq_tensor* t, int32_t nt, doubl
                        double B, double eta, double* lambda_io, double* rate_out, int32_t* choice,
                        float* codebook, uint8_t* m, uint64_t* word_off, uint64_t seed, uint32_t* codes,
                        void* ws, hipStream_t s, bool staging) {
+    uint64_t* words = nullptr;
+    uint32_t epoch = 0;
+    kvq_status st = staging ? thread_fused_words(s, &words, &epoch) : scratch_fused_words(ws, s, &words, &epoch);
+    if (st) return st;
     kvq::RankTable rt;
     rank_table(*p, rt);
     const double lam_in = *lambda_io;
@@ -425,7 +487,7 @@ kvq_status admit_fused(const kvq_plan* p, const kvq_tensor* t, int32_t nt, doubl
     ss.staging = staging;
     const hipError_t e = kvq::launch_admit_fused(t[0].data, nt > 1 ? t[1].data : t[0].data, p->tensor_blocks[0],
                                                  p->n_blocks, rt, lam_in, p->rate_shift, seed, D, H, stats,
-                                                 choice, codebook, m, word_off, codes, ws,
+                                                 choice, codebook, m, word_off, codes, ws, words, epoch,
                                                  ss.direct ? static_cast<kvq::SolveOut*>(dev_out) : nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "one-launch admission");
     return solve_result(p, B, KVQ_SUBGRAD, eta, lam_in, ws, s, ss, lambda_io, rate_out);
@@ -531,9 +593,9 @@ kvq_status kvq_admit_noalloc(const kvq_plan* p, const kvq_tensor* t, int32_t nt,
     if (mode != KVQ_BISECT && mode != KVQ_SUBGRAD)
         return fail(KVQ_EINVAL, "kvq_admit_noalloc takes KVQ_BISECT or KVQ_SUBGRAD");
     const size_t need = kvq::ws_pool_offset(p->n_blocks);
-    if (need > kvq::kNoAllocScratchBytes)
+    if (need > kvq::kNoAllocSolveBytes)
         return fail(KVQ_ENOSPC, "%lld blocks need %zu bytes of solve scratch; the static scratch holds %zu "
-                    "(at most 3668992 blocks)", (long long)p->n_blocks, need, kvq::kNoAllocScratchBytes);
+                    "(at most 3668992 blocks)", (long long)p->n_blocks, need, kvq::kNoAllocSolveBytes);
     // every argument is checked before the scratch is touched
     int dummy = 0;
     st = solve_check(p, D, H, nullptr, stats, B, mode, iters, eta, lambda_io, rate_out, choice, codebook, m,

@@ -78,8 +78,11 @@ __host__ __device__ inline size_t ws_pool_offset(int64_t R) {
 }
 static_assert(sizeof(WsHeader) <= kWsHeaderBytes, "workspace header");
 // Static device scratch of kvq_admit_noalloc: header plus scan tile sums
-// (no greedy pool), enough for ws_pool_offset(R) with R up to 3,668,992.
-constexpr size_t kNoAllocScratchBytes = 45056;
+// (no greedy pool), enough for ws_pool_offset(R) with R up to 3,668,992,
+// then the one-launch admission's published words (kFusedWordsBytes).
+constexpr size_t kNoAllocSolveBytes = 45056;
+constexpr size_t kFusedWordsBytes = 2 * 1024 * sizeof(uint64_t);  // 2 x kFusedMaxBlocks words
+constexpr size_t kNoAllocScratchBytes = kNoAllocSolveBytes + kFusedWordsBytes;
 
 // Block geometry as the kernels see it (passed by value).
 struct Geom {
@@ -335,14 +338,22 @@ hipError_t launch_ws_reset(void* ws, hipStream_t st);
 // One launch of the admission step at a known multiplier for up to
 // kFusedMaxBlocks fp16 blocks of 4096 contiguous entries with s = 16 (grid
 // search): scoring, the choice at lam_in, the codebook, the offsets, the
-// stochastic rounding and packing, the rate sum, preceded by a reset of the
-// workspace header.  `out` (pinned host memory, may be null) receives the
-// solve's result fields.
+// stochastic rounding and packing, the rate sum; the last block writes the
+// workspace header whole.  `out` (pinned host memory, may be null) receives
+// the solve's result fields.  `words` (kFusedWordsBytes of device memory that
+// only these launches write) holds the blocks' published word counts and
+// rates, tagged with `epoch` (1 .. kFusedEpochMax): every launch on one words
+// buffer takes a new epoch, and the buffer is cleared
+// (launch_fused_words_clear) before its first launch and whenever the epochs
+// start over, so a word is never read as a later launch's.
 constexpr int64_t kFusedMaxBlocks = 1024;
+static_assert(kFusedWordsBytes == 2 * kFusedMaxBlocks * sizeof(uint64_t), "fused words");
+constexpr uint32_t kFusedEpochMax = (1u << 28) - 1u;
 hipError_t launch_admit_fused(const void* x0, const void* x1, int64_t nb0, int64_t R, const RankTable& rt,
                               double lam_in, int shift, uint64_t seed, double* D, double* H, float* stats,
                               int32_t* choice, float* codebook, uint8_t* m, uint64_t* off, uint32_t* codes,
-                              void* ws, struct SolveOut* out, hipStream_t st);
+                              void* ws, uint64_t* words, uint32_t epoch, struct SolveOut* out, hipStream_t st);
+hipError_t launch_fused_words_clear(uint64_t* words, hipStream_t st);
 // Read `bytes` (<= kStagingBytes) of device memory into host memory `dst`
 // on stream st and wait for it, through the calling thread's pinned staging
 // buffer (hipHostMalloc'd on first use and kept until the process ends; a
